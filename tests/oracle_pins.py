@@ -1,0 +1,466 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with
+something the pages or the mathematics fix: hand-computed examples (stored
+under ``tests/golden/``), library routines that a special case reduces to
+(torch's fp8/bf16 casts, ``numpy.dot``, torch's scaled-dot-product attention,
+``torch.logsumexp``), closed forms, and invariants.  ``test_oracle.py`` runs
+them one by one; ``test_oracle_mutants.py`` runs all of them against copies of
+the oracle with planted mistakes and requires each mistake to be caught.
+
+Everything here runs on the CPU at tiny sizes.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from lightning_indexer_top_02_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _raw(case_tensor):
+    return inputs.to_numpy_raw(case_tensor)
+
+
+def _np_case(c):
+    """Host views of a Case for the oracle."""
+    return dict(
+        q_offsets=_raw(c.q_offsets), ctx_lens=_raw(c.ctx_lens), block_table=_raw(c.block_table),
+        page_size=c.page_size, dtype=c.idx_dtype, q=_raw(c.q_idx), q_scale=_raw(c.q_scale),
+        w=_raw(c.weights), k_cache=_raw(c.k_cache), k_scale=_raw(c.k_scale))
+
+
+def _decoded(raw, dtype):
+    """Decode stored elements to float64 with torch's own casts (library)."""
+    t = torch.from_numpy(np.ascontiguousarray(raw))
+    if dtype == "f32":
+        return t.double().numpy()
+    if dtype == "bf16":
+        return t.view(torch.bfloat16).double().numpy()
+    return t.view(torch.float8_e4m3fn).double().numpy()
+
+
+def _logical_rows(pool, block_table_row, L, page_size):
+    """De-page: row t of the request is pool[bt[t // P], t % P] (data movement only)."""
+    t = np.arange(L)
+    return pool[block_table_row[t // page_size], t % page_size]
+
+
+def _small_case(seed, dtype="f32", ctx=(37, 150), n_q=(1, 3), H=3, D=8, topk=16, exact=False,
+                H_q=2, qk_dim=12, v_dim=8, sfa_dtype="f32", page_size=16, w_dist="normal8"):
+    return inputs.make_case(seed=seed, ctx_lens=list(ctx), n_q=list(n_q), idx_dtype=dtype,
+                            n_heads_idx=H, head_dim_idx=D, topk=topk, exact=exact,
+                            sfa_dtype=sfa_dtype, n_heads_sfa=H_q, qk_dim=qk_dim, v_dim=v_dim,
+                            sfa_std=1.0, n_decoy=2, page_size=page_size, w_dist=w_dist)
+
+
+# ---------------------------------------------------------------------------
+# element decoding
+# ---------------------------------------------------------------------------
+def check_decode_e4m3_all_codes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.decode_e4m3(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got)), "e4m3 NaN codes differ"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok]), "e4m3 decode differs from torch.float8_e4m3fn"
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok])), "e4m3 sign of zero differs"
+
+
+def check_decode_bf16():
+    rng = np.random.default_rng(5)
+    bits = np.concatenate([rng.integers(0, 65536, 3000), [0, 0x8000, 0x3F80, 0xBF80, 0x7F7F,
+                                                          0x0001, 0x8001, 0x7F80, 0xFF80]])
+    bits = bits.astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.decode_bf16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan]), "bf16 decode differs from torch.bfloat16"
+
+
+# ---------------------------------------------------------------------------
+# hand examples
+# ---------------------------------------------------------------------------
+def _hand_layout(keys, page_size=2):
+    """One request whose single query row is the last of its L positions,
+    keys spread over pages of ``page_size`` with a reversed block table."""
+    L = len(keys)
+    n_pages = (L + page_size - 1) // page_size
+    pool = np.full((n_pages + 1, page_size, len(keys[0])), np.nan, dtype=np.float32)
+    bt = np.arange(n_pages, 0, -1, dtype=np.int32)[None, :]  # page 0 is a NaN decoy
+    for t, k in enumerate(keys):
+        pool[bt[0, t // page_size], t % page_size] = k
+    return pool, bt
+
+
+def check_hand_examples_indexer():
+    with open(os.path.join(GOLDEN, "indexer_hand_examples.json")) as f:
+        g = json.load(f)
+    q = np.array([g["q"]], dtype=np.float32)  # [T=1][H][D]
+    runs = [(g["keys"], c) for c in g["cases"]] + [(g["signed_zero_case"]["keys"],
+                                                    g["signed_zero_case"])]
+    for keys, c in runs:
+        pool, bt = _hand_layout(keys)
+        w = np.array([c["w"]], dtype=np.float32)
+        qo, cl = np.array([0, 1]), np.array([len(keys)])
+        s = oracle.scores(qo, cl, bt, 2, "f32", q, None, w, pool, None)
+        assert np.array_equal(s[0], np.array(c["scores"], dtype=np.float64)), (s, c["scores"])
+        for K, want in c["topk"].items():
+            got = oracle.indexer_topk(qo, cl, bt, 2, "f32", q, None, w, pool, None, int(K))
+            assert got[0].tolist() == want, (K, got[0].tolist(), want)
+
+
+def check_hand_example_sfa():
+    with open(os.path.join(GOLDEN, "sfa_hand_example.json")) as f:
+        g = json.load(f)
+    rows = np.array(g["rows"], dtype=np.float32)
+    pool = np.full((3, 2, g["qk_dim"]), np.nan, dtype=np.float32)
+    pool[2] = rows
+    bt = np.array([[2]], dtype=np.int32)
+    q = np.array([[g["q"]]], dtype=np.float32)
+    for idx in ([[0, 1]], [[1, 0]], [[-1, 1, -1, 0]]):
+        out, lse = oracle.sparse_attn(np.array([0, 1]), bt, 2, "f32", g["scale"], q, pool,
+                                      np.array(idx), g["v_dim"])
+        assert np.allclose(out[0, 0], g["out"], rtol=0, atol=1e-15), (out, g["out"])
+        assert abs(lse[0, 0] - g["lse"]) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# scores
+# ---------------------------------------------------------------------------
+def check_relu_identity_against_dot():
+    """With a one-hot head weight, s(q) - s(-q) = q_h . k_t (relu(x) - relu(-x) = x);
+    the right side is numpy.dot on independently de-paged keys."""
+    for dtype in ("f32", "bf16"):
+        c = _small_case(11, dtype=dtype)
+        a = _np_case(c)
+        vis = oracle.visible(a["q_offsets"], a["ctx_lens"])
+        qd = _decoded(a["q"], dtype)
+        kd = _decoded(a["k_cache"], dtype)
+        H = qd.shape[1]
+        for h in range(H):
+            w = np.zeros_like(a["w"])
+            w[:, h] = 1.0
+            q_neg = _negate_raw(a["q"], dtype)
+            sp = oracle.scores(**{**a, "w": w})
+            sn = oracle.scores(**{**a, "w": w, "q": q_neg})
+            for b in range(len(a["ctx_lens"])):
+                keys = _logical_rows(kd, a["block_table"][b], int(a["ctx_lens"][b]), a["page_size"])
+                for i in range(a["q_offsets"][b], a["q_offsets"][b + 1]):
+                    n = vis[i]
+                    want = keys[:n] @ qd[i, h]
+                    got = sp[i, :n] - sn[i, :n]
+                    assert np.allclose(got, want, rtol=1e-12, atol=1e-12), (dtype, h, i)
+                    assert np.all(sp[i, :n] >= 0) and np.all(sn[i, :n] >= 0)
+
+
+def _negate_raw(raw, dtype):
+    if dtype == "f32":
+        return -raw
+    if dtype == "bf16":
+        return (raw ^ np.uint16(0x8000)).astype(np.uint16)
+    return (raw ^ np.uint8(0x80)).astype(np.uint8)
+
+
+def check_head_weight_linearity():
+    """s(w) = sum_h w_h * s(e_h): the score is linear in the head weights of its
+    own row, with non-negative per-head terms."""
+    c = _small_case(12, dtype="f32")
+    a = _np_case(c)
+    s_full = oracle.scores(**a)
+    T, H = a["w"].shape
+    acc = np.zeros_like(s_full)
+    for h in range(H):
+        e = np.zeros_like(a["w"])
+        e[:, h] = 1.0
+        s_h = oracle.scores(**{**a, "w": e})
+        vis = ~np.isnan(s_h)
+        assert np.all(s_h[vis] >= 0)
+        acc += a["w"][:, h : h + 1].astype(np.float64) * s_h
+    ok = ~np.isnan(s_full)
+    assert np.array_equal(ok, ~np.isnan(acc))
+    assert np.allclose(s_full[ok], acc[ok], rtol=1e-12, atol=1e-12)
+
+
+def check_one_hot_query_reads_key_element():
+    """q_h = e_d (one-hot over the head dim) and w = e_h gives s_t = relu(k_t[d]):
+    the score of every position is one stored key element, read back through
+    the block table by hand."""
+    c = _small_case(13, dtype="f32", H=3, D=5)
+    a = _np_case(c)
+    kd = a["k_cache"].astype(np.float64)
+    vis = oracle.visible(a["q_offsets"], a["ctx_lens"])
+    T, H, D = a["q"].shape
+    for h, d in ((0, 4), (2, 1), (1, 0)):
+        q = np.zeros_like(a["q"])
+        q[:, h, d] = 1.0
+        w = np.zeros_like(a["w"])
+        w[:, h] = 1.0
+        s = oracle.scores(**{**a, "q": q, "w": w})
+        for b in range(len(a["ctx_lens"])):
+            for i in range(a["q_offsets"][b], a["q_offsets"][b + 1]):
+                for t in range(vis[i]):
+                    p = a["block_table"][b][t // a["page_size"]]
+                    want = max(kd[p, t % a["page_size"], d], 0.0)
+                    assert s[i, t] == want, (h, d, i, t)
+
+
+def check_fp8_scales():
+    """fp8 route: real value = code * scale.  Scores equal the fp32 route's on
+    the decoded, pre-multiplied values (q scale per (row, head), k scale per
+    token), to fp32 rounding of the products."""
+    c = _small_case(14, dtype="fp8", H=3, D=16)
+    a = _np_case(c)
+    qv = (_decoded(a["q"], "fp8") * a["q_scale"][:, :, None]).astype(np.float32)
+    kv = _decoded(a["k_cache"], "fp8") * a["k_scale"][:, :, None]
+    kv = kv.astype(np.float32)
+    s8 = oracle.scores(**a)
+    s32 = oracle.scores(**{**a, "dtype": "f32", "q": qv, "q_scale": None, "k_cache": kv,
+                           "k_scale": None})
+    ok = ~np.isnan(s32)
+    assert np.array_equal(ok, ~np.isnan(s8))
+    assert np.allclose(s8[ok], s32[ok], rtol=1e-5, atol=1e-5)
+    # doubling one token's k scale doubles that token's score only
+    b, t = 1, 5
+    p = a["block_table"][b][t // a["page_size"]]
+    ks = a["k_scale"].copy()
+    ks[p, t % a["page_size"]] *= 2
+    s2 = oracle.scores(**{**a, "k_scale": ks})
+    i = int(a["q_offsets"][b])
+    diff = np.nonzero(~np.isclose(s2, s8, rtol=0, atol=0, equal_nan=True))
+    assert set(zip(*diff)) <= {(r, t) for r in range(a["q_offsets"][b], a["q_offsets"][b + 1])}
+    assert np.isclose(s2[i, t], 2 * s8[i, t], rtol=1e-12, atol=0)
+    # doubling one (row, head) q scale changes only that row
+    qs = a["q_scale"].copy()
+    qs[0, 1] *= 2
+    s3 = oracle.scores(**{**a, "q_scale": qs})
+    changed_rows = set(np.nonzero(~np.isclose(s3, s8, equal_nan=True))[0].tolist())
+    assert changed_rows <= {0} and len(changed_rows) == 1
+
+
+def check_causal_visibility():
+    """Rows of a request with n query tokens sit at its last n positions; row j
+    sees L - n + j + 1 positions.  Invisible positions never score and are
+    never selected, however large their keys."""
+    c = _small_case(15, dtype="f32", ctx=(70, 131, 9), n_q=(4, 1, 9), topk=200)
+    a = _np_case(c)
+    vis = oracle.visible(a["q_offsets"], a["ctx_lens"])
+    want = []
+    for b, L in enumerate(a["ctx_lens"]):
+        n = a["q_offsets"][b + 1] - a["q_offsets"][b]
+        want += [L - n + j + 1 for j in range(n)]
+    assert vis.tolist() == want
+    s = oracle.scores(**a)
+    for i, n in enumerate(vis):
+        assert not np.any(np.isnan(s[i, :n])) and np.all(np.isnan(s[i, n:]))
+    # plant huge keys at the last positions of request 0 (visible to row 3 only)
+    k = a["k_cache"].copy()
+    bt = a["block_table"]
+    for t in (67, 68, 69):
+        k[bt[0][t // a["page_size"]], t % a["page_size"]] = 1e3
+    w = np.abs(a["w"])
+    q = np.abs(a["q"])
+    idx = oracle.indexer_topk(**{**a, "k_cache": k, "w": w, "q": q}, K=3)
+    for j in range(4):
+        pos = 66 + j
+        assert np.all(idx[j][idx[j] >= 0] <= pos), (j, idx[j])
+    assert idx[3].tolist() == [67, 68, 69]
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+def _assert_topk_definition(score_row, n_vis, K, sel_row):
+    """Brute force over all pairs: selected positions are ascending, there are
+    min(K, n_vis) of them, the rest is -1, and every selected position beats
+    every unselected visible one (higher score, or equal score and lower
+    position)."""
+    keep = min(K, n_vis)
+    sel = sel_row[:keep]
+    assert np.all(sel_row[keep:] == -1), "padding"
+    assert np.all(np.diff(sel) > 0), "not ascending"
+    assert np.all((sel >= 0) & (sel < n_vis)), "out of range"
+    chosen = np.zeros(n_vis, dtype=bool)
+    chosen[sel] = True
+    for t in np.nonzero(chosen)[0]:
+        for u in np.nonzero(~chosen)[0]:
+            st, su = score_row[t], score_row[u]
+            assert st > su or (st == su and t < u), (t, u, st, su)
+
+
+def check_selection_definition():
+    rng = np.random.default_rng(3)
+    for trial in range(30):
+        T = 3
+        L = int(rng.integers(1, 60))
+        vis = np.array([L, max(1, L - 3), max(1, L // 2)], dtype=np.int32)
+        # integer scores with many ties, plus signed zeros
+        s = rng.integers(-3, 4, size=(T, L)).astype(np.float64)
+        s[rng.random((T, L)) < 0.1] = -0.0
+        for K in (1, 2, 5, L, L + 3):
+            idx = oracle.select(s, vis, K)
+            for i in range(T):
+                _assert_topk_definition(s[i], vis[i], K, idx[i])
+
+
+def check_selection_signed_zero_and_nesting():
+    s = np.array([[0.0, -0.0, 0.0, -0.0, -1.0, 1.0]])
+    for K in range(1, 8):
+        idx = oracle.select(s, np.array([6]), K)[0]
+        want = sorted(([5] + [0, 1, 2, 3] + [4])[: min(K, 6)]) + [-1] * max(0, K - 6)
+        assert idx.tolist() == want, (K, idx)
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((2, 200))
+    vis = np.array([200, 137])
+    prev = [set(), set()]
+    for K in range(1, 210, 7):
+        idx = oracle.select(s, vis, K)
+        for i in range(2):
+            cur = set(idx[i][idx[i] >= 0].tolist())
+            assert prev[i] <= cur
+            prev[i] = cur
+
+
+def check_indexer_topk_full_context():
+    """K equal to (or above) the visible count selects every visible position."""
+    c = _small_case(16, dtype="bf16", ctx=(40, 100), n_q=(1, 2))
+    a = _np_case(c)
+    vis = oracle.visible(a["q_offsets"], a["ctx_lens"])
+    for K in (int(vis.max()), int(vis.max()) + 5):
+        idx = oracle.indexer_topk(**a, K=K)
+        for i, n in enumerate(vis):
+            assert idx[i].tolist() == list(range(n)) + [-1] * (K - n)
+
+
+def check_page_permutation_invariance():
+    c = _small_case(17, dtype="bf16", topk=20, sfa_dtype="bf16")
+    c2 = inputs.permute_pages(c, seed=99)
+    assert not np.array_equal(_raw(c.block_table), _raw(c2.block_table))
+    outs = []
+    for cc in (c, c2):
+        a = _np_case(cc)
+        idx, s = oracle.indexer_topk(**a, K=cc.topk, return_scores=True)
+        o, l = oracle.sparse_attn(a["q_offsets"], a["block_table"], cc.page_size, cc.sfa_dtype,
+                                  cc.scale, _raw(cc.q_sfa), _raw(cc.kv_cache), idx, cc.v_dim)
+        outs.append((idx, s, o, l))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1], equal_nan=True)
+    assert np.array_equal(outs[0][2], outs[1][2])
+    assert np.array_equal(outs[0][3], outs[1][3])
+
+
+# ---------------------------------------------------------------------------
+# sparse attention
+# ---------------------------------------------------------------------------
+def check_sfa_dense_reduction():
+    """Selecting every visible position reduces sparse attention to dense
+    causal softmax attention: compare with torch's scaled_dot_product_attention
+    and torch.logsumexp in float64 on independently de-paged rows."""
+    for dtype in ("f32", "bf16"):
+        c = _small_case(18, dtype="f32", sfa_dtype=dtype, ctx=(33, 90), n_q=(2, 3), H_q=3,
+                        qk_dim=20, v_dim=12)
+        a = _np_case(c)
+        vis = oracle.visible(a["q_offsets"], a["ctx_lens"])
+        K = int(vis.max())
+        idx = np.full((len(vis), K), -1, dtype=np.int32)
+        for i, n in enumerate(vis):
+            idx[i, :n] = np.arange(n)
+        qs, kvs = _raw(c.q_sfa), _raw(c.kv_cache)
+        out, lse = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, dtype,
+                                      c.scale, qs, kvs, idx, c.v_dim)
+        qd = torch.from_numpy(_decoded(qs, dtype))
+        kvd = _decoded(kvs, dtype)
+        for b in range(len(a["ctx_lens"])):
+            rows = torch.from_numpy(_logical_rows(kvd, a["block_table"][b], int(a["ctx_lens"][b]),
+                                                  c.page_size))
+            for i in range(a["q_offsets"][b], a["q_offsets"][b + 1]):
+                n = int(vis[i])
+                kk, vv = rows[:n], rows[:n, : c.v_dim]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qd[i][:, None, :], kk[None].expand(qd.shape[1], -1, -1),
+                    vv[None].expand(qd.shape[1], -1, -1), scale=c.scale)[:, 0, :]
+                assert np.allclose(out[i], ref.numpy(), rtol=1e-11, atol=1e-12), (dtype, i)
+                ref_lse = torch.logsumexp(c.scale * (qd[i] @ kk.T), dim=-1)
+                assert np.allclose(lse[i], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def check_sfa_zero_query_is_mean():
+    """q = 0 gives equal weights: the output is the mean of the selected values."""
+    c = _small_case(19, sfa_dtype="f32", H_q=2, qk_dim=10, v_dim=6)
+    a = _np_case(c)
+    qz = np.zeros_like(_raw(c.q_sfa))
+    kvd = _raw(c.kv_cache).astype(np.float64)
+    idx = np.array([[3, 7, 30, -1], [0, 5, -1, -1], [1, 2, 3, 4], [99, 150 - 3, 12, 77]],
+                   dtype=np.int32)
+    out, lse = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "f32", c.scale,
+                                  qz, _raw(c.kv_cache), idx, c.v_dim)
+    for i in range(4):
+        b = 0 if i < 1 else 1
+        sel = idx[i][idx[i] >= 0]
+        rows = _logical_rows(kvd, a["block_table"][b], int(a["ctx_lens"][b]), c.page_size)[sel]
+        assert np.allclose(out[i], rows[:, : c.v_dim].mean(0)[None, :], rtol=1e-13, atol=1e-14)
+        assert np.allclose(lse[i], math.log(len(sel)), rtol=1e-14)
+
+
+def check_sfa_dominant_row():
+    """One selected row with a logit 1000 above every other gives exactly that
+    row's value vector."""
+    c = _small_case(20, sfa_dtype="f32", H_q=2, qk_dim=10, v_dim=6, ctx=(64,), n_q=(1,))
+    a = _np_case(c)
+    kv = _raw(c.kv_cache).copy()
+    bt = a["block_table"][0]
+    kv[:, :, 9] = 0.0
+    t0 = 21
+    kv[bt[t0 // c.page_size], t0 % c.page_size, 9] = 1.0
+    q = np.zeros_like(_raw(c.q_sfa))
+    q[:, :, 9] = 1000.0
+    idx = np.array([[2, 9, t0, 40, 63]], dtype=np.int32)
+    out, lse = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "f32", 1.0, q,
+                                  kv, idx, c.v_dim)
+    want = kv[bt[t0 // c.page_size], t0 % c.page_size, : c.v_dim].astype(np.float64)
+    assert np.array_equal(out[0, 0], want) and np.array_equal(out[0, 1], want)
+    assert abs(lse[0, 0] - 1000.0) < 1e-9
+
+
+def check_sfa_uses_scale():
+    """Doubling the scale equals doubling q."""
+    c = _small_case(21, sfa_dtype="f32", H_q=2, qk_dim=10, v_dim=6)
+    a = _np_case(c)
+    idx = np.array([[0, 4, 9, 30]] * 4, dtype=np.int32)
+    qs = _raw(c.q_sfa)
+    o1, l1 = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "f32", 0.3, qs,
+                                _raw(c.kv_cache), idx, c.v_dim)
+    o2, l2 = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "f32", 0.6,
+                                (qs * 0.5).astype(np.float32), _raw(c.kv_cache), idx, c.v_dim)
+    o3, _ = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "f32", 0.6, qs,
+                               _raw(c.kv_cache), idx, c.v_dim)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-13) and np.allclose(l1, l2, rtol=1e-12)
+    assert not np.allclose(o1, o3, rtol=1e-6, atol=1e-9)
+
+
+ALL_CHECKS = [
+    check_decode_e4m3_all_codes,
+    check_decode_bf16,
+    check_hand_examples_indexer,
+    check_hand_example_sfa,
+    check_relu_identity_against_dot,
+    check_head_weight_linearity,
+    check_one_hot_query_reads_key_element,
+    check_fp8_scales,
+    check_causal_visibility,
+    check_selection_definition,
+    check_selection_signed_zero_and_nesting,
+    check_indexer_topk_full_context,
+    check_page_permutation_invariance,
+    check_sfa_dense_reduction,
+    check_sfa_zero_query_is_mean,
+    check_sfa_dominant_row,
+    check_sfa_uses_scale,
+]

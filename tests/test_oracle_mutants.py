@@ -1,0 +1,98 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutant is a copy of ``oracle/dsa_oracle.c`` with one planted mistake (a
+dropped term, a wrong sign or index, a transposed operand, a wrong tie rule
+...), compiled with gcc into a temporary library.  Every mutant must fail at
+least one pin of ``oracle_pins.py``.  Runs on the CPU only.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.lib_path()), "dsa_oracle.c")
+
+# (name, text in the oracle source, replacement)
+MUTANTS = [
+    ("relu_dropped", "s += wd[h] * (logit > 0.0 ? logit : 0.0);", "s += wd[h] * logit;"),
+    ("relu_wrong_side", "s += wd[h] * (logit > 0.0 ? logit : 0.0);",
+     "s += wd[h] * (logit < 0.0 ? logit : 0.0);"),
+    ("weight_inside_relu", "s += wd[h] * (logit > 0.0 ? logit : 0.0);",
+     "s += (wd[h] * logit > 0.0 ? wd[h] * logit : 0.0);"),
+    ("weights_of_row0", "wd[h] = (double)w[(size_t)i * H + h];", "wd[h] = (double)w[h];"),
+    ("q_transposed", "load_elem(q, ((size_t)i * H + h) * D + d, dtype)",
+     "load_elem(q, ((size_t)i * D + d) * H + h, dtype)"),
+    ("slot_shifted", "int slot = t % page_size;", "int slot = (t + 1) % page_size;"),
+    ("physical_position", "int page = block_table[(size_t)b * bt_stride + t / page_size];\n            int slot = t % page_size;",
+     "int page = t / page_size;\n            int slot = t % page_size;"),
+    ("k_scale_ignored", "double ks = (dtype == 2) ? (double)k_scale[(size_t)page * page_size + slot] : 1.0;",
+     "double ks = 1.0;"),
+    ("q_scale_per_row", "double qs = (dtype == 2) ? (double)q_scale[(size_t)i * H + h] : 1.0;",
+     "double qs = (dtype == 2) ? (double)q_scale[(size_t)i * H] : 1.0;"),
+    ("causal_off_by_one", "vis[q_offsets[b] + j] = ctx_lens[b] - n + j + 1;",
+     "vis[q_offsets[b] + j] = ctx_lens[b] - n + j;"),
+    ("causal_all_rows_see_all", "vis[q_offsets[b] + j] = ctx_lens[b] - n + j + 1;",
+     "vis[q_offsets[b] + j] = ctx_lens[b];"),
+    ("ties_to_higher_position", "return (x->t > y->t) - (x->t < y->t);",
+     "return (x->t < y->t) - (x->t > y->t);"),
+    ("ascending_scores", "if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;",
+     "if (x->s < y->s) return -1;\n    if (x->s > y->s) return 1;"),
+    ("not_rearranged", "qsort(out, (size_t)keep, sizeof(int32_t), ascending_i32);", ""),
+    ("pad_with_zero", "out[r] = -1;", "out[r] = 0;"),
+    ("e4m3_bias_8", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3_subnormal_implicit_one", "v = ldexp((double)m / 8.0, -6);", "v = ldexp(1.0 + (double)m / 8.0, -6);"),
+    ("e4m3_no_nan", "if (e == 15 && m == 7)\n        return NAN;", ""),
+    ("bf16_low_half", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits;"),
+    ("sfa_scale_dropped", "z[r] = scale * dot;", "z[r] = dot;"),
+    ("sfa_value_from_tail", "o[e] += p * load_elem(kv_cache, base + e, dtype);",
+     "o[e] += p * load_elem(kv_cache, base + (Dqk - Dv) + e, dtype);"),
+    ("sfa_key_without_rope", "for (int d = 0; d < Dqk; ++d)\n                    dot += qd[d]",
+     "for (int d = 0; d < Dv; ++d)\n                    dot += qd[d]"),
+    ("sfa_not_normalised", "o[e] /= l;", "o[e] /= 1.0;"),
+    ("sfa_lse_without_max", "lse[(size_t)i * H + h] = m + log(l);", "lse[(size_t)i * H + h] = log(l);"),
+    ("sfa_padding_read", "if (t < 0)\n                    continue;\n                double p",
+     "if (t < 0)\n                    t = 0;\n                double p"),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutant {name}: pattern not found in the oracle source"
+    path_c = tmp_path / f"{name}.c"
+    path_c.write_text(src.replace(old, new, 1))
+    (tmp_path / "dsa_oracle.h").write_text(open(SRC.replace(".c", ".h")).read())
+    path_so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-std=c99", "-O1", "-fopenmp", "-fPIC", "-shared", str(path_c), "-o",
+                    str(path_so), "-lm"], check=True)
+    return str(path_so)
+
+
+RUNNER = r"""
+import sys
+sys.path[:0] = [sys.argv[1], sys.argv[2]]
+import oracle, oracle_pins
+oracle.load_library(sys.argv[3])
+caught = []
+for check in oracle_pins.ALL_CHECKS:
+    try:
+        check()
+    except Exception as e:
+        caught.append(check.__name__)
+        break
+print("caught by:", caught)
+sys.exit(0 if caught else 3)
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(oracle_mod, tmp_path, name, old, new):
+    so = _build_mutant(tmp_path, name, old, new)
+    tests_dir = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(tests_dir)
+    r = subprocess.run([sys.executable, "-c", RUNNER, root, tests_dir, so], capture_output=True,
+                       text=True, timeout=300, env={**os.environ, "OMP_NUM_THREADS": "2"})
+    assert r.returncode == 0, f"no pin caught the planted mistake {name}: {r.stdout}{r.stderr[-2000:]}"
