@@ -1,0 +1,153 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DSA sparse-attention step.
+ *
+ * The step has three parts, after "Optimizing Inference for Hybrid Attention
+ * Architectures: From Operator Fusion to Sequence Sharding", section
+ * "Breaking Down the Computational Path of Hybrid Attention":
+ *   1. the lightning indexer scores every visible cached position against the
+ *      query, per indexer head, and weights the heads by importance:
+ *          s_t = sum_h w_h * max(q_h . k_t, 0)
+ *   2. it keeps the Top-K positions as sparse indices;
+ *   3. sparse flash attention reads only those rows of the latent KV cache and
+ *      runs softmax attention over them.
+ * Parts 1-2 read the paged K cache directly and write only indices ("Day0
+ * Inference Support and Performance Optimization for New LLM Architectures",
+ * section III, 3.1); part 3 gathers the selected rows from the paged main
+ * cache (same page, section III, 3.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every array pointer is DEVICE memory owned by the caller; the
+ *   library never allocates, frees, copies host<->device or synchronizes.
+ *   Descriptor structs themselves are host memory, read during the call only.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Calls only enqueue work on it and return; results are visible once the
+ *   stream has reached that point.
+ * Workspace: `ws` is caller-owned device memory of at least the size the
+ *   matching *_workspace_size call returns, 256-byte aligned.  The library
+ *   initializes whatever part it needs inside the call (graph-capture safe:
+ *   no memset nodes).  Concurrent calls must not share a workspace.
+ * Errors: arguments are validated on the host before anything is enqueued;
+ *   on a bad argument the call returns a non-zero dsa_status_t and enqueues
+ *   nothing.  Device data (page ids, lengths) is trusted: a page id outside
+ *   [0, num_pages) or a ctx_len above max_ctx_len is undefined behaviour.
+ * Layouts (row-major, contiguous):
+ *   paged pools      [num_pages][page_size][dim]        page_size = 64
+ *   block_table      [batch][max_pages_per_req] int32   physical page ids
+ *   q_offsets        [batch+1] int32; request b owns query rows
+ *                    [q_offsets[b], q_offsets[b+1]) (non-decreasing, q_offsets[0] = 0)
+ *   ctx_lens         [batch] int32; L_b includes request b's own query tokens,
+ *                    so its n_b query rows sit at positions L_b-n_b .. L_b-1
+ *                    and row j sees positions 0 .. L_b-n_b+j (causal).
+ *   fp8 storage      OCP e4m3 (no infinities) codes; value = code * fp32 scale.
+ *   bf16 storage     raw 16-bit patterns.
+ * Indices: logical positions within the request (not physical slots),
+ *   ascending, padded with -1 when fewer than K positions are visible.
+ *   Equal scores at the K-th place: the lower position is kept.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_PAGE_SIZE 64
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,       /* null pointer, bad size or bad combination */
+    DSA_ERR_UNSUPPORTED = 2,       /* valid but not implemented (dims, dtype) */
+    DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+    DSA_ERR_LAUNCH = 4,            /* the HIP runtime refused a launch */
+    DSA_ERR_DEVICE = 5             /* no usable gfx950 device current */
+} dsa_status_t;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
+
+/* Paging and batch description, shared by both caches (one block table and
+ * one page size for the indexer K pool and the latent pool). */
+typedef struct {
+    int32_t batch;             /* B >= 1 */
+    int32_t num_q_tokens;      /* T = q_offsets[B] >= 1 */
+    int32_t max_q_per_req;     /* host bound >= every n_b (sizes grids) */
+    int32_t max_ctx_len;       /* host bound >= every L_b */
+    int32_t max_pages_per_req; /* block-table row stride >= ceil(max_ctx_len / 64) */
+    int32_t page_size;         /* must be 64 */
+    int32_t num_pages;         /* pages in each pool */
+    const int32_t *q_offsets;  /* device [B+1] */
+    const int32_t *ctx_lens;   /* device [B] */
+    const int32_t *block_table;/* device [B][max_pages_per_req] */
+} dsa_paged_t;
+
+/* Lightning indexer.  Supported: dtype F32 with head_dim % 4 == 0 and
+ * n_heads*head_dim <= 4096; BF16 or FP8_E4M3 with head_dim in {64, 128};
+ * 1 <= n_heads <= 64; 1 <= topk <= 4096. */
+typedef struct {
+    int32_t n_heads;           /* H_I */
+    int32_t head_dim;          /* D_I */
+    int32_t topk;              /* K */
+    int32_t dtype;             /* dsa_dtype_t of q and k_cache */
+    const void *q;             /* [T][H_I][D_I] */
+    const float *q_scale;      /* [T][H_I] for FP8_E4M3, else NULL */
+    const float *weights;      /* [T][H_I] head-importance weights */
+    const void *k_cache;       /* [num_pages][64][D_I] */
+    const float *k_scale;      /* [num_pages][64] for FP8_E4M3, else NULL */
+} dsa_indexer_t;
+
+/* Sparse flash attention over a shared MLA latent cache: the key of a
+ * position is its whole row (qk_dim = 576 = 512 latent + 64 rope), the value
+ * its first v_dim = 512 entries.  Supported: dtype F32 or BF16,
+ * qk_dim 576, v_dim 512, n_heads a multiple of 16 up to 128. */
+typedef struct {
+    int32_t n_heads;           /* H_q */
+    int32_t qk_dim;            /* 576 */
+    int32_t v_dim;             /* 512 */
+    int32_t dtype;             /* DSA_F32 or DSA_BF16 (q, kv_cache and out) */
+    float scale;               /* softmax scale, e.g. 1/sqrt(576) */
+    const void *q;             /* [T][H_q][qk_dim] */
+    const void *kv_cache;      /* [num_pages][64][qk_dim] */
+    void *out;                 /* [T][H_q][v_dim], same dtype */
+    float *lse;                /* [T][H_q] natural-log sum-exp, or NULL */
+} dsa_sfa_t;
+
+/* Bytes of workspace dsa_indexer_topk needs for these arguments (0 when the
+ * arguments are invalid). */
+size_t dsa_indexer_topk_workspace_size(const dsa_paged_t *paged, const dsa_indexer_t *idx);
+
+/* Steps 1-2: Top-K positions of every query row.  topk_idx is device
+ * [T][topk] int32 (written in full). */
+dsa_status_t dsa_indexer_topk(const dsa_paged_t *paged, const dsa_indexer_t *idx,
+                              int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream);
+
+size_t dsa_sparse_attn_workspace_size(const dsa_paged_t *paged, const dsa_sfa_t *sfa,
+                                      int32_t topk);
+
+/* Step 3: attention of every query row over its topk_idx row (device
+ * [T][topk] int32 of logical positions, -1 entries skipped; a row with no
+ * valid entry yields a zero output and lse = -inf). */
+dsa_status_t dsa_sparse_attn(const dsa_paged_t *paged, const dsa_sfa_t *sfa,
+                             const int32_t *topk_idx, int32_t topk,
+                             void *ws, size_t ws_bytes, void *stream);
+
+size_t dsa_fused_decode_workspace_size(const dsa_paged_t *paged, const dsa_indexer_t *idx,
+                                       const dsa_sfa_t *sfa);
+
+/* Steps 1-3 in one call.  topk_idx may be NULL (indices then live only in
+ * the workspace); otherwise it receives the indices as dsa_indexer_topk
+ * would.  Results equal dsa_indexer_topk followed by dsa_sparse_attn. */
+dsa_status_t dsa_fused_decode(const dsa_paged_t *paged, const dsa_indexer_t *idx,
+                              const dsa_sfa_t *sfa, int32_t *topk_idx,
+                              void *ws, size_t ws_bytes, void *stream);
+
+const char *dsa_status_string(dsa_status_t status);
+int32_t dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,251 @@
+// abi.hip -- the C ABI of include/dsa.h: host-side validation, workspace
+// sizing and dispatch to the kernel launchers.  Validation runs before any
+// HIP runtime call, so a rejected call touches no device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "dsa_device.h"
+
+namespace {
+
+constexpr int kMaxTopk = 4096;
+constexpr int kMaxIdxHeads = 64;
+constexpr int kSfaMaxHeads = 128;
+constexpr int kNominalCUs = 256;   // MI355X; fixes split choices independently of the device
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+bool valid_paged(const dsa_paged_t* p) {
+  if (!p) return false;
+  if (p->batch < 1 || p->num_q_tokens < 1 || p->max_q_per_req < 1 || p->max_ctx_len < 1) return false;
+  if (p->page_size != DSA_PAGE_SIZE || p->num_pages < 1) return false;
+  if (p->max_q_per_req > p->num_q_tokens || p->max_q_per_req > p->max_ctx_len) return false;
+  if (p->num_q_tokens < p->batch) return false;
+  if ((int64_t)p->max_pages_per_req * DSA_PAGE_SIZE < p->max_ctx_len) return false;
+  if (!p->q_offsets || !p->ctx_lens || !p->block_table) return false;
+  return true;
+}
+
+dsa_status_t check_indexer(const dsa_paged_t* pg, const dsa_indexer_t* x) {
+  if (!valid_paged(pg) || !x) return DSA_ERR_INVALID_ARG;
+  if (!x->q || !x->weights || !x->k_cache) return DSA_ERR_INVALID_ARG;
+  if (x->n_heads < 1 || x->head_dim < 1 || x->topk < 1) return DSA_ERR_INVALID_ARG;
+  if (x->dtype != DSA_F32 && x->dtype != DSA_BF16 && x->dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
+  if (x->dtype == DSA_FP8_E4M3 && (!x->q_scale || !x->k_scale)) return DSA_ERR_INVALID_ARG;
+  if (x->n_heads > kMaxIdxHeads || x->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+  if (x->head_dim != 64 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (x->dtype == DSA_F32 && x->n_heads * x->head_dim > 4096) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+dsa_status_t check_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) {
+  if (!valid_paged(pg) || !s) return DSA_ERR_INVALID_ARG;
+  if (!s->q || !s->kv_cache || !s->out) return DSA_ERR_INVALID_ARG;
+  if (topk < 1 || s->n_heads < 1 || s->qk_dim < 1 || s->v_dim < 1 || s->v_dim > s->qk_dim)
+    return DSA_ERR_INVALID_ARG;
+  if (s->dtype != DSA_F32 && s->dtype != DSA_BF16) return DSA_ERR_INVALID_ARG;
+  if (!std::isfinite(s->scale)) return DSA_ERR_INVALID_ARG;
+  if (s->qk_dim != dsa::kQkDim || s->v_dim != dsa::kVDim) return DSA_ERR_UNSUPPORTED;
+  if (s->n_heads % 16 != 0 || s->n_heads > kSfaMaxHeads || topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+// --- workspace plans ---------------------------------------------------------
+struct IndexerPlan {
+  int64_t score_stride;
+  size_t hist_off, scores_off, total;
+};
+
+IndexerPlan plan_indexer(const dsa_paged_t* pg) {
+  IndexerPlan p;
+  p.score_stride = round_up(pg->max_ctx_len, 256);
+  p.hist_off = 0;
+  p.scores_off = align_up((size_t)pg->num_q_tokens * dsa::kHistBins * 4);
+  p.total = p.scores_off + align_up((size_t)pg->num_q_tokens * p.score_stride * 4);
+  return p;
+}
+
+int sfa_waves(int n_heads) {
+  const int hq = n_heads / 16;
+  for (int nw = 4; nw > 1; --nw)
+    if (hq % nw == 0) return nw;
+  return 1;
+}
+
+struct SfaPlan {
+  int n_split, rows_per_split;
+  size_t part_o_off, part_lse_off, total;
+};
+
+SfaPlan plan_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int topk) {
+  SfaPlan p{1, topk, 0, 0, 0};
+  if (s->dtype == DSA_BF16) {
+    const int64_t blocks = (int64_t)pg->num_q_tokens * (s->n_heads / (16 * sfa_waves(s->n_heads)));
+    int64_t splits = (2 * kNominalCUs + blocks - 1) / blocks;
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (topk + 63) / 64));
+    p.rows_per_split = (int)round_up((topk + splits - 1) / splits, 32);
+    p.n_split = (topk + p.rows_per_split - 1) / p.rows_per_split;
+  }
+  if (p.n_split > 1) {
+    const size_t th = (size_t)pg->num_q_tokens * s->n_heads;
+    p.part_o_off = 0;
+    p.part_lse_off = align_up((size_t)p.n_split * th * dsa::kVDim * 4);
+    p.total = p.part_lse_off + align_up((size_t)p.n_split * th * 4);
+  }
+  return p;
+}
+
+// --- device check --------------------------------------------------------------
+dsa_status_t check_device() {
+  static int cached[64];  // 0 unknown, 1 ok, 2 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DSA_ERR_DEVICE;
+  if (dev < 64 && cached[dev]) return cached[dev] == 1 ? DSA_OK : DSA_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cached[dev] = ok ? 1 : 2;
+  return ok ? DSA_OK : DSA_ERR_DEVICE;
+}
+
+DsaIndexerLaunch indexer_args(const dsa_paged_t* pg, const dsa_indexer_t* x, int32_t* out,
+                              unsigned char* ws, const IndexerPlan& plan) {
+  DsaIndexerLaunch a;
+  a.batch = pg->batch;
+  a.num_rows = pg->num_q_tokens;
+  a.max_q_per_req = pg->max_q_per_req;
+  a.max_ctx_len = pg->max_ctx_len;
+  a.bt_stride = pg->max_pages_per_req;
+  a.q_offsets = pg->q_offsets;
+  a.ctx_lens = pg->ctx_lens;
+  a.block_table = pg->block_table;
+  a.n_heads = x->n_heads;
+  a.head_dim = x->head_dim;
+  a.topk = x->topk;
+  a.dtype = x->dtype;
+  a.q = x->q;
+  a.q_scale = x->q_scale;
+  a.weights = x->weights;
+  a.k_cache = x->k_cache;
+  a.k_scale = x->k_scale;
+  a.out_idx = out;
+  a.hist = reinterpret_cast<uint32_t*>(ws + plan.hist_off);
+  a.scores = reinterpret_cast<float*>(ws + plan.scores_off);
+  a.score_stride = plan.score_stride;
+  return a;
+}
+
+DsaSfaLaunch sfa_args(const dsa_paged_t* pg, const dsa_sfa_t* s, const int32_t* idx, int topk,
+                      unsigned char* ws, const SfaPlan& plan) {
+  DsaSfaLaunch a;
+  a.batch = pg->batch;
+  a.num_rows = pg->num_q_tokens;
+  a.q_offsets = pg->q_offsets;
+  a.block_table = pg->block_table;
+  a.bt_stride = pg->max_pages_per_req;
+  a.n_heads = s->n_heads;
+  a.dtype = s->dtype;
+  a.scale = s->scale;
+  a.q = s->q;
+  a.kv_cache = s->kv_cache;
+  a.idx = idx;
+  a.topk = topk;
+  a.out = s->out;
+  a.lse = s->lse;
+  a.n_split = plan.n_split;
+  a.rows_per_split = plan.rows_per_split;
+  a.part_o = plan.n_split > 1 ? reinterpret_cast<float*>(ws + plan.part_o_off) : nullptr;
+  a.part_lse = plan.n_split > 1 ? reinterpret_cast<float*>(ws + plan.part_lse_off) : nullptr;
+  return a;
+}
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  if (need == 0) return true;
+  return ws && have >= need && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(dsa_status_t s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small or misaligned";
+    case DSA_ERR_LAUNCH: return "kernel launch failed";
+    case DSA_ERR_DEVICE: return "no gfx950 device is current";
+  }
+  return "unknown status";
+}
+
+size_t dsa_indexer_topk_workspace_size(const dsa_paged_t* pg, const dsa_indexer_t* x) {
+  if (check_indexer(pg, x) != DSA_OK) return 0;
+  return plan_indexer(pg).total;
+}
+
+dsa_status_t dsa_indexer_topk(const dsa_paged_t* pg, const dsa_indexer_t* x, int32_t* topk_idx,
+                              void* ws, size_t ws_bytes, void* stream) {
+  dsa_status_t st = check_indexer(pg, x);
+  if (st != DSA_OK) return st;
+  if (!topk_idx) return DSA_ERR_INVALID_ARG;
+  const IndexerPlan plan = plan_indexer(pg);
+  if (!ws_ok(ws, ws_bytes, plan.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device()) != DSA_OK) return st;
+  DsaIndexerLaunch a = indexer_args(pg, x, topk_idx, static_cast<unsigned char*>(ws), plan);
+  return dsa_launch_indexer_topk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+size_t dsa_sparse_attn_workspace_size(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) {
+  if (check_sfa(pg, s, topk) != DSA_OK) return 0;
+  return plan_sfa(pg, s, topk).total;
+}
+
+dsa_status_t dsa_sparse_attn(const dsa_paged_t* pg, const dsa_sfa_t* s, const int32_t* topk_idx,
+                             int32_t topk, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status_t st = check_sfa(pg, s, topk);
+  if (st != DSA_OK) return st;
+  if (!topk_idx) return DSA_ERR_INVALID_ARG;
+  const SfaPlan plan = plan_sfa(pg, s, topk);
+  if (!ws_ok(ws, ws_bytes, plan.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device()) != DSA_OK) return st;
+  DsaSfaLaunch a = sfa_args(pg, s, topk_idx, topk, static_cast<unsigned char*>(ws), plan);
+  return dsa_launch_sparse_attn(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+size_t dsa_fused_decode_workspace_size(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s) {
+  if (check_indexer(pg, x) != DSA_OK || !x || check_sfa(pg, s, x->topk) != DSA_OK) return 0;
+  return align_up(plan_indexer(pg).total) + align_up((size_t)pg->num_q_tokens * x->topk * 4) +
+         plan_sfa(pg, s, x->topk).total;
+}
+
+dsa_status_t dsa_fused_decode(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s,
+                              int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status_t st = check_indexer(pg, x);
+  if (st != DSA_OK) return st;
+  if ((st = check_sfa(pg, s, x->topk)) != DSA_OK) return st;
+  const IndexerPlan ip = plan_indexer(pg);
+  const SfaPlan sp = plan_sfa(pg, s, x->topk);
+  const size_t idx_off = align_up(ip.total);
+  const size_t sfa_off = idx_off + align_up((size_t)pg->num_q_tokens * x->topk * 4);
+  if (!ws_ok(ws, ws_bytes, sfa_off + sp.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device()) != DSA_OK) return st;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + idx_off);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dsa_launch_indexer_topk(indexer_args(pg, x, idx, w, ip), hs) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa_launch_sparse_attn(sfa_args(pg, s, idx, x->topk, w + sfa_off, sp), hs) != hipSuccess)
+    return DSA_ERR_LAUNCH;
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// dsa_device.h -- device helpers and kernel-launcher declarations shared by
+// the HIP sources of the DSA step library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kPage = 64;          // tokens per cache page
+constexpr int kQkDim = 576;        // latent (512) + rope (64)
+constexpr int kVDim = 512;
+constexpr int kHistBits = 11;      // first radix level: top 11 bits of the key
+constexpr int kHistBins = 1 << kHistBits;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+// ---------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even binary32 -> bfloat16 (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Order-preserving 32-bit key of an fp32 score: a larger score gives a larger
+// unsigned key; -0 and +0 map to the same key, so equal scores tie exactly.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------------------
+// Request lookup: the request that owns query row i (q_offsets is sorted).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int request_of_row(const int32_t* q_offsets, int batch, int i) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (q_offsets[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace dsa
+
+// ---------------------------------------------------------------------------
+// Launchers (host side).  Each returns hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+struct DsaIndexerLaunch {
+  int batch, num_rows, max_q_per_req, max_ctx_len, bt_stride;
+  const int32_t* q_offsets;
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  int n_heads, head_dim, topk, dtype;
+  const void* q;
+  const float* q_scale;
+  const float* weights;
+  const void* k_cache;
+  const float* k_scale;
+  int32_t* out_idx;
+  // workspace
+  uint32_t* hist;      // [rows][2048]
+  float* scores;       // [rows][score_stride]
+  int64_t score_stride;
+};
+
+struct DsaSfaLaunch {
+  int batch, num_rows;
+  const int32_t* q_offsets;
+  const int32_t* block_table;
+  int bt_stride;
+  int n_heads, dtype;
+  float scale;
+  const void* q;
+  const void* kv_cache;
+  const int32_t* idx;
+  int topk;
+  void* out;
+  float* lse;
+  // split-KV partials (used when n_split > 1)
+  int n_split, rows_per_split;
+  float* part_o;       // [n_split][rows][H][512]
+  float* part_lse;     // [n_split][rows][H]
+};
+
+hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s);
+hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s);

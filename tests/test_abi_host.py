@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+``include/dsa.h`` declares, and rejects bad arguments on the host before any
+device work (no call here passes validation, so nothing is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lightning_indexer_top_02_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = dsa.load()
+    names = declared_functions()
+    assert "dsa_indexer_topk" in names and "dsa_sparse_attn" in names and "dsa_fused_decode" in names
+    for n in names:
+        assert hasattr(lib, n), f"libdsa.so does not export {n}"
+
+
+def test_version_and_status_strings():
+    assert dsa.abi_version() == 1
+    for s in range(6):
+        assert dsa.status_string(s) and dsa.status_string(s) != "unknown status"
+    assert dsa.status_string(99) == "unknown status"
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def good_paged(**kw):
+    p = dict(batch=2, num_q_tokens=5, max_q_per_req=4, max_ctx_len=1000, max_pages_per_req=16,
+             page_size=64, num_pages=40, q_offsets=FAKE, ctx_lens=FAKE, block_table=FAKE)
+    p.update(kw)
+    return dsa.Paged(**p)
+
+
+def good_indexer(**kw):
+    p = dict(n_heads=64, head_dim=128, topk=256, dtype=1, q=FAKE, q_scale=None, weights=FAKE,
+             k_cache=FAKE, k_scale=None)
+    p.update(kw)
+    return dsa.Indexer(**p)
+
+
+def good_sfa(**kw):
+    p = dict(n_heads=128, qk_dim=576, v_dim=512, dtype=1, scale=1 / 24, q=FAKE, kv_cache=FAKE,
+             out=FAKE, lse=None)
+    p.update(kw)
+    return dsa.Sfa(**p)
+
+
+def call_indexer(paged, idx, out=FAKE, ws=None, ws_bytes=0):
+    return dsa.load().dsa_indexer_topk(ctypes.byref(paged), ctypes.byref(idx), out, ws, ws_bytes, None)
+
+
+def call_sfa(paged, sfa, idx=FAKE, topk=256, ws=None, ws_bytes=0):
+    return dsa.load().dsa_sparse_attn(ctypes.byref(paged), ctypes.byref(sfa), idx, topk, ws, ws_bytes, None)
+
+
+def call_fused(paged, idx, sfa, ws=None, ws_bytes=0):
+    return dsa.load().dsa_fused_decode(ctypes.byref(paged), ctypes.byref(idx), ctypes.byref(sfa), None, ws,
+                                       ws_bytes, None)
+
+
+BAD_PAGED = [dict(batch=0), dict(num_q_tokens=0), dict(page_size=32), dict(max_pages_per_req=15),
+             dict(q_offsets=None), dict(ctx_lens=None), dict(block_table=None), dict(max_q_per_req=0),
+             dict(max_q_per_req=6), dict(num_pages=0), dict(num_q_tokens=1)]
+
+
+@pytest.mark.parametrize("kw", BAD_PAGED, ids=[str(k) for k in BAD_PAGED])
+def test_bad_paging_rejected(kw):
+    assert call_indexer(good_paged(**kw), good_indexer()) == 1
+    assert call_sfa(good_paged(**kw), good_sfa()) == 1
+    assert call_fused(good_paged(**kw), good_indexer(), good_sfa()) == 1
+    assert dsa.load().dsa_indexer_topk_workspace_size(ctypes.byref(good_paged(**kw)),
+                                                      ctypes.byref(good_indexer())) == 0
+
+
+BAD_INDEXER = [(dict(q=None), 1), (dict(weights=None), 1), (dict(k_cache=None), 1), (dict(topk=0), 1),
+               (dict(n_heads=0), 1), (dict(dtype=7), 1), (dict(dtype=2), 1),  # fp8 without scales
+               (dict(dtype=2, q_scale=FAKE), 1), (dict(n_heads=65), 2), (dict(topk=4097), 2),
+               (dict(head_dim=96), 2), (dict(dtype=0, n_heads=64, head_dim=128), 2)]
+
+
+@pytest.mark.parametrize("kw,status", BAD_INDEXER, ids=[str(k) for k, _ in BAD_INDEXER])
+def test_bad_indexer_rejected(kw, status):
+    assert call_indexer(good_paged(), good_indexer(**kw)) == status
+
+
+def test_indexer_null_output_rejected():
+    assert call_indexer(good_paged(), good_indexer(), out=None) == 1
+
+
+BAD_SFA = [(dict(q=None), 1), (dict(kv_cache=None), 1), (dict(out=None), 1), (dict(dtype=2), 1),
+           (dict(v_dim=600), 1), (dict(scale=float("nan")), 1), (dict(qk_dim=512), 2),
+           (dict(n_heads=24), 2), (dict(n_heads=144), 2)]
+
+
+@pytest.mark.parametrize("kw,status", BAD_SFA, ids=[str(k) for k, _ in BAD_SFA])
+def test_bad_sfa_rejected(kw, status):
+    assert call_sfa(good_paged(), good_sfa(**kw)) == status
+
+
+def test_sfa_topk_bounds():
+    assert call_sfa(good_paged(), good_sfa(), topk=0) == 1
+    assert call_sfa(good_paged(), good_sfa(), topk=5000) == 2
+    assert call_sfa(good_paged(), good_sfa(), idx=None) == 1
+
+
+def test_workspace_too_small_rejected_before_device():
+    lib = dsa.load()
+    p, i, s = good_paged(), good_indexer(), good_sfa()
+    need = lib.dsa_indexer_topk_workspace_size(ctypes.byref(p), ctypes.byref(i))
+    assert need > 0
+    assert call_indexer(p, i, ws=FAKE, ws_bytes=need - 1) == 3
+    assert call_indexer(p, i, ws=None, ws_bytes=need) == 3
+    assert call_indexer(p, i, ws=FAKE + 8, ws_bytes=need) == 3  # misaligned
+    need_f = lib.dsa_fused_decode_workspace_size(ctypes.byref(p), ctypes.byref(i), ctypes.byref(s))
+    assert need_f > need
+    assert call_fused(p, i, s, ws=FAKE, ws_bytes=need_f - 1) == 3
+
+
+def test_workspace_sizes():
+    lib = dsa.load()
+    p = good_paged(num_q_tokens=5, max_ctx_len=1000)
+    need = lib.dsa_indexer_topk_workspace_size(ctypes.byref(p), ctypes.byref(good_indexer()))
+    # histogram [T][2048] u32 + scores [T][round_up(L, 256)] f32, each 256-aligned
+    assert need == 5 * 2048 * 4 + 5 * 1024 * 4
+    # one row of 128 heads at small batch splits the index list; fp32 never does
+    one = good_paged(batch=1, num_q_tokens=1, max_q_per_req=1)
+    s_bf16 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa()), 2048)
+    assert s_bf16 > 0 and s_bf16 % 256 == 0
+    s_f32 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa(dtype=0, n_heads=16)), 256)
+    assert s_f32 == 0

@@ -1,0 +1,147 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (see parity.py): Top-K sets bit-exact in exact mode, else equal up to
+the 1e-3 threshold band; outputs within 2e-2 (bf16/fp32 storage) of the
+oracle run on the GPU's own indices; the fused call equals the two separate
+calls bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from lightning_indexer_top_02_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, **kw):
+    print(f"\n[case] {case.name} seed={case.seed} lens={case.ctx_lens.tolist()[:8]} "
+          f"T={case.num_tokens} K={case.topk}", flush=True)
+    case = parity.to_device(case)
+    stats = parity.check_case(case, **kw)
+    print(f"[ok] {case.name}: {stats}", flush=True)
+    return case, stats
+
+
+# --- tiny decode (fp32 indexer 4 x 64, fp32 SFA 16 heads, L = 4096, K = 256) --
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_tiny_decode(exact):
+    _run(inputs.tiny_decode(exact=exact))
+
+
+def test_tiny_decode_page_permutation_is_bit_identical():
+    base = parity.to_device(inputs.tiny_decode())
+    perm = parity.to_device(inputs.permute_pages(inputs.tiny_decode(), seed=5))
+    i1, o1, l1 = parity.gpu_fused_decode(base)
+    i2, o2, l2 = parity.gpu_fused_decode(perm)
+    assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeat_runs_are_bit_identical():
+    case = parity.to_device(inputs.decode_32k(ctx_lens=[9000]))
+    a = parity.gpu_fused_decode(case)
+    b = parity.gpu_fused_decode(case)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# --- 32K decode (bf16 64 x 128, 128 SFA heads, K = 2048) ----------------------
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_decode_32k(exact):
+    _run(inputs.decode_32k(exact=exact))
+
+
+# --- ragged lengths, several query tokens per request, K above some lengths ----
+RAGGED = [1, 63, 64, 65, 300, 4097, 257]
+RAGGED_NQ = [1, 1, 2, 4, 3, 1, 4]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_ragged_wide(dtype, exact):
+    _run(inputs.make_case(name=f"ragged_wide_{dtype}", seed=77, ctx_lens=RAGGED, n_q=RAGGED_NQ,
+                          idx_dtype=dtype, n_heads_idx=64, head_dim_idx=128, topk=256, exact=exact,
+                          sfa_dtype="bf16", n_heads_sfa=128))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_ragged_narrow(dtype, exact):
+    _run(inputs.make_case(name=f"ragged_narrow_{dtype}", seed=78, ctx_lens=RAGGED, n_q=RAGGED_NQ,
+                          idx_dtype=dtype, n_heads_idx=4, head_dim_idx=64, topk=100, exact=exact,
+                          w_dist="uniform", sfa_dtype="bf16" if dtype != "f32" else "f32",
+                          n_heads_sfa=16, sfa_std=1.0))
+
+
+@pytest.mark.parametrize("heads", [5, 17, 48])
+def test_odd_indexer_head_counts(heads):
+    _run(inputs.make_case(name=f"heads{heads}", seed=79, ctx_lens=[5000, 777], n_q=[1, 2],
+                          idx_dtype="bf16", n_heads_idx=heads, head_dim_idx=64, topk=512, exact=True,
+                          sfa_dtype="bf16", n_heads_sfa=32))
+
+
+def test_k_equal_and_above_context():
+    for K in (640, 641, 700):
+        _run(inputs.make_case(name=f"k{K}", seed=80, ctx_lens=[640], n_q=1, idx_dtype="bf16",
+                              n_heads_idx=64, head_dim_idx=128, topk=K, sfa_dtype="bf16", n_heads_sfa=64))
+
+
+# --- batched fp8 route, speculative verify, chunked prefill (reduced sizes) ----
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_batched_fp8_narrow_small(exact):
+    _run(inputs.batched_decode_fp8(batch=8, lo=2000, hi=20000, exact=exact))
+
+
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_spec_verify_small(exact):
+    _run(inputs.spec_verify(batch=2, ctx=20000, exact=exact))
+
+
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_chunked_prefill_small(exact):
+    _run(inputs.chunked_prefill(prefix=1000, new=300, exact=exact))
+
+
+def test_causal_planted_future_keys_never_selected():
+    """Keys after a row's position made huge must never be selected."""
+    case = inputs.spec_verify(batch=1, ctx=3000, exact=True)
+    bt = case.block_table
+    k = case.k_cache.clone()
+    for t in range(2997, 3000):
+        k[bt[0, t // 64], t % 64] = 0x70  # e4m3 code of 128
+    q = case.q_idx.view(torch.float8_e4m3fn).float().abs().to(torch.float8_e4m3fn).view(torch.uint8)
+    w = case.weights.abs() + 1
+    import dataclasses
+    case = dataclasses.replace(case, k_cache=k, q_idx=q.contiguous(), weights=w)
+    _, _ = _run(case)
+    idx = parity.gpu_indexer_topk(parity.to_device(case)).cpu()
+    for j in range(4):
+        pos = 2996 + j
+        row = set(idx[j][idx[j] >= 0].tolist())
+        assert max(row) <= pos
+        assert {t for t in range(2997, 3000) if t <= pos} <= row
+
+
+# --- sparse attention alone, on the oracle's indices ---------------------------
+def test_sfa_on_oracle_indices_with_padding():
+    case = parity.to_device(inputs.decode_32k(ctx_lens=[9000, 1500, 200], n_q=[1, 2, 1], topk=1024))
+    o_idx, _ = parity.oracle_indexer(case)
+    o_idx[1, 700:] = -1     # a short list
+    o_idx[2, :] = -1        # nothing selected
+    g_out, g_lse = parity.gpu_sparse_attn(case, torch.from_numpy(o_idx).cuda())
+    r_out, r_lse = parity.oracle_sfa(case, o_idx)
+    print(parity.compare_out(g_out, r_out, "bf16", gpu_lse=g_lse, ora_lse=r_lse))
+    assert np.all(parity.out_to_f64(g_out, "bf16")[2] == 0.0)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 48, 64, 80, 128])
+def test_sfa_head_counts(heads):
+    case = parity.to_device(inputs.make_case(name=f"sfa{heads}", seed=81, ctx_lens=[3000, 2500], n_q=[1, 3],
+                                             idx_dtype="bf16", n_heads_idx=16, head_dim_idx=64, topk=512,
+                                             sfa_dtype="bf16", n_heads_sfa=heads))
+    idx = parity.gpu_indexer_topk(case)
+    g_out, g_lse = parity.gpu_sparse_attn(case, idx)
+    r_out, r_lse = parity.oracle_sfa(case, idx)
+    print(parity.compare_out(g_out, r_out, "bf16", gpu_lse=g_lse, ora_lse=r_lse))
