@@ -1,0 +1,309 @@
+"""Benchmark of the DSA sparse-attention step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: indexer scoring,
+head weighting, Top-K selection and sparse attention (``dsa_fused_decode``).
+Inputs are seeded synthetic tensors already resident in HBM; the caches are
+replicated R times (different addresses, same content) and the steps rotate
+over the replicas so the 256 MB Infinity Cache cannot hold the working set.
+
+Prints ONE JSON line (rank 0).  ``roofline`` is for the dominant stage; its
+duration is measured with HIP events recorded on the stream the library
+launches on.  ``cpu_baseline`` times the CPU oracle on the host cores on a
+bounded sample of the same workload and checks the GPU result against it.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from lightning_indexer_top_02_amd import dsa, inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "DSA decode tokens/s + HBM GB/s (% peak) at 32K ctx; prefill indexer MFMA util"
+
+WORKLOADS = {
+    "decode_32k": dict(
+        make=lambda dev, batch=1: inputs.decode_32k(batch=batch, device=dev),
+        desc="DSA decode step: batch {batch}, 1 query token, context 32768 in 512 shuffled 64-token "
+             "pages; indexer 64 heads x 128 bf16, Top-K 2048; sparse attention 128 heads x "
+             "(512+64) bf16 latent, bf16 out, fp32 accumulation"),
+    "tiny_decode": dict(
+        make=lambda dev, batch=1: inputs.tiny_decode(device=dev),
+        desc="DSA decode step: batch 1, context 4096, fp32 indexer 4 x 64, Top-K 256, fp32 "
+             "sparse attention 16 heads"),
+    "batched_fp8_narrow": dict(
+        make=lambda dev, batch=64: inputs.batched_decode_fp8(device=dev, batch=batch),
+        desc="DSA decode step: batch {batch}, contexts U[4096,131072], fp8 indexer 4 x 64, Top-K 2048, "
+             "bf16 sparse attention 16 heads"),
+    "batched_fp8_wide": dict(
+        make=lambda dev, batch=64: inputs.batched_decode_fp8(device=dev, batch=batch, wide=True),
+        desc="DSA decode step: batch {batch}, contexts U[4096,131072], fp8 indexer 64 x 128, Top-K "
+             "2048, bf16 sparse attention 128 heads"),
+    "spec_verify": dict(
+        make=lambda dev, batch=16: inputs.spec_verify(device=dev, batch=batch),
+        desc="DSA speculative-verify step: {batch} requests x 4 causal query tokens at context "
+             "262144, fp8 indexer 64 x 128, Top-K 2048, bf16 sparse attention 128 heads"),
+}
+
+
+def elem_bytes(dtype):
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+
+
+def algorithmic_bytes(case: inputs.Case):
+    """Bytes the method itself must move per step, per stage.
+
+    indexer: every visible key once per request (head dim x element size,
+             plus a 4-byte scale for fp8), q, w (and q scales), the block
+             table, and the Top-K indices written.
+    sparse attention: the indices read, K gathered latent rows per query row,
+             q and the output.
+    """
+    lens = case.ctx_lens.cpu().tolist()
+    T, K = case.num_tokens, case.topk
+    eK = elem_bytes(case.idx_dtype)
+    key_row = case.head_dim_idx * eK + (4 if case.idx_dtype == "fp8" else 0)
+    H = case.n_heads_idx
+    idx_bytes = (sum(lens) * key_row + T * H * case.head_dim_idx * eK + T * H * 4 * (2 if case.idx_dtype == "fp8" else 1)
+                 + sum((L + 63) // 64 for L in lens) * 4 + T * K * 4)
+    eS = elem_bytes(case.sfa_dtype)
+    sfa_bytes = (T * K * 4 + T * K * case.qk_dim * eS + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eS)
+    idx_flops = 2 * sum(lens) * H * case.head_dim_idx  # upper bound (every row of a request sees <= L)
+    sfa_flops = 2 * T * K * case.n_heads_sfa * (case.qk_dim + case.v_dim)
+    return {"indexer": idx_bytes, "sparse_attn": sfa_bytes, "total": idx_bytes + sfa_bytes,
+            "indexer_flops": idx_flops, "sparse_attn_flops": sfa_flops}
+
+
+class Step:
+    """Preallocated buffers for one workload and R cache replicas."""
+
+    def __init__(self, case: inputs.Case, replicas: int):
+        self.case = case
+        self.R = replicas
+        self.k = [case.k_cache] + [case.k_cache.clone() for _ in range(replicas - 1)]
+        self.ks = ([case.k_scale] + [case.k_scale.clone() for _ in range(replicas - 1)]
+                   if case.k_scale is not None else [None] * replicas)
+        self.kv = [case.kv_cache] + [case.kv_cache.clone() for _ in range(replicas - 1)]
+        dev = case.q_idx.device
+        T, K = case.num_tokens, case.topk
+        self.idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        odt = torch.float32 if case.sfa_dtype == "f32" else torch.int16
+        self.out = torch.empty((T, case.n_heads_sfa, case.v_dim), dtype=odt, device=dev)
+        self.lse = torch.empty((T, case.n_heads_sfa), dtype=torch.float32, device=dev)
+        self.paged = dsa.make_paged(case.q_offsets, case.ctx_lens, case.block_table, case.num_pages,
+                                    max_q_per_req=case.max_q_per_req, max_ctx_len=case.max_ctx,
+                                    num_q_tokens=T)
+        self.indexers = [dsa.make_indexer(case.q_idx, case.weights, self.k[r], K, case.idx_dtype,
+                                          q_scale=case.q_scale, k_scale=self.ks[r]) for r in range(replicas)]
+        self.sfas = [dsa.make_sfa(case.q_sfa, self.kv[r], self.out, case.scale, case.sfa_dtype, lse=self.lse,
+                                  v_dim=case.v_dim) for r in range(replicas)]
+        n_fused = dsa.fused_decode_workspace_size(self.paged, self.indexers[0], self.sfas[0])
+        n_idx = dsa.indexer_topk_workspace_size(self.paged, self.indexers[0])
+        n_sfa = dsa.sparse_attn_workspace_size(self.paged, self.sfas[0], K)
+        self.ws = dsa.new_workspace(max(n_fused, n_idx, n_sfa), dev)
+        self.ws2 = dsa.new_workspace(n_sfa, dev)
+
+    def fused(self, s: int, stream):
+        r = s % self.R
+        dsa.fused_decode(self.paged, self.indexers[r], self.sfas[r], topk_idx=self.idx, workspace=self.ws,
+                         stream=stream)
+
+    def indexer(self, s: int, stream):
+        dsa.indexer_topk(self.paged, self.indexers[s % self.R], self.idx, workspace=self.ws, stream=stream)
+
+    def sparse_attn(self, s: int, stream):
+        dsa.sparse_attn(self.paged, self.sfas[s % self.R], self.idx, workspace=self.ws2, stream=stream)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter data taken on other sources is stale."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "lightning_indexer_top_02_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel factor), or
+    None when no summary exists for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d["bytes_per_launch"]
+
+
+def calibrate_copy(mb: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    n = mb * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def time_steps(fn, steps, stream):
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(steps):
+        fn(s, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def stage_breakdown(step: Step, steps, stream):
+    """Average duration of each stage, from HIP events around each call."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        evs[s][0].record(stream)
+        step.indexer(s, stream)
+        evs[s][1].record(stream)
+        step.sparse_attn(s, stream)
+        evs[s][2].record(stream)
+    torch.cuda.synchronize()
+    idx = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    sfa = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return idx, sfa
+
+
+def cpu_baseline(case: inputs.Case, step: Step, budget_s: float):
+    """The CPU oracle on a bounded sample of the workload (whole steps, or a
+    subset of query rows), on this host's cores; also checks the GPU result of
+    replica 0 on the same sample."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import parity
+
+    oracle.build(force=False)
+    threads = len(os.sched_getaffinity(0))
+    T = case.num_tokens
+    rows = list(range(T)) if T <= 4 else sorted({0, T - 1, T // 2, T // 3})
+    sub = parity.rows_subcase(case, rows)
+    # GPU result of the same rows (replica 0)
+    stream = torch.cuda.current_stream()
+    step.fused(0, stream)
+    torch.cuda.synchronize()
+    g_idx = step.idx.clone()
+    g_out = step.out.clone()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        o_idx, o_sc = parity.oracle_indexer(sub, nthreads=threads)
+        o_out, _ = parity.oracle_sfa(sub, o_idx, nthreads=threads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    rows_per_s = n * len(rows) / el
+    status = "ok"
+    try:
+        parity.check_rows(case, g_idx, g_out, rows, nthreads=threads)
+    except AssertionError as e:
+        status = f"MISMATCH: {e}"
+    return {"value": rows_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {T} query rows of the same workload (indexer over the full context, "
+                      f"Top-K, sparse attention), repeated {n} times in {el:.1f} s with OpenMP over "
+                      f"{threads} host threads",
+            "parity_vs_gpu": status}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to exceed 512 MB)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain MB-sized device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 10)
+        return
+
+    w = WORKLOADS[args.workload]
+    kw = {} if args.batch is None else {"batch": args.batch}
+    case = w["make"](dev, **kw)
+    state_bytes = sum(x.numel() * x.element_size() for x in (case.k_cache, case.kv_cache, case.k_scale)
+                      if x is not None)
+    R = args.replicas or max(1, min(32, math.ceil(512e6 / state_bytes)))
+    step = Step(case, R)
+    ab = algorithmic_bytes(case)
+    stream = torch.cuda.current_stream()
+
+    for s in range(args.warmup):
+        step.fused(s, stream)
+    torch.cuda.synchronize()
+    ms = time_steps(step.fused, args.steps, stream)
+    t_idx, t_sfa = stage_breakdown(step, args.steps, stream)
+
+    T = case.num_tokens
+    tokens_per_s = T / (ms * 1e-3)
+    dom = "indexer" if t_idx >= t_sfa else "sparse_attn"
+    dom_ms = t_idx if dom == "indexer" else t_sfa
+    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
+    kname = "indexer_topk" if dom == "indexer" else "sparse_attn"
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.idx_dtype if case.idx_dtype == case.sfa_dtype else f"{case.idx_dtype}+{case.sfa_dtype}",
+        "data": "synthetic",
+        "config": {"workload": w["desc"].format(batch=case.batch), "name": case.name, "batch": case.batch,
+                   "query_tokens": T, "max_context": case.max_ctx, "topk": case.topk,
+                   "cache_replicas": R, "parallelism": "single GPU"},
+        "hbm_gbs_step": ab["total"] / (ms * 1e-3) / 1e9,
+        "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa},
+        "roofline": {"kernel": kname, "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kname, args.workload),
+                     "algorithmic_bytes": ab[dom]},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(case, step, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,9 +24,11 @@
  *   Calls only enqueue work on it and return; results are visible once the
  *   stream has reached that point.
  * Workspace: `ws` is caller-owned device memory of at least the size the
- *   matching *_workspace_size call returns, 256-byte aligned.  The library
- *   initializes whatever part it needs inside the call (graph-capture safe:
- *   no memset nodes).  Concurrent calls must not share a workspace.
+ *   matching *_workspace_size call returns, 256-byte aligned.  It must be
+ *   zero-filled once before its first use (dsa_workspace_init does that with
+ *   a kernel, no memset node); every call leaves its counters and histograms
+ *   zero again, so a workspace is reused across calls without re-filling.
+ *   Concurrent calls must not share a workspace.
  * Errors: arguments are validated on the host before anything is enqueued;
  *   on a bad argument the call returns a non-zero dsa_status_t and enqueues
  *   nothing.  Device data (page ids, lengths) is trusted: a page id outside
@@ -97,7 +99,14 @@ typedef struct {
     const float *weights;      /* [T][H_I] head-importance weights */
     const void *k_cache;       /* [num_pages][64][D_I] */
     const float *k_scale;      /* [num_pages][64] for FP8_E4M3, else NULL */
+    int32_t flags;             /* 0, or DSA_INDEXER_TWO_PASS */
 } dsa_indexer_t;
+
+/* Indexer flag: always take the two-pass route (scoring kernel, then one
+ * selection workgroup per row) instead of the single fused kernel.  Results
+ * are identical; the fused kernel is used by default when every request has
+ * at most 4 query rows and max_ctx_len <= 32768. */
+#define DSA_INDEXER_TWO_PASS 1
 
 /* Sparse flash attention over a shared MLA latent cache: the key of a
  * position is its whole row (qk_dim = 576 = 512 latent + 64 rope), the value
@@ -143,6 +152,9 @@ size_t dsa_fused_decode_workspace_size(const dsa_paged_t *paged, const dsa_index
 dsa_status_t dsa_fused_decode(const dsa_paged_t *paged, const dsa_indexer_t *idx,
                               const dsa_sfa_t *sfa, int32_t *topk_idx,
                               void *ws, size_t ws_bytes, void *stream);
+
+/* Zero-fill a workspace (enqueued on `stream`).  ws_bytes % 4 == 0. */
+dsa_status_t dsa_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 const char *dsa_status_string(dsa_status_t status);
 int32_t dsa_abi_version(void);

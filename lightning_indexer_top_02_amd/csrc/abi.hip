@@ -38,6 +38,7 @@ dsa_status_t check_indexer(const dsa_paged_t* pg, const dsa_indexer_t* x) {
   if (x->n_heads < 1 || x->head_dim < 1 || x->topk < 1) return DSA_ERR_INVALID_ARG;
   if (x->dtype != DSA_F32 && x->dtype != DSA_BF16 && x->dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
   if (x->dtype == DSA_FP8_E4M3 && (!x->q_scale || !x->k_scale)) return DSA_ERR_INVALID_ARG;
+  if (x->flags & ~DSA_INDEXER_TWO_PASS) return DSA_ERR_INVALID_ARG;
   if (x->n_heads > kMaxIdxHeads || x->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
   if (x->head_dim != 64 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (x->dtype == DSA_F32 && x->n_heads * x->head_dim > 4096) return DSA_ERR_UNSUPPORTED;
@@ -57,17 +58,22 @@ dsa_status_t check_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) 
 }
 
 // --- workspace plans ---------------------------------------------------------
+// Indexer workspace: arrival counters [batch] u32 | digit histograms
+// [rows][kHistStride] u32 | scores or score keys [rows][round_up(L_max, 256)].
+// The first two regions are zero between calls.
 struct IndexerPlan {
   int64_t score_stride;
-  size_t hist_off, scores_off, total;
+  size_t ctrl_off, hist_off, scores_off, total;
 };
 
 IndexerPlan plan_indexer(const dsa_paged_t* pg) {
   IndexerPlan p;
+  const size_t T = (size_t)pg->num_q_tokens;
   p.score_stride = round_up(pg->max_ctx_len, 256);
-  p.hist_off = 0;
-  p.scores_off = align_up((size_t)pg->num_q_tokens * dsa::kHistBins * 4);
-  p.total = p.scores_off + align_up((size_t)pg->num_q_tokens * p.score_stride * 4);
+  p.ctrl_off = 0;
+  p.hist_off = align_up(4 * (size_t)pg->batch);
+  p.scores_off = p.hist_off + align_up(T * dsa::kHistStride * 4);
+  p.total = p.scores_off + align_up(T * p.score_stride * 4);
   return p;
 }
 
@@ -135,9 +141,11 @@ DsaIndexerLaunch indexer_args(const dsa_paged_t* pg, const dsa_indexer_t* x, int
   a.k_cache = x->k_cache;
   a.k_scale = x->k_scale;
   a.out_idx = out;
+  a.counters = reinterpret_cast<uint32_t*>(ws + plan.ctrl_off);
   a.hist = reinterpret_cast<uint32_t*>(ws + plan.hist_off);
   a.scores = reinterpret_cast<float*>(ws + plan.scores_off);
   a.score_stride = plan.score_stride;
+  a.force_two_pass = (x->flags & DSA_INDEXER_TWO_PASS) != 0;
   return a;
 }
 
@@ -170,9 +178,26 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
   return ws && have >= need && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
 }
 
+__global__ void zero_words(uint32_t* x, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    x[i] = 0u;
+}
+
 }  // namespace
 
 extern "C" {
+
+dsa_status_t dsa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes % 4 != 0 || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return DSA_ERR_INVALID_ARG;
+  if (ws_bytes == 0) return DSA_OK;
+  dsa_status_t st = check_device();
+  if (st != DSA_OK) return st;
+  const size_t n = ws_bytes / 4;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(zero_words, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(ws), n);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 

@@ -10,8 +10,8 @@ namespace dsa {
 constexpr int kPage = 64;          // tokens per cache page
 constexpr int kQkDim = 576;        // latent (512) + rope (64)
 constexpr int kVDim = 512;
-constexpr int kHistBits = 11;      // first radix level: top 11 bits of the key
-constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistBins = 2048;    // bins of the widest radix digit (11 bits)
+constexpr int kHistStride = 3 * kHistBins;  // per-row digit histograms in the workspace
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -71,9 +71,11 @@ struct DsaIndexerLaunch {
   const float* k_scale;
   int32_t* out_idx;
   // workspace
-  uint32_t* hist;      // [rows][2048]
-  float* scores;       // [rows][score_stride]
+  uint32_t* counters;  // [batch] arrival counters of the fused kernel, zero between calls
+  uint32_t* hist;      // [rows][kHistStride] digit histograms (two-pass), zero between calls
+  float* scores;       // [rows][score_stride] scores (two-pass) or score keys (fused)
   int64_t score_stride;
+  bool force_two_pass; // skip the fused kernel
 };
 
 struct DsaSfaLaunch {
@@ -96,4 +98,5 @@ struct DsaSfaLaunch {
 };
 
 hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s);
+hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s);

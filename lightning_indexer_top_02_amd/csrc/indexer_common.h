@@ -1,0 +1,166 @@
+// indexer_common.h -- lightning-indexer scoring shared by the indexer kernels.
+//
+// Score of position t for one query row ("Optimizing Inference for Hybrid
+// Attention Architectures: From Operator Fusion to Sequence Sharding",
+// section "Breaking Down the Computational Path of Hybrid Attention", item 1):
+//     s_t = sum_h w_h * max(q_h . k_t, 0)
+// fp8 route: q_h . k_t = (q̂_h . k̂_t) * sq_h * sk_t with positive scales, so
+// sq_h is folded into w_h and sk_t applied after the head sum.
+//
+// bf16/fp8 keys use MFMA 16x16x32: logits D[m = head][n = position] with the
+// query rows as A (from LDS) and the keys as B, loaded straight from the page
+// in HBM (each lane reads 8 consecutive elements of one key row).  fp32 keys
+// use VALU, one thread per position.
+#pragma once
+
+#include <type_traits>
+
+#include "dsa_device.h"
+
+namespace dsa {
+
+// ReLU that lets NaN through (NaN < 0 is false), so a stray read of poisoned
+// cache data shows up in the result instead of vanishing.
+__device__ __forceinline__ float relu_keep_nan(float v) { return v < 0.f ? 0.f : v; }
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(uint2 a, uint2 b, f32x4 c) {
+  long la = __builtin_bit_cast(long, a), lb = __builtin_bit_cast(long, b);
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(la, lb, c, 0, 0, 0);
+}
+
+// Storage geometry of one indexer variant: DT 0 = fp32, 1 = bf16, 2 = fp8.
+template <int DT, int D>
+struct IdxGeom {
+  static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);   // bytes per element
+  static constexpr int QSTRIDE = DT == 0 ? D * 4 : D * ES + 16;  // LDS bytes per (row, head)
+  using frag_t = typename std::conditional<DT == 1, uint4, uint2>::type;
+};
+
+// LDS bytes for the staged queries and weights of `rows` rows.
+template <int DT, int D>
+__host__ __device__ constexpr size_t query_lds_bytes(int rows, int Hpad) {
+  return (size_t)rows * Hpad * (IdxGeom<DT, D>::QSTRIDE + 4);
+}
+
+// Stage `nrows` query rows starting at global row `row0` (heads past H are
+// zero) and their weights (times the q scale for fp8) into LDS.
+template <int DT, int D, int NT>
+__device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, const float* q_scale,
+                              const float* w, int row0, int nrows, int H, int Hpad) {
+  using G = IdxGeom<DT, D>;
+  constexpr int CPH = D * G::ES / 16;  // 16-byte chunks per head
+  const unsigned char* qg = static_cast<const unsigned char*>(q);
+  const int total = nrows * Hpad * CPH;
+  for (int c = threadIdx.x; c < total; c += NT) {
+    const int r = c / (Hpad * CPH);
+    const int rem = c - r * Hpad * CPH;
+    const int h = rem / CPH, part = rem - h * CPH;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (h < H) v = *reinterpret_cast<const uint4*>(qg + ((int64_t)(row0 + r) * H + h) * (D * G::ES) + part * 16);
+    *reinterpret_cast<uint4*>(qs + (r * Hpad + h) * G::QSTRIDE + part * 16) = v;
+  }
+  for (int c = threadIdx.x; c < nrows * Hpad; c += NT) {
+    const int r = c / Hpad, h = c - r * Hpad;
+    float wv = 0.f;
+    if (h < H) {
+      const int64_t o = (int64_t)(row0 + r) * H + h;
+      wv = w[o];
+      if (DT == 2) wv *= q_scale[o];  // q scale > 0 folds through the ReLU
+    }
+    wsm[r * Hpad + h] = wv;
+  }
+}
+
+// One wave scores NPT tiles of 16 positions of one page (slots slot0 ..
+// slot0 + 16 NPT - 1) for `nrows` staged rows.  emit(r, slot, score) runs on
+// lanes 0..15 for slots slot0 + pt * 16 + lane.
+template <int DT, int D, int NPT, class Emit>
+__device__ __forceinline__ void score_tiles_mfma(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
+                                                 const unsigned char* kpage, const float* kscale_page,
+                                                 int slot0, Emit&& emit) {
+  using G = IdxGeom<DT, D>;
+  using frag_t = typename G::frag_t;
+  constexpr int KS = D / 32;  // contraction steps
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  frag_t kf[NPT][KS];
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[pt][ks] =
+          *reinterpret_cast<const frag_t*>(kpage + ((slot0 + pt * 16 + l16) * D + ks * 32 + g * 8) * G::ES);
+  float kscale[NPT];
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt) kscale[pt] = (DT == 2) ? kscale_page[slot0 + pt * 16 + l16] : 1.f;
+
+  for (int r = 0; r < nrows; ++r) {
+    float sacc[NPT];
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) sacc[pt] = 0.f;
+    for (int ht = 0; ht < Hpad / 16; ++ht) {
+      f32x4 acc[NPT];
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const unsigned char* qrow = qs + (r * Hpad + ht * 16 + l16) * G::QSTRIDE + g * 8 * G::ES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const frag_t a = *reinterpret_cast<const frag_t*>(qrow + ks * 32 * G::ES);
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, kf[pt][ks], acc[pt]);
+      }
+      // acc[pt][i] = logit of head ht*16 + 4g + i at slot slot0 + pt*16 + l16
+      const float* wr = wsm + r * Hpad + ht * 16 + 4 * g;
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[pt] += wr[i] * relu_keep_nan(acc[pt][i]);
+    }
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) {
+      float s = sacc[pt];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (g == 0) emit(r, slot0 + pt * 16 + l16, s * kscale[pt]);
+    }
+  }
+}
+
+// One wave scores the 64 positions of one page.
+template <int DT, int D, class Emit>
+__device__ __forceinline__ void score_page_mfma(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
+                                                const unsigned char* kpage, const float* kscale_page,
+                                                Emit&& emit) {
+  score_tiles_mfma<DT, D, 4>(qs, wsm, Hpad, nrows, kpage, kscale_page, 0, emit);
+}
+
+// One thread scores one fp32 key row for `nrows` staged rows.
+template <int D, class Emit>
+__device__ __forceinline__ void score_pos_f32(const float* qs, const float* wsm, int H, int nrows,
+                                              const float* krow_ptr, Emit&& emit) {
+  const float4* krow = reinterpret_cast<const float4*>(krow_ptr);
+  float4 kr[D / 4];
+#pragma unroll
+  for (int d = 0; d < D / 4; ++d) kr[d] = krow[d];
+  for (int r = 0; r < nrows; ++r) {
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) {
+      const float4* qh = reinterpret_cast<const float4*>(qs + (r * H + h) * D);
+      float logit = 0.f;
+#pragma unroll
+      for (int d = 0; d < D / 4; ++d) {
+        const float4 qv = qh[d];
+        logit = fmaf(qv.x, kr[d].x, logit);
+        logit = fmaf(qv.y, kr[d].y, logit);
+        logit = fmaf(qv.z, kr[d].z, logit);
+        logit = fmaf(qv.w, kr[d].w, logit);
+      }
+      s = fmaf(wsm[r * H + h], relu_keep_nan(logit), s);
+    }
+    emit(r, s);
+  }
+}
+
+}  // namespace dsa

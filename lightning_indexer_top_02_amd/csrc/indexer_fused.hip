@@ -1,0 +1,213 @@
+// indexer_fused.hip -- lightning indexer, latency path (gfx950): scoring,
+// head weighting and Top-K selection in one kernel launch.
+//
+// The pages fuse the three indexer steps into one operator that reads the
+// paged K cache directly and outputs only the Top-K indices ("Day0 Inference
+// Support and Performance Optimization for New LLM Architectures", section
+// III, 3.1; "Optimizing Inference for Hybrid Attention Architectures: From
+// Operator Fusion to Sequence Sharding", section "Fusing Index Screening with
+// Multi-Stream Orchestration").  On one MI355X a single decode row is too
+// short for one workgroup to stream at HBM speed, and measured cross-XCD
+// synchronisation inside a kernel costs tens of microseconds per round (every
+// workgroup of a team re-reading one shared histogram), so this kernel never
+// waits:
+//   * every workgroup scores 256 consecutive positions of one request (one
+//     16-position MFMA tile per wave) for all of that request's query rows,
+//     and writes the scores as order-preserving 32-bit keys to the workspace;
+//   * it then counts itself done on the request's arrival counter; the last
+//     workgroup to arrive loads each row's keys (at most 32768, 32 per
+//     thread) into registers and runs the whole radix select there
+//     (select_in_regs), writing the indices in ascending order.
+// The keys make one round trip through the L2/Infinity Cache (4 bytes per
+// position against the 128-256 bytes of key read per position).  Rows longer
+// than 32768 positions take the two-pass route (indexer.hip).
+#include <algorithm>
+
+#include "dsa_device.h"
+#include "indexer_common.h"
+#include "radix_select.h"
+
+namespace dsa {
+
+struct FusedParams {
+  const int32_t* q_offsets;
+  const int32_t* ctx_lens;
+  const int32_t* bt;
+  int batch, bt_stride;
+  int H, Hpad, rcap;
+  const void* q;
+  const float* q_scale;
+  const float* w;
+  const void* k;
+  const float* k_scale;
+  int K;
+  int32_t* out;
+  int G;                // workgroups per request
+  int row_cap;          // min(max_ctx_len, kFusedMaxRow)
+  uint32_t* keys;       // [rows][key_stride] score keys
+  int64_t key_stride;
+  uint32_t* counters;   // [batch] arrival counters, zero between calls
+};
+
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kFusedChunk = kFusedWaves * 16;  // positions per workgroup
+constexpr int kFusedMaxRow = 32768;            // longest row the selection holds in LDS
+constexpr int kFusedMaxRows = 4;               // query rows per request
+constexpr int kKeysPerThread = kFusedMaxRow / kFusedThreads;
+
+template <int DT, int D>
+__global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
+  using Gm = IdxGeom<DT, D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ __align__(16) int wsum[kFusedWaves];
+  __shared__ int res[2];
+  __shared__ int s_last;
+
+  const int G = p.G, K = p.K;
+  const int b = blockIdx.x / G, m = blockIdx.x - b * G;
+  const int q0 = p.q_offsets[b], nb = p.q_offsets[b + 1] - q0;
+  const int first_pos = p.ctx_lens[b] - nb;  // position of the request's first query row
+  const int pos_max = first_pos + nb - 1;    // last position any of its rows sees
+  const int c0 = m * kFusedChunk;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const bool any_select = pos_max + 1 > K;   // the last row sees the most positions
+
+  // ---- scoring: one 16-position tile per wave --------------------------------
+  if (any_select && c0 <= pos_max) {
+    unsigned char* qs = smem;
+    float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * Gm::QSTRIDE);
+    stage_queries<DT, D, kFusedThreads>(qs, wsm, p.q, p.q_scale, p.w, q0, nb, p.H, p.Hpad);
+    __syncthreads();
+    auto emit = [&](int r, int pos, float s) {
+      if (pos <= first_pos + r) p.keys[(int64_t)(q0 + r) * p.key_stride + pos] = score_key(s);
+    };
+    const int t0 = c0 + wave * 16;
+    if (t0 <= pos_max) {
+      const int phys = p.bt[(int64_t)b * p.bt_stride + (t0 >> 6)];
+      if (DT == 0) {
+        const int lane = tid & 63;
+        if (lane < 16 && t0 + lane <= pos_max) {
+          const int pos = t0 + lane;
+          const float* krow = static_cast<const float*>(p.k) + ((int64_t)phys * kPage + (pos & 63)) * D;
+          score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, nb, krow,
+                           [&](int r, float s) { emit(r, pos, s); });
+        }
+      } else {
+        const unsigned char* kpage =
+            static_cast<const unsigned char*>(p.k) + (int64_t)phys * kPage * D * Gm::ES;
+        const float* ksp = DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr;
+        score_tiles_mfma<DT, D, 1>(qs, wsm, p.Hpad, nb, kpage, ksp, t0 & 63,
+                                   [&](int r, int slot, float s) { emit(r, (t0 & ~63) + slot, s); });
+      }
+    }
+  }
+
+  // ---- arrival: the last workgroup of the request selects ---------------------
+  // Each thread waits for its own key stores; one agent-scope release per
+  // workgroup then publishes them (a device-wide fence in every thread costs
+  // tens of microseconds at this grid size).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    if (!any_select) {
+      s_last = m == 0;  // nothing to rank: workgroup 0 writes the outputs
+    } else {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t old = __hip_atomic_fetch_add(p.counters + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (uint32_t)G - 1;
+      if (s_last) {
+        __hip_atomic_store(p.counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every other workgroup's keys
+      }
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem);  // the query staging area is free now
+  for (int r = 0; r < nb; ++r) {
+    const int vis = first_pos + r + 1;
+    int32_t* out = p.out + (int64_t)(q0 + r) * K;
+    if (vis <= K) {
+      for (int t = tid; t < K; t += kFusedThreads) out[t] = t < vis ? t : -1;
+      continue;
+    }
+    // the row's keys in registers, kKeysPerThread consecutive ones per thread
+    const uint32_t* grow = p.keys + (int64_t)(q0 + r) * p.key_stride;
+    const int pos0 = tid * kKeysPerThread;
+    uint32_t key[kKeysPerThread];
+#pragma unroll
+    for (int c = 0; c < kKeysPerThread; c += 4) {
+      const int t = pos0 + c;
+      if (t + 4 <= vis) {
+        const uint4 v = *reinterpret_cast<const uint4*>(grow + t);
+        key[c] = v.x;
+        key[c + 1] = v.y;
+        key[c + 2] = v.z;
+        key[c + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) key[c + j] = t + j < vis ? grow[t + j] : 0u;
+      }
+    }
+    select_in_regs<kFusedThreads, kKeysPerThread>(key, vis, K, out, hist, wsum, res);
+  }
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+namespace {
+
+template <int DT, int D>
+hipError_t launch_fused(FusedParams p, int batch, int max_ctx, hipStream_t s) {
+  p.G = (max_ctx + kFusedChunk - 1) / kFusedChunk;
+  p.row_cap = std::min(max_ctx, kFusedMaxRow);
+  const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad), (size_t)kHistBins * 4);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(li_fused<DT, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((li_fused<DT, D>), dim3(p.G * batch), dim3(kFusedThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool dsa_indexer_fused_fits(int max_q_per_req, int max_ctx_len) {
+  return max_q_per_req <= kFusedMaxRows && max_ctx_len <= kFusedMaxRow;
+}
+
+hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s) {
+  if (a.force_two_pass || !dsa_indexer_fused_fits(a.max_q_per_req, a.max_ctx_len))
+    return dsa_launch_indexer_two_pass(a, s);
+  FusedParams p;
+  p.q_offsets = a.q_offsets;
+  p.ctx_lens = a.ctx_lens;
+  p.bt = a.block_table;
+  p.batch = a.batch;
+  p.bt_stride = a.bt_stride;
+  p.H = a.n_heads;
+  p.Hpad = a.dtype == 0 ? a.n_heads : ((a.n_heads + 15) / 16) * 16;
+  p.rcap = a.max_q_per_req;
+  p.q = a.q;
+  p.q_scale = a.q_scale;
+  p.w = a.weights;
+  p.k = a.k_cache;
+  p.k_scale = a.k_scale;
+  p.K = a.topk;
+  p.out = a.out_idx;
+  p.G = p.row_cap = 0;
+  p.keys = reinterpret_cast<uint32_t*>(a.scores);
+  p.key_stride = a.score_stride;
+  p.counters = a.counters;
+  const bool d64 = a.head_dim == 64;
+  switch (a.dtype) {
+    case 0: return d64 ? launch_fused<0, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<0, 128>(p, a.batch, a.max_ctx_len, s);
+    case 1: return d64 ? launch_fused<1, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<1, 128>(p, a.batch, a.max_ctx_len, s);
+    default: return d64 ? launch_fused<2, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<2, 128>(p, a.batch, a.max_ctx_len, s);
+  }
+}

@@ -1,0 +1,246 @@
+// radix_select.h -- workgroup-level pieces of the radix Top-K selection.
+//
+// Keys are the order-preserving 32-bit images of fp32 scores (score_key), so
+// "K largest scores" is "K largest keys".  The K-th largest key is found one
+// radix digit at a time (11, 11 and 10 bits from the top): a histogram of the
+// current digit over the keys that match the digits found so far, then a
+// scan from the top bin down to the bin where the running count reaches the
+// number of keys still needed.
+#pragma once
+
+#include "dsa_device.h"
+
+namespace dsa {
+
+constexpr int kLevelShift[3] = {21, 10, 0};   // low bit of each digit
+constexpr int kLevelBins[3] = {2048, 2048, 1024};
+
+// Largest bin `bin` with (keys in bins >= bin) >= k; above = keys in bins > bin;
+// total = keys in all bins.  Run by one full wave (64 lanes); every lane
+// returns the result.  Lane l reads its PER = nbins / 64 bins (the top ones
+// for lane 0) with 16-byte LDS loads, so the bins are read once, in parallel.
+// If the bins hold fewer than k keys it returns bin 0, above 0.
+template <int PER>
+__device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& bin, int& above, int& total) {
+  constexpr int nbins = PER * 64;
+  const int lane = threadIdx.x & 63;
+  const int lo = nbins - (lane + 1) * PER;  // lane owns bins [lo, lo + PER)
+  uint32_t v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; j += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(bins + lo + j);
+    v[j] = q.x;
+    v[j + 1] = q.y;
+    v[j + 2] = q.z;
+    v[j + 3] = q.w;
+  }
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) local += (int)v[j];
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  total = __shfl(incl, 63);
+  const int before = incl - local;
+  int rb = -1, ra = 0;
+  if (before < k && incl >= k) {
+    int acc = before;
+    bool done = false;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      if (!done && acc + (int)v[j] >= k) {
+        rb = lo + j;
+        ra = acc;
+        done = true;
+      }
+      acc += (int)v[j];
+    }
+  }
+  const uint64_t found = __ballot(rb >= 0);
+  if (found == 0) {
+    bin = 0;
+    above = 0;
+    return;
+  }
+  const int src = __ffsll((long long)found) - 1;
+  bin = __shfl(rb, src);
+  above = __shfl(ra, src);
+}
+
+__device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int nbins, int k, int& bin, int& above) {
+  int total;
+  if (nbins == 2048) kth_bin_wave<32>(bins, k, bin, above, total);
+  else kth_bin_wave<16>(bins, k, bin, above, total);
+}
+
+// Exclusive prefix sum of v over a workgroup of NT threads in thread order.
+// `wsum` is LDS scratch of NT/64 ints (16-byte aligned).  Contains two barriers.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int& total, int* wsum) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int ws[NW];
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int w = 0; w < NW; w += 4) {
+      const int4 q = *reinterpret_cast<const int4*>(wsum + w);
+      ws[w] = q.x;
+      ws[w + 1] = q.y;
+      ws[w + 2] = q.z;
+      ws[w + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ws[w] = wsum[w];
+  }
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wave ? ws[w] : 0;
+    total += ws[w];
+  }
+  return base + incl - v;
+}
+
+}  // namespace dsa
+
+namespace dsa {
+
+// Top-K of one row of `vis` <= NT * KPT keys held in registers, written to
+// out[0..K) in ascending position order; ties at the K-th key go to the lower
+// positions (rows with vis <= K are the caller's business).
+//
+// Layout: thread t holds key[c] = key of position KPT * t + c, so position
+// order is thread order.  Slots at or past `vis` must hold key 0, which lies
+// below the key of every finite score (only negative NaN patterns map under
+// it), so it is never above, equal to or at the K-th key of a row with
+// vis > K.
+//
+// Digits: the K-th key is found 11, 11 and 10 bits at a time with LDS
+// histograms (`hist`, kHistBins words) of the keys matching the digits found
+// so far.  The first digit only counts keys at or above a lower bound taken
+// from a sample (the first key of every thread, binned; the bin holding about
+// twice the sample rank the K-th key should have): when at least K keys clear
+// the bound, the K-th key is among them and its digit is exact from their
+// histogram alone; otherwise the digit is recounted over every key.  This
+// keeps the LDS atomics, which serialise on the busy bins, to a few thousand.
+//
+// Output: the kept keys are the keys above the K-th plus the first `need`
+// keys equal to it, so one scan of per-thread (above, equal) counts gives
+// every thread its output offset, above_before + min(equal_before, need).
+// `wsum` holds NT / 64 ints, `res` 2.
+template <int NT, int KPT>
+__device__ void select_in_regs(const uint32_t (&key)[KPT], int vis, int K, int32_t* out, uint32_t* hist,
+                               int* wsum, int* res) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = tid * KPT;  // position of key[0]
+  const bool active = base < vis;
+
+  // ---- lower bound for the first digit from one sample key per thread ------
+  for (int c = tid; c < kHistBins; c += NT) hist[c] = 0u;
+  __syncthreads();
+  if (active) atomicAdd(&hist[key[0] >> kLevelShift[0]], 1u);
+  __syncthreads();
+  const int nsamp = min(NT, (vis + KPT - 1) / KPT);
+  const int srank = min(nsamp, (int)(((int64_t)2 * K * nsamp + vis - 1) / vis) + 8);
+  if (wave == 0) {
+    int bin, above;
+    kth_bin_wave(hist, kHistBins, srank, bin, above);
+    if (lane == 0) res[0] = bin;
+  }
+  __syncthreads();
+  const uint32_t lo_bin = (uint32_t)res[0];
+  __syncthreads();
+
+  uint32_t prefix = 0u;
+  int need = K;
+  for (int level = 0; level < 3; ++level) {
+    const int nbins = kLevelBins[level], shift = kLevelShift[level];
+    for (int c = tid; c < nbins; c += NT) hist[c] = 0u;
+    __syncthreads();
+    if (level == 0) {
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+          const uint32_t d = key[c] >> shift;
+          if (d >= lo_bin) atomicAdd(&hist[d], 1u);
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int bin, above, total;
+        kth_bin_wave<32>(hist, K, bin, above, total);
+        if (lane == 0) res[0] = total;
+      }
+      __syncthreads();
+      if (res[0] < K) {  // the sample bound was too high: count every key
+        for (int c = tid; c < nbins; c += NT) hist[c] = 0u;
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int c = 0; c < KPT; ++c) atomicAdd(&hist[key[c] >> shift], 1u);
+        }
+      }
+    } else {
+      const int pshift = kLevelShift[level - 1];
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+          const uint32_t k = key[c];
+          if ((k >> pshift) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int bin, above;
+      kth_bin_wave(hist, nbins, need, bin, above);
+      if (lane == 0) {
+        res[0] = bin;
+        res[1] = above;
+      }
+    }
+    __syncthreads();
+    prefix = level == 0 ? (uint32_t)res[0] : ((prefix << (level == 1 ? 11 : 10)) | (uint32_t)res[0]);
+    need -= res[1];
+    __syncthreads();
+  }
+  const uint32_t kth = prefix;  // the K-th largest key; `need` keys equal to it are kept
+
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    ngt += key[c] > kth;
+    neq += key[c] == kth;
+  }
+  int packed_total;
+  const int packed_before = block_excl_scan<NT>(ngt | (neq << 16), packed_total, wsum);
+  const int gt_before = packed_before & 0xffff, eq_before = packed_before >> 16;
+  int o = gt_before + min(eq_before, need);
+  int er = eq_before;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool e = key[c] == kth;
+    if (key[c] > kth || (e && er < need)) {
+      if (o < K) out[o] = base + c;
+      ++o;
+    }
+    er += e;
+  }
+  __syncthreads();
+}
+
+}  // namespace dsa

@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK = 0
+INDEXER_TWO_PASS = 1  # flag: scores through the workspace instead of the fused team kernel
 DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2}
 _STORAGE = {
     "f32": (torch.float32,),
@@ -61,6 +62,7 @@ class Indexer(ctypes.Structure):
         ("weights", ctypes.c_void_p),
         ("k_cache", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -106,6 +108,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_fused_decode_workspace_size.argtypes = [PP, PI, PS]
         lib.dsa_fused_decode.restype = ctypes.c_int
         lib.dsa_fused_decode.argtypes = [PP, PI, PS, P, P, S, P]
+        lib.dsa_workspace_init.restype = ctypes.c_int
+        lib.dsa_workspace_init.argtypes = [P, S, P]
         _lib = lib
     return _lib
 
@@ -162,7 +166,7 @@ def make_paged(q_offsets: torch.Tensor, ctx_lens: torch.Tensor, block_table: tor
                  int(num_pages), _ptr(q_offsets), _ptr(ctx_lens), _ptr(block_table))
 
 
-def make_indexer(q, weights, k_cache, topk, dtype, q_scale=None, k_scale=None) -> Indexer:
+def make_indexer(q, weights, k_cache, topk, dtype, q_scale=None, k_scale=None, flags=0) -> Indexer:
     _check_tensor(q, "q", _STORAGE[dtype])
     _check_tensor(k_cache, "k_cache", _STORAGE[dtype])
     _check_tensor(weights, "weights", (torch.float32,))
@@ -172,7 +176,7 @@ def make_indexer(q, weights, k_cache, topk, dtype, q_scale=None, k_scale=None) -
     if k_cache.shape[-1] != D or weights.shape != (T, H):
         raise ValueError("indexer shapes disagree")
     return Indexer(H, D, int(topk), DTYPE_CODE[dtype], _ptr(q), _ptr(q_scale), _ptr(weights),
-                   _ptr(k_cache), _ptr(k_scale))
+                   _ptr(k_cache), _ptr(k_scale), int(flags))
 
 
 def make_sfa(q, kv_cache, out, scale, dtype, lse=None, v_dim=512) -> Sfa:
@@ -187,13 +191,26 @@ def make_sfa(q, kv_cache, out, scale, dtype, lse=None, v_dim=512) -> Sfa:
                _ptr(lse))
 
 
+def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    """Allocate a workspace and zero-fill it with dsa_workspace_init."""
+    ws = torch.empty(max(int(nbytes) + 255 & ~255, 256), dtype=torch.uint8, device=device)
+    workspace_init(ws, stream)
+    return ws
+
+
+def workspace_init(ws: torch.Tensor, stream=None):
+    st = load().dsa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if st != DSA_OK:
+        raise DsaError(st, "dsa_workspace_init")
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
                              f"{nbytes} needed")
         return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return new_workspace(nbytes, device)
 
 
 def indexer_topk_workspace_size(paged: Paged, idx: Indexer) -> int:

@@ -46,9 +46,10 @@ def paged_of(case: inputs.Case) -> dsa.Paged:
                           num_q_tokens=case.num_tokens)
 
 
-def indexer_of(case: inputs.Case, topk=None) -> dsa.Indexer:
+def indexer_of(case: inputs.Case, topk=None, two_pass=False) -> dsa.Indexer:
     return dsa.make_indexer(case.q_idx, case.weights, case.k_cache, topk or case.topk, case.idx_dtype,
-                            q_scale=case.q_scale, k_scale=case.k_scale)
+                            q_scale=case.q_scale, k_scale=case.k_scale,
+                            flags=dsa.INDEXER_TWO_PASS if two_pass else 0)
 
 
 def sfa_tensors(case: inputs.Case):
@@ -58,10 +59,13 @@ def sfa_tensors(case: inputs.Case):
     return out, lse
 
 
-def gpu_indexer_topk(case: inputs.Case, topk=None) -> torch.Tensor:
+def gpu_indexer_topk(case: inputs.Case, topk=None, two_pass=False) -> torch.Tensor:
+    """Indices from dsa_indexer_topk (fused route unless two_pass)."""
     K = topk or case.topk
     out = torch.full((case.num_tokens, K), -7, dtype=torch.int32, device=case.q_idx.device)
-    dsa.indexer_topk(paged_of(case), indexer_of(case, K), out)
+    paged, idx = paged_of(case), indexer_of(case, K, two_pass)
+    ws = dsa.new_workspace(dsa.indexer_topk_workspace_size(paged, idx), case.q_idx.device)
+    dsa.indexer_topk(paged, idx, out, workspace=ws)
     return out
 
 
@@ -162,9 +166,12 @@ def compare_out(gpu_out, ora_out, dtype: str, tol=None, gpu_lse=None, ora_lse=No
 
 
 def check_case(case: inputs.Case, tol=None, nthreads=None, fused=True):
-    """Full parity of one case: indexer, SFA on the GPU's indices, fused path."""
+    """Full parity of one case: both indexer routes (identical to each other,
+    and to the oracle up to the bar), SFA on the GPU's indices, fused path."""
     vis = oracle.visible(_np(case.q_offsets), _np(case.ctx_lens))
     g_idx = gpu_indexer_topk(case)
+    g_idx2 = gpu_indexer_topk(case, two_pass=True)
+    assert torch.equal(g_idx, g_idx2), "fused and two-pass indexer routes disagree"
     o_idx, o_sc = oracle_indexer(case, nthreads=nthreads)
     stats = compare_topk(g_idx, o_idx, o_sc, vis, case.exact)
     if case.sfa_dtype != "none":

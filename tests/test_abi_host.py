@@ -46,7 +46,7 @@ def good_paged(**kw):
 
 def good_indexer(**kw):
     p = dict(n_heads=64, head_dim=128, topk=256, dtype=1, q=FAKE, q_scale=None, weights=FAKE,
-             k_cache=FAKE, k_scale=None)
+             k_cache=FAKE, k_scale=None, flags=0)
     p.update(kw)
     return dsa.Indexer(**p)
 
@@ -88,7 +88,7 @@ def test_bad_paging_rejected(kw):
 BAD_INDEXER = [(dict(q=None), 1), (dict(weights=None), 1), (dict(k_cache=None), 1), (dict(topk=0), 1),
                (dict(n_heads=0), 1), (dict(dtype=7), 1), (dict(dtype=2), 1),  # fp8 without scales
                (dict(dtype=2, q_scale=FAKE), 1), (dict(n_heads=65), 2), (dict(topk=4097), 2),
-               (dict(head_dim=96), 2), (dict(dtype=0, n_heads=64, head_dim=128), 2)]
+               (dict(head_dim=96), 2), (dict(dtype=0, n_heads=64, head_dim=128), 2), (dict(flags=2), 1)]
 
 
 @pytest.mark.parametrize("kw,status", BAD_INDEXER, ids=[str(k) for k, _ in BAD_INDEXER])
@@ -116,6 +116,13 @@ def test_sfa_topk_bounds():
     assert call_sfa(good_paged(), good_sfa(), idx=None) == 1
 
 
+def test_workspace_init_rejects_bad_buffers():
+    lib = dsa.load()
+    assert lib.dsa_workspace_init(None, 256, None) == 1
+    assert lib.dsa_workspace_init(FAKE + 4, 256, None) == 1   # misaligned
+    assert lib.dsa_workspace_init(FAKE, 255, None) == 1       # not whole words
+
+
 def test_workspace_too_small_rejected_before_device():
     lib = dsa.load()
     p, i, s = good_paged(), good_indexer(), good_sfa()
@@ -133,8 +140,9 @@ def test_workspace_sizes():
     lib = dsa.load()
     p = good_paged(num_q_tokens=5, max_ctx_len=1000)
     need = lib.dsa_indexer_topk_workspace_size(ctypes.byref(p), ctypes.byref(good_indexer()))
-    # histogram [T][2048] u32 + scores [T][round_up(L, 256)] f32, each 256-aligned
-    assert need == 5 * 2048 * 4 + 5 * 1024 * 4
+    # arrival counters [B] u32 | digit histograms [T][3 * 2048] u32 |
+    # scores [T][round_up(L, 256)] f32, each region 256-byte aligned
+    assert need == 256 + 5 * 6144 * 4 + 5 * 1024 * 4
     # one row of 128 heads at small batch splits the index list; fp32 never does
     one = good_paged(batch=1, num_q_tokens=1, max_q_per_req=1)
     s_bf16 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa()), 2048)

@@ -145,3 +145,27 @@ def test_sfa_head_counts(heads):
     g_out, g_lse = parity.gpu_sparse_attn(case, idx)
     r_out, r_lse = parity.oracle_sfa(case, idx)
     print(parity.compare_out(g_out, r_out, "bf16", gpu_lse=g_lse, ora_lse=r_lse))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_32k", "spec_verify"])
+def test_workspace_reuse_across_calls(name):
+    """Many calls on one workspace: the fused indexer's arrival counters and
+    the two-pass histograms must return to zero after every call."""
+    from lightning_indexer_top_02_amd import dsa
+    case = {"tiny": lambda: inputs.tiny_decode(),
+            "decode_32k": lambda: inputs.decode_32k(ctx_lens=[32768, 5000], n_q=[1, 1]),
+            "spec_verify": lambda: inputs.spec_verify(batch=3, ctx=9000)}[name]()
+    case = parity.to_device(case)
+    paged, idx = parity.paged_of(case), parity.indexer_of(case)
+    ws = dsa.new_workspace(dsa.indexer_topk_workspace_size(paged, idx), "cuda")
+    first = None
+    for it in range(50):
+        out = torch.empty((case.num_tokens, case.topk), dtype=torch.int32, device="cuda")
+        dsa.indexer_topk(paged, idx, out, workspace=ws)
+        if first is None:
+            first = out.clone()
+        else:
+            assert torch.equal(out, first), f"call {it} differs"
+    ctrl = ws[: 4 * case.batch].view(torch.int32)
+    assert int(ctrl.abs().sum()) == 0, "arrival counters not back to zero"
+    assert torch.equal(first, parity.gpu_indexer_topk(case, two_pass=True))
