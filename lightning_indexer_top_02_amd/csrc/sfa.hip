@@ -10,12 +10,14 @@
 // first 512 entries as the value.
 //
 // bf16 kernel (sfa_bf16): a workgroup owns one query row, 16 heads per wave,
-// and one contiguous slice of the row's index list.  The selected rows are
-// gathered through the block table in chunks of 32 into LDS (the scattered
-// reads become 1152-byte row reads, "aggregating random small reads",
-// "Optimizing Inference for Hybrid Attention LLMs: Practices for Fast
-// Adaptation", section 3, item 2), and every wave of the workgroup reuses
-// them.  Per chunk and wave, MFMA computes S^T = K Q^T (32 rows x 16 heads,
+// and one contiguous slice of the row's index list.  The slice's pool rows
+// are looked up through the block table once; the rows are then gathered in
+// chunks of 32 into LDS (the scattered reads become 1152-byte row reads,
+// "aggregating random small reads", "Optimizing Inference for Hybrid
+// Attention LLMs: Practices for Fast Adaptation", section 3, item 2), the
+// next chunk's loads in flight in registers while the current chunk is
+// computed (the same page's "overlapping gather and compute"), and every wave
+// of the workgroup reuses them.  Per chunk and wave, MFMA computes S^T = K Q^T (32 rows x 16 heads,
 // contraction 576), an online softmax updates the running max and sum per
 // head, and MFMA accumulates O^T += V^T P^T (512 dims x 16 heads,
 // contraction over the 32 rows).  Computing the transposed products keeps
@@ -58,66 +60,145 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
+// LDS layout of one staged chunk of 32 rows:
+//   krow: row-major copy of the whole 576-wide rows (the A operand of
+//         S^T = K Q^T), 1168-byte rows;
+//   vt:   the value part (dims 0..511) transposed, vt[dim][slot], 80 bytes
+//         per dim, where slot 8g + e holds row r(g, e) = 4g + e (e < 4) or
+//         16 + 4g + e - 4 (e >= 4): the rows a lane of lane group g holds in
+//         its S^T accumulators, so the probabilities are the B operand of
+//         O^T += V^T P^T as they come out of the softmax and the A operand
+//         is one 16-byte read.
+//   The paddings make the MFMA operand reads and the staging writes
+//   conflict-free (or at most 2-way) across the 64 LDS banks.
+constexpr int kVtStride = 80;
+constexpr int kKrowBytes = kSfaRows * kRowStride;
+constexpr int kVtBytes = kVDim * kVtStride;
+
+__device__ __forceinline__ int slot_row(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+
+// Stage the 8 rows of lane group g (slot order), 8 value dims starting at
+// dim 8 dc, into krow and (transposed) into vt.
+__device__ __forceinline__ void stage_vblock(unsigned char* krow, unsigned char* vt, int g, int dc,
+                                             const uint4 (&a)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    *reinterpret_cast<uint4*>(krow + slot_row(g, e) * kRowStride + dc * 16) = a[e];
+  // 8 x 8 transpose of 16-bit elements: t[j] holds dim 8 dc + j of the 8 rows
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = j >> 1;
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    uint4 t;
+    t.x = __builtin_amdgcn_perm(((const uint32_t*)&a[1])[k], ((const uint32_t*)&a[0])[k], sel);
+    t.y = __builtin_amdgcn_perm(((const uint32_t*)&a[3])[k], ((const uint32_t*)&a[2])[k], sel);
+    t.z = __builtin_amdgcn_perm(((const uint32_t*)&a[5])[k], ((const uint32_t*)&a[4])[k], sel);
+    t.w = __builtin_amdgcn_perm(((const uint32_t*)&a[7])[k], ((const uint32_t*)&a[6])[k], sel);
+    *reinterpret_cast<uint4*>(vt + (dc * 8 + j) * kVtStride + g * 16) = t;
+  }
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
-  __shared__ __align__(16) unsigned char kvs[kSfaRows * kRowStride];
-  __shared__ int rvalid[kSfaRows];
   constexpr int NT = NW * 64;
+  constexpr int kBlocks = 4 * (kVDim / 8);              // (lane group, 8-dim chunk) blocks per chunk
+  constexpr int kRope = kSfaRows * ((kQkDim - kVDim) / 8);  // 16-byte rope pieces per chunk
+  constexpr int BPT = (kBlocks + NT - 1) / NT;            // value blocks per thread
+  constexpr int RPT = (kRope + NT - 1) / NT;               // rope pieces per thread
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* krow = smem;
+  unsigned char* vt = smem + kKrowBytes;
+  int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + kVtBytes);  // pool row of each selected row, -1 = none
+
   const int split = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
   const int b = request_of_row(p.q_offsets, p.batch, i);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int h = hg * (16 * NW) + wave * 16 + l16;  // this lane's head column
+  const int r_begin = split * p.rows_per_split;
+  const int nrows = max(0, min(p.K, r_begin + p.rows_per_split) - r_begin);
+  const uint16_t* kvg = static_cast<const uint16_t*>(p.kv);
 
+  // pool rows of this split's selected rows (index -> page -> slot), once
+  {
+    const int32_t* irow = p.idx + (int64_t)i * p.K + r_begin;
+    const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
+    const int nr = (nrows + kSfaRows - 1) / kSfaRows * kSfaRows;
+    for (int r = tid; r < nr; r += NT) {
+      const int t = r < nrows ? irow[r] : -1;
+      rowidx[r] = t >= 0 ? btrow[t >> 6] * kPage + (t & 63) : -1;
+    }
+  }
   // Q fragments of this lane's head: qf[s] = q[h][32 s + 8 g .. + 8]
   uint4 qf[kQkDim / 32];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)i * p.H + h) * kQkDim;
 #pragma unroll
-    for (int s = 0; s < kQkDim / 32; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + s * 32 + g * 8);
+    for (int s2 = 0; s2 < kQkDim / 32; ++s2) qf[s2] = *reinterpret_cast<const uint4*>(qrow + s2 * 32 + g * 8);
   }
   f32x4 o[kVDim / 16];
 #pragma unroll
   for (int et = 0; et < kVDim / 16; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
   const float zscale = p.scale * kLog2e;
+  __syncthreads();
 
-  const int r_begin = split * p.rows_per_split;
-  const int r_end = min(p.K, r_begin + p.rows_per_split);
-  const int32_t* irow = p.idx + (int64_t)i * p.K;
-  const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
-  const uint16_t* kvg = static_cast<const uint16_t*>(p.kv);
-
-  for (int c0 = r_begin; c0 < r_end; c0 += kSfaRows) {
-    __syncthreads();
-    for (int c = tid; c < kSfaRows * (kRowBytes / 16); c += NT) {
-      const int r = c / (kRowBytes / 16), part = c - r * (kRowBytes / 16);
-      const int rr = c0 + r;
-      const int t = rr < r_end ? irow[rr] : -1;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t >= 0) {
-        const int phys = btrow[t >> 6];
-        v = *reinterpret_cast<const uint4*>(kvg + ((int64_t)phys * kPage + (t & 63)) * kQkDim + part * 8);
-      }
-      *reinterpret_cast<uint4*>(kvs + r * kRowStride + part * 16) = v;
-      if (part == 0) rvalid[r] = t >= 0;
-    }
-    __syncthreads();
-
-    // S^T tiles: s0[i] = S[head l16][row 4g+i], s1[i] = S[head l16][row 16+4g+i]
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* ka = kvs + l16 * kRowStride + g * 16;
+  // gather of one chunk into registers: BPT value blocks and RPT rope pieces
+  uint4 va[BPT][8], ra[RPT];
+  auto gather = [&](int c0) {
 #pragma unroll
-    for (int s = 0; s < kQkDim / 32; ++s) {
-      uint4 a0 = *reinterpret_cast<const uint4*>(ka + s * 64);
-      uint4 a1 = *reinterpret_cast<const uint4*>(ka + 16 * kRowStride + s * 64);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[s]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s]), s1, 0, 0, 0);
+    for (int j = 0; j < BPT; ++j) {
+      const int blk = tid + j * NT;
+      const int gg = blk & 3, dc = blk >> 2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = blk < kBlocks ? rowidx[c0 + slot_row(gg, e)] : -1;
+        va[j][e] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + dc * 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int it = tid + j * NT;
+      const int row = it < kRope ? rowidx[c0 + (it >> 3)] : -1;
+      ra[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + kVDim + (it & 7) * 8)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int blk = tid + j * NT;
+      if (blk < kBlocks) stage_vblock(krow, vt, blk & 3, blk >> 2, va[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int it = tid + j * NT;
+      if (it < kRope) *reinterpret_cast<uint4*>(krow + (it >> 3) * kRowStride + kVDim * 2 + (it & 7) * 16) = ra[j];
+    }
+  };
+
+  if (nrows > 0) gather(0);
+  for (int c0 = 0; c0 < nrows; c0 += kSfaRows) {
+    __syncthreads();  // the previous chunk is no longer read
+    stage();
+    __syncthreads();
+    if (c0 + kSfaRows < nrows) gather(c0 + kSfaRows);  // in flight during this chunk's math
+
+    // S^T tiles: s0[e] = S[head l16][row 4g+e], s1[e] = S[head l16][row 16+4g+e]
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    const unsigned char* ka = krow + l16 * kRowStride + g * 16;
+#pragma unroll
+    for (int s2 = 0; s2 < kQkDim / 32; ++s2) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(ka + s2 * 64);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(ka + 16 * kRowStride + s2 * 64);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[s2]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s2]), s1, 0, 0, 0);
     }
     float z[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      z[e] = rvalid[4 * g + e] ? s0[e] * zscale : -INFINITY;
-      z[4 + e] = rvalid[16 + 4 * g + e] ? s1[e] * zscale : -INFINITY;
+      z[e] = rowidx[c0 + 4 * g + e] >= 0 ? s0[e] * zscale : -INFINITY;
+      z[4 + e] = rowidx[c0 + 16 + 4 * g + e] >= 0 ? s1[e] * zscale : -INFINITY;
     }
     float tmax = z[0];
 #pragma unroll
@@ -142,26 +223,17 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
     lsum = lsum * alpha + psum;
     m = mnew;
 
-    // B operand of O^T += V^T P^T: element e of lane group g is row r(e) with
-    // r(e) = 4g + e (e < 4) and 16 + 4g + e - 4 (e >= 4), the rows this lane
-    // already holds in s0/s1.
-    uint4 pf;
+    uint4 pf;  // B operand of O^T += V^T P^T, slot order
     pf.x = pack_bf16x2(pr[0], pr[1]);
     pf.y = pack_bf16x2(pr[2], pr[3]);
     pf.z = pack_bf16x2(pr[4], pr[5]);
     pf.w = pack_bf16x2(pr[6], pr[7]);
-    const uint16_t* vb = reinterpret_cast<const uint16_t*>(kvs) + l16;
-    const int rs = kRowStride / 2;
+    const unsigned char* vb = vt + l16 * kVtStride + g * 16;
 #pragma unroll
     for (int et = 0; et < kVDim / 16; ++et) {
-      const uint16_t* vc = vb + et * 16;
-      uint4 va;
-      va.x = (uint32_t)vc[(4 * g + 0) * rs] | ((uint32_t)vc[(4 * g + 1) * rs] << 16);
-      va.y = (uint32_t)vc[(4 * g + 2) * rs] | ((uint32_t)vc[(4 * g + 3) * rs] << 16);
-      va.z = (uint32_t)vc[(16 + 4 * g + 0) * rs] | ((uint32_t)vc[(16 + 4 * g + 1) * rs] << 16);
-      va.w = (uint32_t)vc[(16 + 4 * g + 2) * rs] | ((uint32_t)vc[(16 + 4 * g + 3) * rs] << 16);
+      const uint4 av = *reinterpret_cast<const uint4*>(vb + et * 16 * kVtStride);
       o[et] *= alpha;
-      o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pf), o[et], 0, 0, 0);
+      o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pf), o[et], 0, 0, 0);
     }
   }
 
@@ -188,27 +260,40 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
 }
 
 // Merge split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
-// One wave per (query row, head), 8 dims per lane.
+// One 64-lane workgroup per (query row, head), 8 dims per lane; the split
+// loop keeps four splits' loads in flight.
 template <bool BF16>
-__global__ __launch_bounds__(256) void sfa_combine(SfaParams p) {
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= p.T * p.H) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t th = w;  // = i * H + h
+__global__ __launch_bounds__(64) void sfa_combine(SfaParams p) {
+  const int64_t th = blockIdx.x;  // = i * H + h
+  const int lane = threadIdx.x;
+  const int64_t stride = (int64_t)p.T * p.H;
   float M = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.part_lse[s * (int64_t)p.T * p.H + th]);
+  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.part_lse[s * stride + th]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < p.n_split; ++s) {
-      const float l = p.part_lse[s * (int64_t)p.T * p.H + th];
-      if (l == -INFINITY) continue;
-      const float wgt = expf(l - M);
-      den += wgt;
-      const float4* src = reinterpret_cast<const float4*>(p.part_o + (s * (int64_t)p.T * p.H + th) * kVDim + lane * 8);
-      float4 a = src[0], c = src[1];
-      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
-      acc[4] += wgt * c.x; acc[5] += wgt * c.y; acc[6] += wgt * c.z; acc[7] += wgt * c.w;
+    const float* po = p.part_o + th * kVDim + lane * 8;
+    for (int s0 = 0; s0 < p.n_split; s0 += 4) {
+      float wgt[4];
+      float4 a[4], c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = s0 + j;
+        const float l = s < p.n_split ? p.part_lse[s * stride + th] : -INFINITY;
+        wgt[j] = l == -INFINITY ? 0.f : expf(l - M);
+        if (s < p.n_split) {
+          a[j] = reinterpret_cast<const float4*>(po + s * stride * kVDim)[0];
+          c[j] = reinterpret_cast<const float4*>(po + s * stride * kVDim)[1];
+        } else {
+          a[j] = c[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        den += wgt[j];
+        acc[0] += wgt[j] * a[j].x; acc[1] += wgt[j] * a[j].y; acc[2] += wgt[j] * a[j].z; acc[3] += wgt[j] * a[j].w;
+        acc[4] += wgt[j] * c[j].x; acc[5] += wgt[j] * c[j].y; acc[6] += wgt[j] * c[j].z; acc[7] += wgt[j] * c[j].w;
+      }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -307,6 +392,17 @@ __global__ __launch_bounds__(kF32Threads) void sfa_f32(SfaParams p) {
 
 using namespace dsa;
 
+template <int NW>
+static hipError_t launch_sfa(dim3 grid, size_t lds, hipStream_t s, const SfaParams& p) {
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sfa_bf16<NW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sfa_bf16<NW>, grid, dim3(NW * 64), lds, s, p);
+  return hipGetLastError();
+}
+
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   SfaParams p;
   p.q_offsets = a.q_offsets;
@@ -335,15 +431,18 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   for (int c = 4; c > 1; --c)
     if ((a.n_heads / 16) % c == 0) { nw = c; break; }
   dim3 grid(a.n_split, a.n_heads / (16 * nw), a.num_rows);
+  hipError_t e0;
+  const size_t lds = (size_t)kKrowBytes + kVtBytes +
+                     (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
   switch (nw) {
-    case 1: hipLaunchKernelGGL(sfa_bf16<1>, grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(sfa_bf16<2>, grid, dim3(128), 0, s, p); break;
-    case 3: hipLaunchKernelGGL(sfa_bf16<3>, grid, dim3(192), 0, s, p); break;
-    default: hipLaunchKernelGGL(sfa_bf16<4>, grid, dim3(256), 0, s, p); break;
+    case 1: e0 = launch_sfa<1>(grid, lds, s, p); break;
+    case 2: e0 = launch_sfa<2>(grid, lds, s, p); break;
+    case 3: e0 = launch_sfa<3>(grid, lds, s, p); break;
+    default: e0 = launch_sfa<4>(grid, lds, s, p); break;
   }
+  if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  const int waves = a.num_rows * a.n_heads;
-  hipLaunchKernelGGL(sfa_combine<true>, dim3((waves + 3) / 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(sfa_combine<true>, dim3(a.num_rows * a.n_heads), dim3(64), 0, s, p);
   return hipGetLastError();
 }
