@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 from lightning_indexer_top_02_amd import dsa, inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense, MI355X
 METRIC = "DSA decode tokens/s + HBM GB/s (% peak) at 32K ctx; prefill indexer MFMA util"
 
 WORKLOADS = {
@@ -50,6 +51,12 @@ WORKLOADS = {
         make=lambda dev, batch=64: inputs.batched_decode_fp8(device=dev, batch=batch, wide=True),
         desc="DSA decode step: batch {batch}, contexts U[4096,131072], fp8 indexer 64 x 128, Top-K "
              "2048, bf16 sparse attention 128 heads"),
+    "chunked_prefill": dict(
+        make=lambda dev, batch=1, sfa=True: inputs.chunked_prefill(device=dev, **({} if sfa else
+                                                                                 {"sfa_dtype": None})),
+        desc="DSA chunked-prefill step: 4096 query tokens appended to a 61440-token prefix (65536 "
+             "positions, causal), indexer 64 heads x 128 bf16, Top-K 2048 per row, sparse attention "
+             "128 heads x (512+64) bf16"),
     "spec_verify": dict(
         make=lambda dev, batch=16: inputs.spec_verify(device=dev, batch=batch),
         desc="DSA speculative-verify step: {batch} requests x 4 causal query tokens at context "
@@ -61,14 +68,22 @@ def elem_bytes(dtype):
     return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
 
 
+def visible_per_row(case: inputs.Case):
+    """Positions each query row sees (its request's length minus the rows after it)."""
+    qo = case.q_offsets.cpu().tolist()
+    lens = case.ctx_lens.cpu().tolist()
+    return [lens[b] - (qo[b + 1] - qo[b]) + j + 1 for b in range(len(lens)) for j in range(qo[b + 1] - qo[b])]
+
+
 def algorithmic_bytes(case: inputs.Case):
-    """Bytes the method itself must move per step, per stage.
+    """Bytes (and flops) the method itself needs per step, per stage.
 
     indexer: every visible key once per request (head dim x element size,
              plus a 4-byte scale for fp8), q, w (and q scales), the block
-             table, and the Top-K indices written.
+             table, and the Top-K indices written; flops = 2 H_I D_I per
+             visible (row, position) pair (the logits).
     sparse attention: the indices read, K gathered latent rows per query row,
-             q and the output.
+             q and the output; flops = 2 H_q (576 + 512) per selected row.
     """
     lens = case.ctx_lens.cpu().tolist()
     T, K = case.num_tokens, case.topk
@@ -77,10 +92,11 @@ def algorithmic_bytes(case: inputs.Case):
     H = case.n_heads_idx
     idx_bytes = (sum(lens) * key_row + T * H * case.head_dim_idx * eK + T * H * 4 * (2 if case.idx_dtype == "fp8" else 1)
                  + sum((L + 63) // 64 for L in lens) * 4 + T * K * 4)
-    eS = elem_bytes(case.sfa_dtype)
-    sfa_bytes = (T * K * 4 + T * K * case.qk_dim * eS + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eS)
-    idx_flops = 2 * sum(lens) * H * case.head_dim_idx  # upper bound (every row of a request sees <= L)
-    sfa_flops = 2 * T * K * case.n_heads_sfa * (case.qk_dim + case.v_dim)
+    eS = elem_bytes(case.sfa_dtype) if case.sfa_dtype != "none" else 0
+    sel = sum(min(v, K) for v in visible_per_row(case))
+    sfa_bytes = (T * K * 4 + sel * case.qk_dim * eS + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eS)
+    idx_flops = 2 * sum(visible_per_row(case)) * H * case.head_dim_idx
+    sfa_flops = 2 * sel * case.n_heads_sfa * (case.qk_dim + case.v_dim)
     return {"indexer": idx_bytes, "sparse_attn": sfa_bytes, "total": idx_bytes + sfa_bytes,
             "indexer_flops": idx_flops, "sparse_attn_flops": sfa_flops}
 
@@ -94,18 +110,24 @@ class Step:
         self.k = [case.k_cache] + [case.k_cache.clone() for _ in range(replicas - 1)]
         self.ks = ([case.k_scale] + [case.k_scale.clone() for _ in range(replicas - 1)]
                    if case.k_scale is not None else [None] * replicas)
-        self.kv = [case.kv_cache] + [case.kv_cache.clone() for _ in range(replicas - 1)]
+        self.kv = ([case.kv_cache] + [case.kv_cache.clone() for _ in range(replicas - 1)]
+                   if case.kv_cache is not None else [None] * replicas)
         dev = case.q_idx.device
         T, K = case.num_tokens, case.topk
         self.idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-        odt = torch.float32 if case.sfa_dtype == "f32" else torch.int16
-        self.out = torch.empty((T, case.n_heads_sfa, case.v_dim), dtype=odt, device=dev)
-        self.lse = torch.empty((T, case.n_heads_sfa), dtype=torch.float32, device=dev)
+        if case.sfa_dtype != "none":
+            odt = torch.float32 if case.sfa_dtype == "f32" else torch.int16
+            self.out = torch.empty((T, case.n_heads_sfa, case.v_dim), dtype=odt, device=dev)
+            self.lse = torch.empty((T, case.n_heads_sfa), dtype=torch.float32, device=dev)
         self.paged = dsa.make_paged(case.q_offsets, case.ctx_lens, case.block_table, case.num_pages,
                                     max_q_per_req=case.max_q_per_req, max_ctx_len=case.max_ctx,
                                     num_q_tokens=T)
         self.indexers = [dsa.make_indexer(case.q_idx, case.weights, self.k[r], K, case.idx_dtype,
                                           q_scale=case.q_scale, k_scale=self.ks[r]) for r in range(replicas)]
+        self.scores = None
+        if case.sfa_dtype == "none":  # scoring only
+            self.sfas = None
+            return
         self.sfas = [dsa.make_sfa(case.q_sfa, self.kv[r], self.out, case.scale, case.sfa_dtype, lse=self.lse,
                                   v_dim=case.v_dim) for r in range(replicas)]
         n_fused = dsa.fused_decode_workspace_size(self.paged, self.indexers[0], self.sfas[0])
@@ -124,6 +146,13 @@ class Step:
 
     def sparse_attn(self, s: int, stream):
         dsa.sparse_attn(self.paged, self.sfas[s % self.R], self.idx, workspace=self.ws2, stream=stream)
+
+    def scores_only(self, s: int, stream):
+        """The indexer's scoring kernel alone (dsa_indexer_scores)."""
+        if self.scores is None:
+            self.scores = torch.empty((self.case.num_tokens, self.case.max_ctx), dtype=torch.float32,
+                                      device=self.case.q_idx.device)
+        dsa.indexer_scores(self.paged, self.indexers[s % self.R], self.scores, stream=stream)
 
 
 def kernel_source_hash() -> str:
@@ -187,6 +216,27 @@ def stage_breakdown(step: Step, steps, stream):
     return idx, sfa
 
 
+def prefill_scoring(steps: int, warmup: int, stream):
+    """MFMA utilisation of the indexer's scoring kernel on the chunked-prefill
+    shape (4096 rows x 64 heads x 128 bf16 against 65536 positions, causal):
+    useful flops (2 H_I D_I per visible pair) over the kernel's average
+    duration from HIP events on the launch stream."""
+    case = WORKLOADS["chunked_prefill"]["make"](torch.device("cuda:0"), sfa=False)
+    step = Step(case, 1)
+    for s in range(warmup):
+        step.scores_only(s, stream)
+    ms = time_steps(step.scores_only, steps, stream)
+    flops = algorithmic_bytes(case)["indexer_flops"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[case.idx_dtype]
+    out = {"kernel": "indexer scores, row-tiled MFMA (li_prefill)", "workload": WORKLOADS["chunked_prefill"]["desc"],
+           "bound": "mfma", "ms": ms, "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+           "useful_flops": flops, "steps": steps, "warmup": warmup}
+    del step, case
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case: inputs.Case, step: Step, budget_s: float):
     """The CPU oracle on a bounded sample of the workload (whole steps, or a
     subset of query rows), on this host's cores; also checks the GPU result of
@@ -238,6 +288,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to exceed 512 MB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=20,
+                    help="steps of the chunked-prefill scoring measurement (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain MB-sized device copy (counter calibration)")
     args = ap.parse_args()
@@ -273,8 +325,20 @@ def main():
     tokens_per_s = T / (ms * 1e-3)
     dom = "indexer" if t_idx >= t_sfa else "sparse_attn"
     dom_ms = t_idx if dom == "indexer" else t_sfa
-    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
-    kname = "indexer_topk" if dom == "indexer" else "sparse_attn"
+    if case.max_q_per_req > 4 and case.idx_dtype in MFMA_PEAK_TFLOPS and dom == "indexer":
+        # many rows per request: the scoring GEMM dominates and is MFMA-bound
+        t_sc = time_steps(step.scores_only, args.steps, stream)
+        peak = MFMA_PEAK_TFLOPS[case.idx_dtype]
+        ach = ab["indexer_flops"] / (t_sc * 1e-3) / 1e12
+        roofline = {"kernel": "indexer_scores", "bound": "mfma", "achieved": ach, "peak": peak,
+                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": measured_traffic("indexer_scores", args.workload),
+                    "algorithmic_flops": ab["indexer_flops"], "kernel_ms": t_sc}
+    else:
+        kname = "indexer_topk" if dom == "indexer" else "sparse_attn"
+        achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kname, args.workload),
+                    "algorithmic_bytes": ab[dom], "kernel_ms": dom_ms}
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -294,13 +358,17 @@ def main():
         "hbm_gbs_step": ab["total"] / (ms * 1e-3) / 1e9,
         "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa},
-        "roofline": {"kernel": kname, "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kname, args.workload),
-                     "algorithmic_bytes": ab[dom]},
+        "roofline": roofline,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if args.prefill_steps and args.workload != "chunked_prefill":
+        del step
+        torch.cuda.empty_cache()
+        result["prefill_indexer_mfma"] = prefill_scoring(args.prefill_steps, max(2, args.prefill_steps // 10), stream)
+        step = None
     if not args.no_cpu:
+        if step is None:
+            step = Step(case, 1)
         result["cpu_baseline"] = cpu_baseline(case, step, args.cpu_budget)
     print(json.dumps(result), flush=True)
 

@@ -99,7 +99,7 @@ typedef struct {
     const float *weights;      /* [T][H_I] head-importance weights */
     const void *k_cache;       /* [num_pages][64][D_I] */
     const float *k_scale;      /* [num_pages][64] for FP8_E4M3, else NULL */
-    int32_t flags;             /* 0, or DSA_INDEXER_TWO_PASS */
+    int32_t flags;             /* 0, or DSA_INDEXER_* flags below */
 } dsa_indexer_t;
 
 /* Indexer flag: always take the two-pass route (scoring kernel, then one
@@ -107,6 +107,17 @@ typedef struct {
  * are identical; the fused kernel is used by default when every request has
  * at most 4 query rows and max_ctx_len <= 32768. */
 #define DSA_INDEXER_TWO_PASS 1
+
+/* Indexer flags: take the two-pass route and pick its scoring kernel.
+ * SCORE_ROWS is the row-tiled MFMA kernel (a workgroup per 4 query rows of a
+ * request walks all of the request's positions; BF16/FP8 only, FP32 gives
+ * DSA_ERR_UNSUPPORTED); SCORE_POSITIONS is the position-tiled kernel (a
+ * workgroup per 256 positions and 4 query rows).  Setting both is
+ * DSA_ERR_INVALID_ARG.  Without either the library picks by shape (rows when
+ * a request has more than 4 query rows and there are at least 1024 rows).
+ * Scores, and so results, are identical on every route. */
+#define DSA_INDEXER_SCORE_ROWS 2
+#define DSA_INDEXER_SCORE_POSITIONS 4
 
 /* Sparse flash attention over a shared MLA latent cache: the key of a
  * position is its whole row (qk_dim = 576 = 512 latent + 64 rope), the value
@@ -132,6 +143,20 @@ size_t dsa_indexer_topk_workspace_size(const dsa_paged_t *paged, const dsa_index
  * [T][topk] int32 (written in full). */
 dsa_status_t dsa_indexer_topk(const dsa_paged_t *paged, const dsa_indexer_t *idx,
                               int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Steps 1-2 up to the weighted scores, without selection: for every query
+ * row i (position pos_i = L_b - n_b + j) and every t <= pos_i,
+ * scores[i * score_stride + t] = sum_h w_h * max(q_h . k_t, 0) (fp8: the
+ * scaled form), in fp32 ("Optimizing Inference for Hybrid Attention
+ * Architectures: From Operator Fusion to Sequence Sharding", section
+ * "Breaking Down the Computational Path of Hybrid Attention", item 1).
+ * scores is device [T][score_stride] fp32 with score_stride >= max_ctx_len;
+ * entries t > pos_i are not written.  The values are bit-identical to the
+ * ones dsa_indexer_topk selects from (it is its scoring kernel alone, taken
+ * as the flags choose; DSA_INDEXER_TWO_PASS has no effect).  Needs no
+ * workspace.  INVALID_ARG for a NULL scores or a short score_stride. */
+dsa_status_t dsa_indexer_scores(const dsa_paged_t *paged, const dsa_indexer_t *idx,
+                                float *scores, int64_t score_stride, void *stream);
 
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_t *paged, const dsa_sfa_t *sfa,
                                       int32_t topk);

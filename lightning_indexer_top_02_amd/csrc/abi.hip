@@ -38,10 +38,13 @@ dsa_status_t check_indexer(const dsa_paged_t* pg, const dsa_indexer_t* x) {
   if (x->n_heads < 1 || x->head_dim < 1 || x->topk < 1) return DSA_ERR_INVALID_ARG;
   if (x->dtype != DSA_F32 && x->dtype != DSA_BF16 && x->dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
   if (x->dtype == DSA_FP8_E4M3 && (!x->q_scale || !x->k_scale)) return DSA_ERR_INVALID_ARG;
-  if (x->flags & ~DSA_INDEXER_TWO_PASS) return DSA_ERR_INVALID_ARG;
+  constexpr int32_t kRouteFlags = DSA_INDEXER_SCORE_ROWS | DSA_INDEXER_SCORE_POSITIONS;
+  if (x->flags & ~(DSA_INDEXER_TWO_PASS | kRouteFlags)) return DSA_ERR_INVALID_ARG;
+  if ((x->flags & kRouteFlags) == kRouteFlags) return DSA_ERR_INVALID_ARG;
   if (x->n_heads > kMaxIdxHeads || x->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
   if (x->head_dim != 64 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (x->dtype == DSA_F32 && x->n_heads * x->head_dim > 4096) return DSA_ERR_UNSUPPORTED;
+  if (x->dtype == DSA_F32 && (x->flags & DSA_INDEXER_SCORE_ROWS)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -145,7 +148,8 @@ DsaIndexerLaunch indexer_args(const dsa_paged_t* pg, const dsa_indexer_t* x, int
   a.hist = reinterpret_cast<uint32_t*>(ws + plan.hist_off);
   a.scores = reinterpret_cast<float*>(ws + plan.scores_off);
   a.score_stride = plan.score_stride;
-  a.force_two_pass = (x->flags & DSA_INDEXER_TWO_PASS) != 0;
+  a.force_two_pass = (x->flags & (DSA_INDEXER_TWO_PASS | DSA_INDEXER_SCORE_ROWS | DSA_INDEXER_SCORE_POSITIONS)) != 0;
+  a.score_route = (x->flags & DSA_INDEXER_SCORE_ROWS) ? 1 : (x->flags & DSA_INDEXER_SCORE_POSITIONS) ? 2 : 0;
   return a;
 }
 
@@ -228,6 +232,20 @@ dsa_status_t dsa_indexer_topk(const dsa_paged_t* pg, const dsa_indexer_t* x, int
   if ((st = check_device()) != DSA_OK) return st;
   DsaIndexerLaunch a = indexer_args(pg, x, topk_idx, static_cast<unsigned char*>(ws), plan);
   return dsa_launch_indexer_topk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+dsa_status_t dsa_indexer_scores(const dsa_paged_t* pg, const dsa_indexer_t* x, float* scores,
+                                int64_t score_stride, void* stream) {
+  dsa_status_t st = check_indexer(pg, x);
+  if (st != DSA_OK) return st;
+  if (!scores || score_stride < pg->max_ctx_len) return DSA_ERR_INVALID_ARG;
+  if ((st = check_device()) != DSA_OK) return st;
+  DsaIndexerLaunch a = indexer_args(pg, x, nullptr, nullptr, IndexerPlan{});
+  a.counters = nullptr;
+  a.hist = nullptr;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  return dsa_launch_indexer_scores(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) {

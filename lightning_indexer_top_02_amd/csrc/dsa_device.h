@@ -72,10 +72,11 @@ struct DsaIndexerLaunch {
   int32_t* out_idx;
   // workspace
   uint32_t* counters;  // [batch] arrival counters of the fused kernel, zero between calls
-  uint32_t* hist;      // [rows][kHistStride] digit histograms (two-pass), zero between calls
+  uint32_t* hist;      // [rows][kHistStride] digit histograms (two-pass), zero between calls; null: scores only
   float* scores;       // [rows][score_stride] scores (two-pass) or score keys (fused)
   int64_t score_stride;
   bool force_two_pass; // skip the fused kernel
+  int score_route;     // two-pass scoring: 0 chosen by shape, 1 row-tiled, 2 position-tiled
 };
 
 struct DsaSfaLaunch {
@@ -99,4 +100,8 @@ struct DsaSfaLaunch {
 
 hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s);
+// Scoring kernel of the two-pass route alone (a.hist may be null: no histograms).
+hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s);
+hipError_t dsa_launch_indexer_prefill_scores(const DsaIndexerLaunch& a, hipStream_t s);
+bool dsa_indexer_rows_route(const DsaIndexerLaunch& a);
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s);

@@ -2,7 +2,9 @@
 // HBM, then one selection workgroup per query row.
 //
 // Used when rows are too long (or too many per request) for the single fused
-// kernel (indexer_fused.hip).  The scoring follows "Optimizing Inference for
+// kernel (indexer_fused.hip).  Requests with many query rows (chunked prefill)
+// are scored by the row-tiled MFMA kernel of indexer_prefill.hip instead of
+// li_score; both write the same scores and histograms.  The scoring follows "Optimizing Inference for
 // Hybrid Attention Architectures: From Operator Fusion to Sequence Sharding",
 // section "Breaking Down the Computational Path of Hybrid Attention", item 1,
 // reading keys straight from the paged K cache ("Day0 Inference Support and
@@ -41,7 +43,7 @@ struct LiParams {
   const float* k_scale;
   float* scores;
   int64_t score_stride;
-  uint32_t* hist;  // [rows][kHistStride]; level-1 digit histogram at offset 0
+  uint32_t* hist;  // [rows][kHistStride]; level-1 digit histogram at offset 0 (null: scores only)
 };
 
 constexpr int kRowsPerBlock = 4;
@@ -104,6 +106,7 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
     }
   }
   __syncthreads();
+  if (!p.hist) return;
   for (int c = threadIdx.x; c < br.nrows * kHistBins; c += kScoreThreads) {
     const uint32_t v = hl[c];
     if (v) {
@@ -315,7 +318,7 @@ static hipError_t launch_score(const LiParams& p, dim3 grid, hipStream_t s) {
   return launch_dyn(li_score<DT, D>, grid, dim3(kScoreThreads), lds, s, p);
 }
 
-hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s) {
+hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s) {
   LiParams p;
   p.q_offsets = a.q_offsets;
   p.ctx_lens = a.ctx_lens;
@@ -334,15 +337,24 @@ hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s)
   p.score_stride = a.score_stride;
   p.hist = a.hist;
 
-  const dim3 grid((a.max_ctx_len + kChunk - 1) / kChunk, (a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock,
-                  a.batch);
   hipError_t e;
-  const bool d64 = a.head_dim == 64;
-  switch (a.dtype) {
-    case 0: e = d64 ? launch_score<0, 64>(p, grid, s) : launch_score<0, 128>(p, grid, s); break;
-    case 1: e = d64 ? launch_score<1, 64>(p, grid, s) : launch_score<1, 128>(p, grid, s); break;
-    default: e = d64 ? launch_score<2, 64>(p, grid, s) : launch_score<2, 128>(p, grid, s); break;
+  if (dsa_indexer_rows_route(a)) {
+    e = dsa_launch_indexer_prefill_scores(a, s);
+  } else {
+    const dim3 grid((a.max_ctx_len + kChunk - 1) / kChunk, (a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock,
+                    a.batch);
+    const bool d64 = a.head_dim == 64;
+    switch (a.dtype) {
+      case 0: e = d64 ? launch_score<0, 64>(p, grid, s) : launch_score<0, 128>(p, grid, s); break;
+      case 1: e = d64 ? launch_score<1, 64>(p, grid, s) : launch_score<1, 128>(p, grid, s); break;
+      default: e = d64 ? launch_score<2, 64>(p, grid, s) : launch_score<2, 128>(p, grid, s); break;
+    }
   }
+  return e;
+}
+
+hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s) {
+  hipError_t e = dsa_launch_indexer_scores(a, s);
   if (e != hipSuccess) return e;
 
   TopkParams tp;

@@ -21,7 +21,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK = 0
-INDEXER_TWO_PASS = 1  # flag: scores through the workspace instead of the fused team kernel
+INDEXER_TWO_PASS = 1  # flag: scores through the workspace instead of the fused kernel
+INDEXER_SCORE_ROWS = 2  # flag: two-pass route, row-tiled MFMA scoring kernel
+INDEXER_SCORE_POSITIONS = 4  # flag: two-pass route, position-tiled scoring kernel
 DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2}
 _STORAGE = {
     "f32": (torch.float32,),
@@ -100,6 +102,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_indexer_topk_workspace_size.argtypes = [PP, PI]
         lib.dsa_indexer_topk.restype = ctypes.c_int
         lib.dsa_indexer_topk.argtypes = [PP, PI, P, P, S, P]
+        lib.dsa_indexer_scores.restype = ctypes.c_int
+        lib.dsa_indexer_scores.argtypes = [PP, PI, P, ctypes.c_int64, P]
         lib.dsa_sparse_attn_workspace_size.restype = S
         lib.dsa_sparse_attn_workspace_size.argtypes = [PP, PS, ctypes.c_int32]
         lib.dsa_sparse_attn.restype = ctypes.c_int
@@ -228,6 +232,19 @@ def indexer_topk(paged: Paged, idx: Indexer, out: torch.Tensor, workspace=None, 
     if st != DSA_OK:
         raise DsaError(st, "dsa_indexer_topk")
     return out
+
+
+def indexer_scores(paged: Paged, idx: Indexer, scores: torch.Tensor, stream=None):
+    """Weighted indexer scores into ``scores`` (float32 [T][stride], stride >=
+    max_ctx_len); entries past a row's position are left as they were."""
+    _check_tensor(scores, "scores", (torch.float32,))
+    if scores.dim() != 2 or scores.shape[0] < paged.num_q_tokens:
+        raise ValueError("scores must be 2-D [T][stride] with a row per query token")
+    st = load().dsa_indexer_scores(ctypes.byref(paged), ctypes.byref(idx), _ptr(scores),
+                                   int(scores.shape[1]), _stream(stream))
+    if st != DSA_OK:
+        raise DsaError(st, "dsa_indexer_scores")
+    return scores
 
 
 def sparse_attn_workspace_size(paged: Paged, sfa: Sfa, topk: int) -> int:

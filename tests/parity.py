@@ -46,10 +46,17 @@ def paged_of(case: inputs.Case) -> dsa.Paged:
                           num_q_tokens=case.num_tokens)
 
 
-def indexer_of(case: inputs.Case, topk=None, two_pass=False) -> dsa.Indexer:
+def indexer_of(case: inputs.Case, topk=None, flags=0) -> dsa.Indexer:
     return dsa.make_indexer(case.q_idx, case.weights, case.k_cache, topk or case.topk, case.idx_dtype,
-                            q_scale=case.q_scale, k_scale=case.k_scale,
-                            flags=dsa.INDEXER_TWO_PASS if two_pass else 0)
+                            q_scale=case.q_scale, k_scale=case.k_scale, flags=flags)
+
+
+def indexer_routes(case: inputs.Case):
+    """Flags that force each indexer route the case supports."""
+    routes = {"default": 0, "positions": dsa.INDEXER_SCORE_POSITIONS}
+    if case.idx_dtype != "f32" and case.n_heads_idx <= 64:
+        routes["rows"] = dsa.INDEXER_SCORE_ROWS
+    return routes
 
 
 def sfa_tensors(case: inputs.Case):
@@ -59,14 +66,21 @@ def sfa_tensors(case: inputs.Case):
     return out, lse
 
 
-def gpu_indexer_topk(case: inputs.Case, topk=None, two_pass=False) -> torch.Tensor:
-    """Indices from dsa_indexer_topk (fused route unless two_pass)."""
+def gpu_indexer_topk(case: inputs.Case, topk=None, flags=0) -> torch.Tensor:
+    """Indices from dsa_indexer_topk (route chosen by the library unless flags force one)."""
     K = topk or case.topk
     out = torch.full((case.num_tokens, K), -7, dtype=torch.int32, device=case.q_idx.device)
-    paged, idx = paged_of(case), indexer_of(case, K, two_pass)
+    paged, idx = paged_of(case), indexer_of(case, K, flags)
     ws = dsa.new_workspace(dsa.indexer_topk_workspace_size(paged, idx), case.q_idx.device)
     dsa.indexer_topk(paged, idx, out, workspace=ws)
     return out
+
+
+def gpu_indexer_scores(case: inputs.Case, flags=0) -> torch.Tensor:
+    """Weighted scores from dsa_indexer_scores; never-written entries stay NaN."""
+    sc = torch.full((case.num_tokens, case.max_ctx), float("nan"), dtype=torch.float32, device=case.q_idx.device)
+    dsa.indexer_scores(paged_of(case), indexer_of(case, flags=flags), sc)
+    return sc
 
 
 def gpu_sparse_attn(case: inputs.Case, idx: torch.Tensor):
@@ -148,6 +162,42 @@ def compare_topk(gpu_idx, ora_idx, ora_scores, vis, exact: bool, rows=None):
     return {"positions_in_band": n_diff, "max_rel_from_threshold": max_rel}
 
 
+# Score tolerance relative to the row's term magnitude.  fp32 and bf16:
+# fp32 accumulation-order differences only (bf16 products are exact in fp32).
+# fp8: gfx950's fp8 MFMA does not sum its 32 products in full fp32 (an
+# in-bounds probe: one 448 x 1 product plus 31 products of 2^-6 gives 448.875
+# for 448.984375, and 448^2 + 31 x 1 loses 7 of the 31), so its dot products
+# carry errors of a few 1e-5 of their largest product.
+SCORE_REL_TOL = {"f32": 1e-5, "bf16": 1e-5, "fp8": 1e-4}
+
+
+def compare_scores(gpu_scores, ora_scores, vis, exact: bool, magnitude=None, dtype="bf16"):
+    """Scores of the visible positions equal (exact mode) or within
+    SCORE_REL_TOL[dtype] of the row's largest term magnitude
+    M_t = sum_h |w_h| ReLU(l_h) (``magnitude``: the oracle's scores with |w|;
+    without it, the row's largest |score|).  The summation error of a sum of
+    signed terms is bounded by the sum of their absolute values times the
+    rounding unit, not by the sum itself.  Nothing past a row's position may
+    be written."""
+    g = gpu_scores.cpu().double().numpy() if isinstance(gpu_scores, torch.Tensor) else np.asarray(gpu_scores)
+    o = np.asarray(ora_scores)
+    m = np.abs(o) if magnitude is None else np.asarray(magnitude)
+    worst = 0.0
+    for i in range(o.shape[0]):
+        v = int(vis[i])
+        gi, oi = g[i, :v], o[i, :v]
+        assert np.all(np.isfinite(gi)), f"row {i}: non-finite GPU score"
+        assert np.all(np.isnan(g[i, v:])), f"row {i}: GPU wrote past the row's position"
+        if exact:
+            assert np.array_equal(gi, oi), f"row {i}: scores differ in exact mode"
+            continue
+        scale = float(np.max(m[i, :v], initial=0.0)) or 1.0
+        err = float(np.max(np.abs(gi - oi), initial=0.0)) / scale
+        assert err <= SCORE_REL_TOL[dtype], f"row {i}: score error {err:.3g} of the row's term magnitude"
+        worst = max(worst, err)
+    return {"score_max_rel_err": worst}
+
+
 def compare_out(gpu_out, ora_out, dtype: str, tol=None, gpu_lse=None, ora_lse=None):
     g = out_to_f64(gpu_out, dtype)
     err = float(np.max(np.abs(g - ora_out))) if g.size else 0.0
@@ -166,12 +216,13 @@ def compare_out(gpu_out, ora_out, dtype: str, tol=None, gpu_lse=None, ora_lse=No
 
 
 def check_case(case: inputs.Case, tol=None, nthreads=None, fused=True):
-    """Full parity of one case: both indexer routes (identical to each other,
+    """Full parity of one case: every indexer route (identical to each other,
     and to the oracle up to the bar), SFA on the GPU's indices, fused path."""
     vis = oracle.visible(_np(case.q_offsets), _np(case.ctx_lens))
     g_idx = gpu_indexer_topk(case)
-    g_idx2 = gpu_indexer_topk(case, two_pass=True)
-    assert torch.equal(g_idx, g_idx2), "fused and two-pass indexer routes disagree"
+    for name, flags in indexer_routes(case).items():
+        if flags:
+            assert torch.equal(g_idx, gpu_indexer_topk(case, flags=flags)), f"indexer route '{name}' disagrees"
     o_idx, o_sc = oracle_indexer(case, nthreads=nthreads)
     stats = compare_topk(g_idx, o_idx, o_sc, vis, case.exact)
     if case.sfa_dtype != "none":

@@ -88,7 +88,8 @@ def test_bad_paging_rejected(kw):
 BAD_INDEXER = [(dict(q=None), 1), (dict(weights=None), 1), (dict(k_cache=None), 1), (dict(topk=0), 1),
                (dict(n_heads=0), 1), (dict(dtype=7), 1), (dict(dtype=2), 1),  # fp8 without scales
                (dict(dtype=2, q_scale=FAKE), 1), (dict(n_heads=65), 2), (dict(topk=4097), 2),
-               (dict(head_dim=96), 2), (dict(dtype=0, n_heads=64, head_dim=128), 2), (dict(flags=2), 1)]
+               (dict(head_dim=96), 2), (dict(dtype=0, n_heads=64, head_dim=128), 2), (dict(flags=8), 1),
+               (dict(flags=6), 1), (dict(flags=7), 1), (dict(dtype=0, n_heads=4, head_dim=64, flags=2), 2)]
 
 
 @pytest.mark.parametrize("kw,status", BAD_INDEXER, ids=[str(k) for k, _ in BAD_INDEXER])
@@ -149,3 +150,13 @@ def test_workspace_sizes():
     assert s_bf16 > 0 and s_bf16 % 256 == 0
     s_f32 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa(dtype=0, n_heads=16)), 256)
     assert s_f32 == 0
+
+
+def test_indexer_scores_argument_checks():
+    lib = dsa.load()
+    sc = ctypes.c_void_p(FAKE)
+    assert lib.dsa_indexer_scores(ctypes.byref(good_paged()), ctypes.byref(good_indexer()), None, 4096, None) == 1
+    short = good_paged().max_ctx_len - 1
+    assert lib.dsa_indexer_scores(ctypes.byref(good_paged()), ctypes.byref(good_indexer()), sc, short, None) == 1
+    assert lib.dsa_indexer_scores(ctypes.byref(good_paged()), ctypes.byref(good_indexer(n_heads=65)), sc,
+                                  1 << 20, None) == 2

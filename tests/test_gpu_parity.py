@@ -5,6 +5,8 @@ the 1e-3 threshold band; outputs within 2e-2 (bf16/fp32 storage) of the
 oracle run on the GPU's own indices; the fused call equals the two separate
 calls bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -104,6 +106,87 @@ def test_chunked_prefill_small(exact):
     _run(inputs.chunked_prefill(prefix=1000, new=300, exact=exact))
 
 
+# --- many query rows per request: the row-tiled scoring kernel -----------------
+# Requests of 300, 17, 130 (a from-scratch prefill: every position is a query
+# row) and 5 rows; head counts with and without padding to 16.
+PREFILL_LENS = [700, 2000, 130, 64]
+PREFILL_NQ = [300, 17, 130, 5]
+
+
+@pytest.mark.parametrize("dtype,dim,heads", [("bf16", 128, 64), ("bf16", 64, 40), ("fp8", 128, 64),
+                                             ("fp8", 64, 23)])
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_prefill_ragged_rows(dtype, dim, heads, exact):
+    _run(inputs.make_case(name=f"prefill_ragged_{dtype}_{dim}x{heads}", seed=90, ctx_lens=PREFILL_LENS,
+                          n_q=PREFILL_NQ, idx_dtype=dtype, n_heads_idx=heads, head_dim_idx=dim, topk=256,
+                          sfa_dtype="bf16", n_heads_sfa=16, exact=exact), fused=False)
+
+
+# --- scores alone (dsa_indexer_scores) against the oracle's scores -------------
+SCORE_CASES = {
+    "tiny_f32": lambda exact: inputs.tiny_decode(exact=exact),
+    "ragged_bf16": lambda exact: inputs.make_case(name="sc_bf16", seed=91, ctx_lens=PREFILL_LENS, n_q=PREFILL_NQ,
+                                                  idx_dtype="bf16", n_heads_idx=64, head_dim_idx=128, topk=64,
+                                                  sfa_dtype=None, exact=exact),
+    "ragged_fp8_d64": lambda exact: inputs.make_case(name="sc_fp8", seed=92, ctx_lens=PREFILL_LENS, n_q=PREFILL_NQ,
+                                                     idx_dtype="fp8", n_heads_idx=19, head_dim_idx=64, topk=64,
+                                                     sfa_dtype=None, exact=exact),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCORE_CASES))
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_indexer_scores(name, exact):
+    case = parity.to_device(SCORE_CASES[name](exact))
+    print(f"\n[case] scores {case.name} T={case.num_tokens}", flush=True)
+    vis = oracle.visible(case.q_offsets.cpu().numpy(), case.ctx_lens.cpu().numpy())
+    _, o_sc = parity.oracle_indexer(case)
+    _, mag = parity.oracle_indexer(dataclasses.replace(case, weights=case.weights.abs()))
+    first = None
+    for route, flags in parity.indexer_routes(case).items():
+        g = parity.gpu_indexer_scores(case, flags)
+        print(route, parity.compare_scores(g, o_sc, vis, case.exact, mag, case.idx_dtype), flush=True)
+        if first is None:
+            first = g
+        else:
+            assert torch.equal(torch.nan_to_num(first, nan=7.0), torch.nan_to_num(g, nan=7.0)), route
+
+
+# --- full-size workloads, checked on sampled rows -----------------------------
+def _full(case, rows, routes=True):
+    print(f"\n[case] {case.name} seed={case.seed} B={case.batch} T={case.num_tokens} "
+          f"max_ctx={case.max_ctx} K={case.topk} rows={rows}", flush=True)
+    idx = parity.gpu_indexer_topk(case)
+    if routes:
+        for name, flags in parity.indexer_routes(case).items():
+            if flags:
+                assert torch.equal(idx, parity.gpu_indexer_topk(case, flags=flags)), f"route {name} differs"
+    out, _ = parity.gpu_sparse_attn(case, idx)
+    stats = parity.check_rows(case, idx, out, rows)
+    print(f"[ok] {case.name}: {stats}", flush=True)
+
+
+def test_chunked_prefill_full():
+    """4096 query rows appended to a 61440-token prefix (65536 positions)."""
+    case = inputs.chunked_prefill(device="cuda")
+    _full(case, [0, 1, 1000, 2047, 3333, 4095])
+
+
+def test_spec_verify_full():
+    """16 requests x 4 causal query rows at 262144 positions, fp8 indexer."""
+    case = inputs.spec_verify(device="cuda")
+    _full(case, [0, 3, 17, 38, 60, 63], routes=False)
+
+
+@pytest.mark.parametrize("wide", [False, True], ids=["narrow", "wide"])
+def test_batched_fp8_full(wide):
+    """64 single-row requests, lengths uniform in [4096, 131072], fp8 indexer."""
+    case = inputs.batched_decode_fp8(wide=wide, device="cuda")
+    lens = case.ctx_lens.cpu()
+    rows = sorted({0, 63, int(lens.argmax()), int(lens.argmin()), 21, 42})
+    _full(case, rows)
+
+
 def test_causal_planted_future_keys_never_selected():
     """Keys after a row's position made huge must never be selected."""
     case = inputs.spec_verify(batch=1, ctx=3000, exact=True)
@@ -168,4 +251,5 @@ def test_workspace_reuse_across_calls(name):
             assert torch.equal(out, first), f"call {it} differs"
     ctrl = ws[: 4 * case.batch].view(torch.int32)
     assert int(ctrl.abs().sum()) == 0, "arrival counters not back to zero"
-    assert torch.equal(first, parity.gpu_indexer_topk(case, two_pass=True))
+    for flags in parity.indexer_routes(case).values():
+        assert torch.equal(first, parity.gpu_indexer_topk(case, flags=flags))
