@@ -10,17 +10,26 @@
 // head dim, i.e. a GEMM of [rows x heads, D] by [D, positions], followed by
 // ReLU, the head weights and a sum over heads.
 //
-// A workgroup owns 4 query rows of one request, one per wave.  A wave keeps
+// A workgroup owns 8 query rows of one request, one per wave.  A wave keeps
 // its row's whole query (64 heads x D) in registers as the MFMA A operand and
-// walks the request's positions in tiles of 128, which the four waves share
+// walks the request's positions in tiles of 128, which the eight waves share
 // through LDS (the next tile's keys are in flight in registers while the
-// current one is used).  Per 64 positions a wave runs heads x positions x D
-// as 16x16x32 MFMAs into 4 x 4 accumulator tiles, then folds ReLU, the
-// weights and the 64-head sum into the accumulators (the heads of a position
-// sit in one lane column, so the sum is in-lane plus two lane swaps) and
-// writes 64 fp32 scores.  Tiles past the causal edge of the rows are skipped.
-// Each row's level-1 digit histogram (top 11 key bits) is complete inside
-// the workgroup, so it is stored without atomics for the selection kernel.
+// current one is used, and its block-table entries one tile further ahead).
+//
+// Within a tile a wave takes 32 positions at a time: 64 heads x 32 positions
+// x D as 16x16x32 MFMAs into 4 x 2 accumulator tiles, with the key fragments
+// of each contraction step read from LDS one step ahead.  The epilogue of a
+// sub-tile (ReLU, weights, the 64-head sum, the store) is issued together
+// with the MFMAs of the next one, on a second accumulator set, so the vector
+// ALU work overlaps the matrix cores instead of following them.  In the
+// accumulators the heads of a position sit in one lane column: lane group g
+// (lanes 16g .. 16g + 15) holds heads 16t + 4g + i, summed in-lane in
+// ascending head order; the four group sums are combined as
+// (s0 + s1) + (s2 + s3) with two row permutes, the order of the other indexer
+// kernels, so every scoring route gives bit-identical scores.  Tiles past the
+// causal edge of a row are skipped.  Each row's level-1 digit histogram (top
+// 11 key bits) is complete inside the workgroup, so it is stored without
+// atomics for the selection kernel.
 #include <algorithm>
 
 #include "dsa_device.h"
@@ -45,20 +54,24 @@ struct PrefillParams {
   uint32_t* hist;  // [rows][kHistStride]: level-1 histogram at offset 0 (null: scores only)
 };
 
-constexpr int kPfThreads = 256;
+constexpr int kPfThreads = 512;
 constexpr int kPfRows = kPfThreads / 64;  // query rows per workgroup
 constexpr int kPfTile = 128;              // positions per LDS tile
+constexpr int kPfSub = 32;                // positions per MFMA sub-tile
 constexpr int kPfHeads = 64;              // heads held in registers (H is padded to this)
 
 template <int DT, int D>
-__global__ __launch_bounds__(kPfThreads, 2) void li_prefill(PrefillParams p) {
+__global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   using Gm = IdxGeom<DT, D>;
   using frag_t = typename Gm::frag_t;
   constexpr int ES = Gm::ES;
   constexpr int KS = D / 32;                     // contraction steps
+  constexpr int MT = kPfHeads / 16;              // head tiles
+  constexpr int NSUB = kPfTile / kPfSub;         // sub-tiles per tile
   constexpr int KROW = D * ES + 16;              // padded LDS bytes per key row
   constexpr int TILE_BYTES = kPfTile * D * ES;   // key bytes per tile
   constexpr int VPT = TILE_BYTES / 16 / kPfThreads;  // 16-byte loads per thread per tile
+  static_assert(NSUB % 2 == 0, "sub-tiles alternate between two accumulator sets");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* ktile = smem;                                              // [kPfTile][KROW]
   float* ksc = reinterpret_cast<float*>(smem + kPfTile * KROW);             // [kPfTile] fp8 scales
@@ -79,12 +92,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void li_prefill(PrefillParams p) {
   for (int c = tid; c < kPfRows * kHistBins; c += kPfThreads) lhist[c] = 0u;
 
   // this wave's query row as A fragments: qf[mt][ks] = q[row][mt*16 + l16][ks*32 + g*8 ..]
-  frag_t qf[kPfHeads / 16][KS];
-  float wl[kPfHeads / 16][4];  // weights of heads mt*16 + 4g + i (times the q scale for fp8)
+  frag_t qf[MT][KS];
+  float wl[MT][4];  // weights of heads mt*16 + 4g + i (times the q scale for fp8)
   {
     const unsigned char* qg = static_cast<const unsigned char*>(p.q);
 #pragma unroll
-    for (int mt = 0; mt < kPfHeads / 16; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const int h = mt * 16 + l16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -109,97 +122,149 @@ __global__ __launch_bounds__(kPfThreads, 2) void li_prefill(PrefillParams p) {
   const int ntiles = (vis_last + kPfTile - 1) / kPfTile;
   const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
   const unsigned char* kg = static_cast<const unsigned char*>(p.k);
+  constexpr int PPR = D * ES / 16;       // 16-byte pieces per key row
+  constexpr int PAGES = kPfTile / kPage;  // pages per tile
+  // Physical pages of a tile (-1 past the last page any row here sees: those
+  // pieces are zero-filled).  They are loaded one tile ahead of the keys, so
+  // the key loads never wait on a block-table read.
+  auto load_phys = [&](int tile, int (&ph)[PAGES]) {
+#pragma unroll
+    for (int i = 0; i < PAGES; ++i) {
+      const int pg = tile * PAGES + i;
+      ph[i] = pg * kPage < vis_last ? btrow[pg] : -1;
+    }
+  };
   uint4 pre[VPT];
   float pre_s = 0.f;
-  auto fetch = [&](int tile) {
+  auto fetch = [&](const int (&ph)[PAGES]) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int c = tid + j * kPfThreads;        // 16-byte piece of the tile
-      const int pos = c / (D * ES / 16);         // position within the tile
-      const int part = c - pos * (D * ES / 16);
-      const int t = tile * kPfTile + pos;
+      const int c = tid + j * kPfThreads;  // 16-byte piece of the tile
+      const int pos = c / PPR;             // position within the tile
+      const int part = c - pos * PPR;
+      int phys = ph[0];
+#pragma unroll
+      for (int i = 1; i < PAGES; ++i) phys = (pos >> 6) == i ? ph[i] : phys;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t < vis_last) {  // the block table only covers the request's pages
-        const int phys = btrow[t >> 6];
-        v = *reinterpret_cast<const uint4*>(kg + ((int64_t)phys * kPage + (t & 63)) * (D * ES) + part * 16);
-      }
+      if (phys >= 0)
+        v = *reinterpret_cast<const uint4*>(kg + ((int64_t)phys * kPage + (pos & 63)) * (D * ES) + part * 16);
       pre[j] = v;
     }
     if (DT == 2 && tid < kPfTile) {
-      const int t = tile * kPfTile + tid;
-      pre_s = t < vis_last ? p.k_scale[(int64_t)btrow[t >> 6] * kPage + (t & 63)] : 0.f;
+      int phys = ph[0];
+#pragma unroll
+      for (int i = 1; i < PAGES; ++i) phys = (tid >> 6) == i ? ph[i] : phys;
+      pre_s = phys >= 0 ? p.k_scale[(int64_t)phys * kPage + (tid & 63)] : 0.f;
     }
   };
   auto stage = [&]() {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int c = tid + j * kPfThreads;
-      const int pos = c / (D * ES / 16);
-      const int part = c - pos * (D * ES / 16);
+      const int pos = c / PPR;
+      const int part = c - pos * PPR;
       *reinterpret_cast<uint4*>(ktile + pos * KROW + part * 16) = pre[j];
     }
     if (DT == 2 && tid < kPfTile) ksc[tid] = pre_s;
   };
 
-  if (ntiles > 0) fetch(0);
+  // Two accumulator sets: the MFMAs of a sub-tile go to one while the
+  // epilogue of the previous sub-tile reads the other.
+  f32x4 acc[2][MT][2];
+  float sc_k[2] = {1.f, 1.f};  // fp8: this lane's key scale, per set
+  // B fragments of contraction step ks of sub-tile sub (positions sub*32 + pt*16 + l16)
+  auto load_b = [&](frag_t (&bf)[2], int sub, int ks) {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+      bf[pt] = *reinterpret_cast<const frag_t*>(ktile + (sub * kPfSub + pt * 16 + l16) * KROW + (ks * 32 + g * 8) * ES);
+  };
+  // The MFMAs of one sub-tile.  bf holds its first step's fragments on entry;
+  // every step loads the next step's fragments (the next sub-tile's first one
+  // at the end, when there is one in this tile) before its own MFMAs, so the
+  // LDS latency is hidden behind them.
+  auto mfma_sub = [&](f32x4 (&a)[MT][2], float& kscale, int sub, frag_t (&bf)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) a[mt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag_t cur[2] = {bf[0], bf[1]};
+      if (ks + 1 < KS) load_b(bf, sub, ks + 1);
+      else if (sub + 1 < NSUB) load_b(bf, sub + 1, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) a[mt][pt] = mfma_16x16x32(qf[mt][ks], cur[pt], a[mt][pt]);
+    }
+    // the scale of the position this lane ends up holding (lanes g < 2)
+    if (DT == 2) kscale = ksc[sub * kPfSub + (g & 1) * 16 + l16];
+  };
+  // a[mt][pt][i] = logit of head mt*16 + 4g + i at position sub*32 + pt*16 + l16.
+  // Returns, on lanes g < 2, the score of position 16 (g & 1) + l16 of the
+  // sub-tile: in-lane group sums of each position tile, then two row swaps
+  // (VALU permutes, no LDS): lanes 16-row r and r^1 exchange so that even
+  // rows add up tile 0 and odd rows tile 1 of groups g, g^1, then the 32-lane
+  // halves exchange and add, giving (s0 + s1) + (s2 + s3).
+  auto epilogue = [&](const f32x4 (&a)[MT][2], float kscale) {
+    float sp[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      float s = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += wl[mt][i] * relu_keep_nan(a[mt][pt][i]);
+      sp[pt] = s;
+    }
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sp[0]), __float_as_uint(sp[1]), false, false);
+    const float pair = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+    float s = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    if (DT == 2) s *= kscale;
+    return s;
+  };
+  auto emit = [&](float s, int pos) {
+    if (g < 2 && pos < myvis) {
+      p.scores[(int64_t)row * p.score_stride + pos] = s;
+      atomicAdd(&lhist[wave * kHistBins + (score_key(s) >> kLevelShift[0])], 1u);
+    }
+  };
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) acc[1][mt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int pending = -1;  // first position of the sub-tile waiting in acc[1], or -1
+
+  int ph_next[PAGES];
+  load_phys(0, ph_next);
+  if (ntiles > 0) fetch(ph_next);
+  load_phys(1, ph_next);
   for (int tile = 0; tile < ntiles; ++tile) {
     __syncthreads();  // the previous tile is no longer read
     stage();
     __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);
-    if (!row_ok) continue;
-#pragma unroll 1
-    for (int sub = 0; sub < kPfTile / 64; ++sub) {
-      const int t0 = tile * kPfTile + sub * 64;
-      if (t0 >= myvis) break;
-      f32x4 acc[kPfHeads / 16][4];
-#pragma unroll
-      for (int mt = 0; mt < kPfHeads / 16; ++mt)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[mt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        frag_t bf[4];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          bf[pt] = *reinterpret_cast<const frag_t*>(ktile + (sub * 64 + pt * 16 + l16) * KROW + (ks * 32 + g * 8) * ES);
-#pragma unroll
-        for (int mt = 0; mt < kPfHeads / 16; ++mt)
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt) acc[mt][pt] = mfma_16x16x32(qf[mt][ks], bf[pt], acc[mt][pt]);
-      }
-      // acc[mt][pt][i] = logit of head mt*16 + 4g + i at position t0 + pt*16 + l16.
-      // In-lane head sums per position tile, then a reduce-scatter over the
-      // four lane groups that leaves lane (g, l16) with the score of position
-      // t0 + 16g + l16; the additions pair the groups as (g0+g1)+(g2+g3), the
-      // order the other indexer kernels use, so all routes agree bit for bit.
-      float sp[4];
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        float s = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < kPfHeads / 16; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s += wl[mt][i] * relu_keep_nan(acc[mt][pt][i]);
-        sp[pt] = s;
-      }
-      const bool lo = g & 1, hi = g >> 1;
-      // groups g, g^1: lo = 0 keeps tiles 0 and 2, lo = 1 keeps tiles 1 and 3
-      const float ka = lo ? sp[1] : sp[0], kb = lo ? sp[3] : sp[2];
-      const float sa = lo ? sp[0] : sp[1], sb = lo ? sp[2] : sp[3];
-      const float pa = ka + __shfl_xor(sa, 16), pb = kb + __shfl_xor(sb, 16);
-      // groups g, g^2: hi = 0 keeps tile lo, hi = 1 keeps tile 2 + lo
-      const float keep = hi ? pb : pa, send = hi ? pa : pb;
-      float s = keep + __shfl_xor(send, 32);
-      const int slot = sub * 64 + g * 16 + l16;
-      const int pos = tile * kPfTile + slot;
-      if (DT == 2) s *= ksc[slot];
-      if (pos < myvis) {
-        p.scores[(int64_t)row * p.score_stride + pos] = s;
-        atomicAdd(&lhist[wave * kHistBins + (score_key(s) >> kLevelShift[0])], 1u);
-      }
+    if (tile + 1 < ntiles) {
+      fetch(ph_next);
+      load_phys(tile + 2, ph_next);
     }
+    if (tile * kPfTile >= myvis) continue;  // (also every wave without a row)
+    frag_t bf[2];
+    load_b(bf, 0, 0);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int cur = sub & 1;
+      // the previous sub-tile (the last one of the previous tile when sub == 0)
+      const int prev_pos = sub == 0 ? pending : tile * kPfTile + (sub - 1) * kPfSub;
+      mfma_sub(acc[cur], sc_k[cur], sub, bf);
+      const float s = epilogue(acc[cur ^ 1], sc_k[cur ^ 1]);
+      if (prev_pos >= 0) emit(s, prev_pos + (g & 1) * 16 + l16);
+    }
+    pending = tile * kPfTile + (NSUB - 1) * kPfSub;
   }
+  if (pending >= 0) emit(epilogue(acc[1], sc_k[1]), pending + (g & 1) * 16 + l16);
+
   __syncthreads();
   if (!p.hist) return;
   for (int c = tid; c < nrows * kHistBins; c += kPfThreads) {
@@ -231,7 +296,7 @@ static hipError_t launch_prefill(const PrefillParams& p, dim3 grid, hipStream_t 
 bool dsa_indexer_rows_route(const DsaIndexerLaunch& a) {
   if (a.dtype == 0 || a.n_heads > kPfHeads) return false;
   if (a.score_route != 0) return a.score_route == 1;
-  return a.max_q_per_req > kPfRows && a.num_rows >= 256 * kPfRows;
+  return a.max_q_per_req > 4 && a.num_rows >= 1024;
 }
 
 // Scores and level-1 histograms of every row (bf16 or fp8 keys, at most 64
