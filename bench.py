@@ -31,6 +31,7 @@ from lightning_indexer_top_02_amd import dsa, inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense, MI355X
+VALU_F32_PEAK_TFLOPS = 157.3  # fp32 routes run on the vector ALUs
 METRIC = "DSA decode tokens/s + HBM GB/s (% peak) at 32K ctx; prefill indexer MFMA util"
 
 WORKLOADS = {
@@ -82,10 +83,13 @@ def algorithmic_bytes(case: inputs.Case):
              plus a 4-byte scale for fp8), q, w (and q scales), the block
              table, and the Top-K indices written; flops = 2 H_I D_I per
              visible (row, position) pair (the logits).
-    sparse attention: the indices read, K gathered latent rows per query row,
-             q and the output; flops = 2 H_q (576 + 512) per selected row.
+    sparse attention: the indices read, the latent rows gathered (each cached
+             row of a request at most once: min(sum over its rows of the
+             rows each selects, its length)), q and the output; flops =
+             2 H_q (576 + 512) per selected (query row, cached row) pair.
     """
     lens = case.ctx_lens.cpu().tolist()
+    qo = case.q_offsets.cpu().tolist()
     T, K = case.num_tokens, case.topk
     eK = elem_bytes(case.idx_dtype)
     key_row = case.head_dim_idx * eK + (4 if case.idx_dtype == "fp8" else 0)
@@ -93,12 +97,37 @@ def algorithmic_bytes(case: inputs.Case):
     idx_bytes = (sum(lens) * key_row + T * H * case.head_dim_idx * eK + T * H * 4 * (2 if case.idx_dtype == "fp8" else 1)
                  + sum((L + 63) // 64 for L in lens) * 4 + T * K * 4)
     eS = elem_bytes(case.sfa_dtype) if case.sfa_dtype != "none" else 0
-    sel = sum(min(v, K) for v in visible_per_row(case))
-    sfa_bytes = (T * K * 4 + sel * case.qk_dim * eS + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eS)
-    idx_flops = 2 * sum(visible_per_row(case)) * H * case.head_dim_idx
+    vis = visible_per_row(case)
+    sel = sum(min(v, K) for v in vis)
+    rows_read = sum(min(sum(min(v, K) for v in vis[qo[b]:qo[b + 1]]), lens[b]) for b in range(len(lens)))
+    sfa_bytes = (T * K * 4 + rows_read * case.qk_dim * eS + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eS)
+    idx_flops = 2 * sum(vis) * H * case.head_dim_idx
     sfa_flops = 2 * sel * case.n_heads_sfa * (case.qk_dim + case.v_dim)
     return {"indexer": idx_bytes, "sparse_attn": sfa_bytes, "total": idx_bytes + sfa_bytes,
             "indexer_flops": idx_flops, "sparse_attn_flops": sfa_flops}
+
+
+def compute_peak(dtype: str) -> float:
+    return MFMA_PEAK_TFLOPS.get(dtype, VALU_F32_PEAK_TFLOPS)
+
+
+def roofline_entry(kernel: str, workload: str, nbytes: float, flops: float, ms: float, peak_tflops: float):
+    """Roofline of one kernel (or call): the bound is whichever of HBM bytes
+    at 8 TB/s and flops at the compute peak takes longer; achieved is the
+    algorithmic figure over the measured duration."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_cmp = flops / (peak_tflops * 1e12)
+    sec = ms * 1e-3
+    if t_cmp > t_hbm:
+        ach = flops / sec / 1e12
+        return {"kernel": kernel, "bound": "mfma" if peak_tflops != VALU_F32_PEAK_TFLOPS else "alu",
+                "achieved": ach, "peak": peak_tflops, "unit": "TFLOP/s", "frac": ach / peak_tflops,
+                "traffic": measured_traffic(kernel, workload), "algorithmic_flops": flops,
+                "algorithmic_bytes": nbytes, "kernel_ms": ms}
+    ach = nbytes / sec / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(kernel, workload),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "kernel_ms": ms}
 
 
 class Step:
@@ -231,7 +260,8 @@ def prefill_scoring(steps: int, warmup: int, stream):
     peak = MFMA_PEAK_TFLOPS[case.idx_dtype]
     out = {"kernel": "indexer scores, row-tiled MFMA (li_prefill)", "workload": WORKLOADS["chunked_prefill"]["desc"],
            "bound": "mfma", "ms": ms, "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
-           "useful_flops": flops, "steps": steps, "warmup": warmup}
+           "useful_flops": flops, "traffic": measured_traffic("indexer_scores", "chunked_prefill"),
+           "steps": steps, "warmup": warmup}
     del step, case
     torch.cuda.empty_cache()
     return out
@@ -324,21 +354,20 @@ def main():
     T = case.num_tokens
     tokens_per_s = T / (ms * 1e-3)
     dom = "indexer" if t_idx >= t_sfa else "sparse_attn"
-    dom_ms = t_idx if dom == "indexer" else t_sfa
-    if case.max_q_per_req > 4 and case.idx_dtype in MFMA_PEAK_TFLOPS and dom == "indexer":
-        # many rows per request: the scoring GEMM dominates and is MFMA-bound
-        t_sc = time_steps(step.scores_only, args.steps, stream)
-        peak = MFMA_PEAK_TFLOPS[case.idx_dtype]
-        ach = ab["indexer_flops"] / (t_sc * 1e-3) / 1e12
-        roofline = {"kernel": "indexer_scores", "bound": "mfma", "achieved": ach, "peak": peak,
-                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": measured_traffic("indexer_scores", args.workload),
-                    "algorithmic_flops": ab["indexer_flops"], "kernel_ms": t_sc}
+    rows_route = case.max_q_per_req > 4 and T >= 1024 and case.idx_dtype in MFMA_PEAK_TFLOPS
+    kernels_ms = {}
+    if rows_route:
+        # the indexer call is two launches: the scoring GEMM, then per-row selection
+        kernels_ms["indexer_scores"] = time_steps(step.scores_only, args.steps, stream)
+    if dom == "indexer" and rows_route:
+        roofline = roofline_entry("indexer_scores", args.workload, ab["indexer"], ab["indexer_flops"],
+                                  kernels_ms["indexer_scores"], compute_peak(case.idx_dtype))
+    elif dom == "indexer":
+        roofline = roofline_entry("indexer_topk", args.workload, ab["indexer"], ab["indexer_flops"], t_idx,
+                                  compute_peak(case.idx_dtype))
     else:
-        kname = "indexer_topk" if dom == "indexer" else "sparse_attn"
-        achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
-        roofline = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kname, args.workload),
-                    "algorithmic_bytes": ab[dom], "kernel_ms": dom_ms}
+        roofline = roofline_entry("sparse_attn", args.workload, ab["sparse_attn"], ab["sparse_attn_flops"], t_sfa,
+                                  compute_peak(case.sfa_dtype))
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -357,7 +386,7 @@ def main():
                    "cache_replicas": R, "parallelism": "single GPU"},
         "hbm_gbs_step": ab["total"] / (ms * 1e-3) / 1e9,
         "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa},
+        "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa, **kernels_ms},
         "roofline": roofline,
         "kernel_source_hash": kernel_source_hash(),
     }
