@@ -42,6 +42,29 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------------------
+// Reductions over the four 16-lane groups of a wave (lane l, l ^ 16, l ^ 32,
+// l ^ 48: one column of an MFMA 16x16 result), with the VALU row permutes of
+// gfx950 instead of LDS shuffles.  v_permlane16_swap exchanges rows 1 and 3
+// of its first operand with rows 0 and 2 of its second, so swapping a value
+// with itself leaves the row pair (2k, 2k+1) in the two outputs, in that
+// order on every lane; v_permlane32_swap does the same for the two halves.
+// Every lane gets (x0 op x1) op (x2 op x3), with xg the value of group g.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// ---------------------------------------------------------------------------
 // Request lookup: the request that owns query row i (q_offsets is sorted).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int request_of_row(const int32_t* q_offsets, int batch, int i) {

@@ -10,8 +10,9 @@
 // reading keys straight from the paged K cache ("Day0 Inference Support and
 // Performance Optimization for New LLM Architectures", section III, 3.1).
 //
-// li_score: one workgroup = 4 waves = 4 cache pages (256 positions) of one
-// request and up to 4 of its query rows (the rows share one read of the keys).
+// li_score: one workgroup = 4 waves, stepping 4 cache pages (256 positions)
+// at a time through one request for up to 4 of its query rows (the rows share
+// one read of the keys).
 // It writes fp32 scores and a per-row histogram of the top 11 key bits (LDS,
 // then one global atomic per non-empty bin): the first radix level.
 //
@@ -48,10 +49,11 @@ struct LiParams {
 
 constexpr int kRowsPerBlock = 4;
 constexpr int kScoreThreads = 256;  // 4 waves, one page each
-constexpr int kChunk = 256;         // positions per workgroup
+constexpr int kChunk = 256;         // positions per workgroup and step
+constexpr int kScoreTargetWGs = 2048;  // workgroups the scoring grid aims for
 
 struct BlockRows {
-  int b, q0, nb, r0, nrows, first_pos, pos_max, c0;
+  int b, q0, nb, r0, nrows, first_pos, pos_max;
 };
 
 __device__ __forceinline__ bool block_rows(const LiParams& p, BlockRows& br) {
@@ -63,10 +65,12 @@ __device__ __forceinline__ bool block_rows(const LiParams& p, BlockRows& br) {
   br.nrows = min(kRowsPerBlock, br.nb - br.r0);
   br.first_pos = p.ctx_lens[br.b] - br.nb;          // position of the request's first query row
   br.pos_max = br.first_pos + br.r0 + br.nrows - 1;  // last position any row here may see
-  br.c0 = blockIdx.x * kChunk;
-  return br.c0 <= br.pos_max;
+  return (int)blockIdx.x * kChunk <= br.pos_max;
 }
 
+// Workgroup x of a (request, row group) takes chunks x, x + gridDim.x, ...:
+// the queries are staged once, the histogram collects every chunk, and each
+// wave loads its next page while it scores the current one.
 template <int DT, int D>
 __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
   BlockRows br;
@@ -86,23 +90,33 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
     }
   };
   const int wave = threadIdx.x >> 6;
+  const int step = gridDim.x * kChunk;
+  const int32_t* btrow = p.bt + (int64_t)br.b * p.bt_stride;
   if (DT == 0) {
-    const int pos = br.c0 + threadIdx.x;
-    if (pos <= br.pos_max) {
-      const int phys = p.bt[(int64_t)br.b * p.bt_stride + (pos >> 6)];
-      const float* krow = static_cast<const float*>(p.k) + ((int64_t)phys * kPage + (pos & 63)) * D;
-      score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, br.nrows, krow,
-                       [&](int r, float s) { emit(r, pos, s); });
+    for (int c0 = blockIdx.x * kChunk; c0 <= br.pos_max; c0 += step) {
+      const int pos = c0 + threadIdx.x;
+      if (pos <= br.pos_max) {
+        const float* krow = static_cast<const float*>(p.k) + ((int64_t)btrow[pos >> 6] * kPage + (pos & 63)) * D;
+        score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, br.nrows, krow,
+                         [&](int r, float s) { emit(r, pos, s); });
+      }
     }
   } else {
-    const int pg = (br.c0 >> 6) + wave;  // logical page handled by this wave
-    if (pg * kPage <= br.pos_max) {
-      const int phys = p.bt[(int64_t)br.b * p.bt_stride + pg];
-      const unsigned char* kpage =
-          static_cast<const unsigned char*>(p.k) + (int64_t)phys * kPage * D * IdxGeom<DT, D>::ES;
-      const float* ksp = DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr;
-      score_page_mfma<DT, D>(qs, wsm, p.Hpad, br.nrows, kpage, ksp,
-                             [&](int r, int slot, float s) { emit(r, pg * kPage + slot, s); });
+    const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
+    auto load = [&](KeyTiles<DT, D, 4>& t, int pg) {
+      const int phys = btrow[pg];
+      load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * IdxGeom<DT, D>::ES,
+                               DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, 0);
+    };
+    KeyTiles<DT, D, 4> cur, nxt;
+    int pg = blockIdx.x * (kChunk / kPage) + wave;  // logical page handled by this wave
+    const int pstep = step / kPage;
+    if (pg * kPage <= br.pos_max) load(nxt, pg);
+    for (; pg * kPage <= br.pos_max; pg += pstep) {
+      cur = nxt;
+      if ((pg + pstep) * kPage <= br.pos_max) load(nxt, pg + pstep);
+      score_key_tiles<DT, D, 4>(qs, wsm, p.Hpad, br.nrows, cur, 0,
+                                [&](int r, int slot, float s) { emit(r, pg * kPage + slot, s); });
     }
   }
   __syncthreads();
@@ -341,8 +355,11 @@ hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s) {
   if (dsa_indexer_rows_route(a)) {
     e = dsa_launch_indexer_prefill_scores(a, s);
   } else {
-    const dim3 grid((a.max_ctx_len + kChunk - 1) / kChunk, (a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock,
-                    a.batch);
+    // chunks per (request, row group), spread so the grid is a few workgroups per compute unit
+    const int chunks = (a.max_ctx_len + kChunk - 1) / kChunk;
+    const int groups = a.batch * ((a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int gx = std::max(1, std::min(chunks, (kScoreTargetWGs + groups - 1) / groups));
+    const dim3 grid(gx, (a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock, a.batch);
     const bool d64 = a.head_dim == 64;
     switch (a.dtype) {
       case 0: e = d64 ? launch_score<0, 64>(p, grid, s) : launch_score<0, 128>(p, grid, s); break;

@@ -74,28 +74,41 @@ __device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, cons
   }
 }
 
-// One wave scores NPT tiles of 16 positions of one page (slots slot0 ..
-// slot0 + 16 NPT - 1) for `nrows` staged rows.  emit(r, slot, score) runs on
-// lanes 0..15 for slots slot0 + pt * 16 + lane.
+// Key fragments of NPT tiles of 16 positions of one page (slots slot0 ..
+// slot0 + 16 NPT - 1), in the B-operand layout: kf[pt][ks] holds 8 elements
+// of position slot0 + pt*16 + l16 starting at dim ks*32 + 8g; kscale[pt] its
+// fp8 scale (1 otherwise).
+template <int DT, int D, int NPT>
+struct KeyTiles {
+  typename IdxGeom<DT, D>::frag_t kf[NPT][D / 32];
+  float kscale[NPT];
+};
+
+template <int DT, int D, int NPT>
+__device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const unsigned char* kpage,
+                                               const float* kscale_page, int slot0) {
+  using G = IdxGeom<DT, D>;
+  using frag_t = typename G::frag_t;
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      t.kf[pt][ks] =
+          *reinterpret_cast<const frag_t*>(kpage + ((slot0 + pt * 16 + l16) * D + ks * 32 + g * 8) * G::ES);
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt) t.kscale[pt] = (DT == 2) ? kscale_page[slot0 + pt * 16 + l16] : 1.f;
+}
+
+// One wave scores NPT loaded key tiles for `nrows` staged rows.  emit(r,
+// slot, score) runs on lanes 0..15 for slots slot0 + pt * 16 + lane.
 template <int DT, int D, int NPT, class Emit>
-__device__ __forceinline__ void score_tiles_mfma(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
-                                                 const unsigned char* kpage, const float* kscale_page,
-                                                 int slot0, Emit&& emit) {
+__device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
+                                                const KeyTiles<DT, D, NPT>& t, int slot0, Emit&& emit) {
   using G = IdxGeom<DT, D>;
   using frag_t = typename G::frag_t;
   constexpr int KS = D / 32;  // contraction steps
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  frag_t kf[NPT][KS];
-#pragma unroll
-  for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[pt][ks] =
-          *reinterpret_cast<const frag_t*>(kpage + ((slot0 + pt * 16 + l16) * D + ks * 32 + g * 8) * G::ES);
-  float kscale[NPT];
-#pragma unroll
-  for (int pt = 0; pt < NPT; ++pt) kscale[pt] = (DT == 2) ? kscale_page[slot0 + pt * 16 + l16] : 1.f;
-
   for (int r = 0; r < nrows; ++r) {
     float sacc[NPT];
 #pragma unroll
@@ -109,7 +122,7 @@ __device__ __forceinline__ void score_tiles_mfma(const unsigned char* qs, const 
       for (int ks = 0; ks < KS; ++ks) {
         const frag_t a = *reinterpret_cast<const frag_t*>(qrow + ks * 32 * G::ES);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, kf[pt][ks], acc[pt]);
+        for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, t.kf[pt][ks], acc[pt]);
       }
       // acc[pt][i] = logit of head ht*16 + 4g + i at slot slot0 + pt*16 + l16
       const float* wr = wsm + r * Hpad + ht * 16 + 4 * g;
@@ -120,12 +133,21 @@ __device__ __forceinline__ void score_tiles_mfma(const unsigned char* qs, const 
     }
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
-      float s = sacc[pt];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (g == 0) emit(r, slot0 + pt * 16 + l16, s * kscale[pt]);
+      const float s = group4_sum(sacc[pt]);
+      if (g == 0) emit(r, slot0 + pt * 16 + l16, s * t.kscale[pt]);
     }
   }
+}
+
+// One wave scores NPT tiles of 16 positions of one page (slots slot0 ..
+// slot0 + 16 NPT - 1) for `nrows` staged rows.
+template <int DT, int D, int NPT, class Emit>
+__device__ __forceinline__ void score_tiles_mfma(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
+                                                 const unsigned char* kpage, const float* kscale_page,
+                                                 int slot0, Emit&& emit) {
+  KeyTiles<DT, D, NPT> t;
+  load_key_tiles<DT, D, NPT>(t, kpage, kscale_page, slot0);
+  score_key_tiles<DT, D, NPT>(qs, wsm, Hpad, nrows, t, slot0, emit);
 }
 
 // One wave scores the 64 positions of one page.

@@ -11,9 +11,11 @@
 // synchronisation inside a kernel costs tens of microseconds per round (every
 // workgroup of a team re-reading one shared histogram), so this kernel never
 // waits:
-//   * every workgroup scores 256 consecutive positions of one request (one
-//     16-position MFMA tile per wave) for all of that request's query rows,
-//     and writes the scores as order-preserving 32-bit keys to the workspace;
+//   * the G workgroups of a request score its positions in chunks of 256
+//     (one 16-position MFMA tile per wave), chunk m, m + G, ... for workgroup
+//     m, for all of that request's query rows, and write the scores as
+//     order-preserving 32-bit keys to the workspace (G = all chunks for a
+//     single request; fewer, each looping, for a batch);
 //   * it then counts itself done on the request's arrival counter; the last
 //     workgroup to arrive loads each row's keys (at most 32768, 32 per
 //     thread) into registers and runs the whole radix select there
@@ -42,7 +44,7 @@ struct FusedParams {
   const float* k_scale;
   int K;
   int32_t* out;
-  int G;                // workgroups per request
+  int G;                // workgroups per request (each takes every G-th chunk)
   int row_cap;          // min(max_ctx_len, kFusedMaxRow)
   uint32_t* keys;       // [rows][key_stride] score keys
   int64_t key_stride;
@@ -73,7 +75,10 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const bool any_select = pos_max + 1 > K;   // the last row sees the most positions
 
-  // ---- scoring: one 16-position tile per wave --------------------------------
+  // ---- scoring: one 16-position tile per wave per chunk ----------------------
+  // Workgroup m of a request takes chunks m, m + G, m + 2G, ... (G is chosen
+  // so the whole batch gives a few workgroups per compute unit); the next
+  // chunk's key tile is loaded before the current one is scored.
   if (any_select && c0 <= pos_max) {
     unsigned char* qs = smem;
     float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * Gm::QSTRIDE);
@@ -82,23 +87,33 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
     auto emit = [&](int r, int pos, float s) {
       if (pos <= first_pos + r) p.keys[(int64_t)(q0 + r) * p.key_stride + pos] = score_key(s);
     };
-    const int t0 = c0 + wave * 16;
-    if (t0 <= pos_max) {
-      const int phys = p.bt[(int64_t)b * p.bt_stride + (t0 >> 6)];
-      if (DT == 0) {
-        const int lane = tid & 63;
+    const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
+    if (DT == 0) {
+      const int lane = tid & 63;
+      for (int c = c0; c <= pos_max; c += G * kFusedChunk) {
+        const int t0 = c + wave * 16;
         if (lane < 16 && t0 + lane <= pos_max) {
           const int pos = t0 + lane;
-          const float* krow = static_cast<const float*>(p.k) + ((int64_t)phys * kPage + (pos & 63)) * D;
+          const float* krow = static_cast<const float*>(p.k) + ((int64_t)btrow[pos >> 6] * kPage + (pos & 63)) * D;
           score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, nb, krow,
                            [&](int r, float s) { emit(r, pos, s); });
         }
-      } else {
-        const unsigned char* kpage =
-            static_cast<const unsigned char*>(p.k) + (int64_t)phys * kPage * D * Gm::ES;
-        const float* ksp = DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr;
-        score_tiles_mfma<DT, D, 1>(qs, wsm, p.Hpad, nb, kpage, ksp, t0 & 63,
-                                   [&](int r, int slot, float s) { emit(r, (t0 & ~63) + slot, s); });
+      }
+    } else {
+      const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
+      auto load = [&](KeyTiles<DT, D, 1>& t, int t0) {
+        const int phys = btrow[t0 >> 6];
+        load_key_tiles<DT, D, 1>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
+                                 DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, t0 & 63);
+      };
+      KeyTiles<DT, D, 1> cur, nxt;
+      int t0 = c0 + wave * 16;
+      if (t0 <= pos_max) load(nxt, t0);
+      for (; t0 <= pos_max; t0 += G * kFusedChunk) {
+        cur = nxt;
+        if (t0 + G * kFusedChunk <= pos_max) load(nxt, t0 + G * kFusedChunk);
+        score_key_tiles<DT, D, 1>(qs, wsm, p.Hpad, nb, cur, t0 & 63,
+                                  [&](int r, int slot, float s) { emit(r, (t0 & ~63) + slot, s); });
       }
     }
   }
@@ -161,9 +176,13 @@ using namespace dsa;
 
 namespace {
 
+// Workgroups a batch should fill: a few per compute unit.
+constexpr int kFusedTargetWGs = 512;
+
 template <int DT, int D>
 hipError_t launch_fused(FusedParams p, int batch, int max_ctx, hipStream_t s) {
-  p.G = (max_ctx + kFusedChunk - 1) / kFusedChunk;
+  const int chunks = (max_ctx + kFusedChunk - 1) / kFusedChunk;
+  p.G = std::max(1, std::min(chunks, (kFusedTargetWGs + batch - 1) / batch));
   p.row_cap = std::min(max_ctx, kFusedMaxRow);
   const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad), (size_t)kHistBins * 4);
   if (lds > 65536) {

@@ -55,6 +55,7 @@ constexpr int kRowBytes = kQkDim * 2;        // 1152 bytes of bf16
 constexpr int kRowStride = kRowBytes + 16;   // padded LDS row (bank spread)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescale = 8.f;  // log2 headroom before the running maximum is moved
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
@@ -98,22 +99,36 @@ __device__ __forceinline__ void stage_vblock(unsigned char* krow, unsigned char*
   }
 }
 
+// Exchange area between the two waves of a head tile (LDS, after the chunk
+// buffers and the row table): the chunk maxima of each half's 16 rows, the
+// probabilities each half feeds the other's P.V, and the final sums.
+struct SfaXchg {
+  float tmax[2][4][16];   // [half][head tile][head]
+  uint2 pv[2][4][64];     // [half][head tile][lane]: 4 bf16 probabilities
+  float lsum[2][4][16];   // [half][head tile][head]
+};
+
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
-  constexpr int NT = NW * 64;
+__global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
+  constexpr int NT = NW * 128;
   constexpr int kBlocks = 4 * (kVDim / 8);              // (lane group, 8-dim chunk) blocks per chunk
   constexpr int kRope = kSfaRows * ((kQkDim - kVDim) / 8);  // 16-byte rope pieces per chunk
   constexpr int BPT = (kBlocks + NT - 1) / NT;            // value blocks per thread
   constexpr int RPT = (kRope + NT - 1) / NT;               // rope pieces per thread
+  constexpr int kHalfDims = kVDim / 2;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* krow = smem;
   unsigned char* vt = smem + kKrowBytes;
-  int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + kVtBytes);  // pool row of each selected row, -1 = none
+  SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + kKrowBytes + kVtBytes);
+  int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + kVtBytes + sizeof(SfaXchg));  // pool row, -1 = none
 
   const int split = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
   const int b = request_of_row(p.q_offsets, p.batch, i);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-  const int h = hg * (16 * NW) + wave * 16 + l16;  // this lane's head column
+  // wave = (half, head tile): the tile's 16 heads; S for rows 16 half .. +16 of
+  // each chunk, P.V for value dims 256 half .. +256
+  const int ht = wave % NW, half = wave / NW;
+  const int h = hg * (16 * NW) + ht * 16 + l16;  // this lane's head column
   const int r_begin = split * p.rows_per_split;
   const int nrows = max(0, min(p.K, r_begin + p.rows_per_split) - r_begin);
   const uint16_t* kvg = static_cast<const uint16_t*>(p.kv);
@@ -135,9 +150,9 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
 #pragma unroll
     for (int s2 = 0; s2 < kQkDim / 32; ++s2) qf[s2] = *reinterpret_cast<const uint4*>(qrow + s2 * 32 + g * 8);
   }
-  f32x4 o[kVDim / 16];
+  f32x4 o[kHalfDims / 16];
 #pragma unroll
-  for (int et = 0; et < kVDim / 16; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int et = 0; et < kHalfDims / 16; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
   const float zscale = p.scale * kLog2e;
   __syncthreads();
@@ -158,7 +173,8 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
     }
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int it = tid + j * NT;
+      // rope pieces go to the threads past the value blocks first
+      const int it = (tid + kBlocks + j * NT) % (RPT * NT);
       const int row = it < kRope ? rowidx[c0 + (it >> 3)] : -1;
       ra[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + kVDim + (it & 7) * 8)
                        : make_uint4(0u, 0u, 0u, 0u);
@@ -172,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
     }
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int it = tid + j * NT;
+      const int it = (tid + kBlocks + j * NT) % (RPT * NT);
       if (it < kRope) *reinterpret_cast<uint4*>(krow + (it >> 3) * kRowStride + kVDim * 2 + (it & 7) * 16) = ra[j];
     }
   };
@@ -184,132 +200,150 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16(SfaParams p) {
     __syncthreads();
     if (c0 + kSfaRows < nrows) gather(c0 + kSfaRows);  // in flight during this chunk's math
 
-    // S^T tiles: s0[e] = S[head l16][row 4g+e], s1[e] = S[head l16][row 16+4g+e]
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* ka = krow + l16 * kRowStride + g * 16;
+    // S^T tile of this half: s[e] = S[head l16][row 16 half + 4g + e]; two
+    // accumulators (even and odd contraction steps) halve the dependent chain
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    const unsigned char* ka = krow + (16 * half + l16) * kRowStride + g * 16;
 #pragma unroll
-    for (int s2 = 0; s2 < kQkDim / 32; ++s2) {
+    for (int s2 = 0; s2 < kQkDim / 32; s2 += 2) {
       const uint4 a0 = *reinterpret_cast<const uint4*>(ka + s2 * 64);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(ka + 16 * kRowStride + s2 * 64);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[s2]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s2]), s1, 0, 0, 0);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(ka + (s2 + 1) * 64);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[s2]), sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s2 + 1]), sb, 0, 0, 0);
     }
-    float z[8];
+    sa += sb;
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = rowidx[c0 + 16 * half + 4 * g + e] >= 0 ? sa[e] * zscale : -INFINITY;
+    float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    tmax = group4_max(tmax);
+    if (g == 0) xc->tmax[half][ht][l16] = tmax;
+    __syncthreads();
+    tmax = fmaxf(tmax, xc->tmax[half ^ 1][ht][l16]);  // the chunk's maximum, the same in both halves
+    // Lazy rescaling: the reference maximum m only moves when some head's
+    // chunk maximum exceeds it by more than 2^kRescale (the exponentials stay
+    // <= 2^kRescale otherwise, well inside fp32 and bf16), and then for the
+    // whole wave, so most chunks skip the pass over the accumulators.  Both
+    // halves take the same decision from the same values.
+    if (__ballot(tmax > m + kRescale)) {
+      const float mnew = fmaxf(m, tmax);
+      if (__ballot(m != -INFINITY)) {  // (all zero before the first rows)
+        const float alpha = exp2f(m - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int et = 0; et < kHalfDims / 16; ++et) o[et] *= alpha;
+      }
+      m = mnew;
+    }
+    float pr[4], psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      z[e] = rowidx[c0 + 4 * g + e] >= 0 ? s0[e] * zscale : -INFINITY;
-      z[4 + e] = rowidx[c0 + 16 + 4 * g + e] >= 0 ? s1[e] * zscale : -INFINITY;
+      pr[e] = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m);
+      psum += pr[e];
     }
-    float tmax = z[0];
+    lsum += group4_sum(psum);  // this half's rows only; the halves are added at the end
+    uint2 mine;
+    mine.x = pack_bf16x2(pr[0], pr[1]);
+    mine.y = pack_bf16x2(pr[2], pr[3]);
+    xc->pv[half][ht][lane] = mine;
+    __syncthreads();
+    const uint2 other = xc->pv[half ^ 1][ht][lane];
+    // B operand of O^T += V^T P^T in slot order: rows 4g + e (half 0), then 16 + 4g + e (half 1)
+    uint4 pf;
+    pf.x = half ? other.x : mine.x;
+    pf.y = half ? other.y : mine.y;
+    pf.z = half ? mine.x : other.x;
+    pf.w = half ? mine.y : other.y;
+    const unsigned char* vb = vt + (kHalfDims * half + l16) * kVtStride + g * 16;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    float pr[8], alpha = 1.f, psum = 0.f;
-    if (mnew == -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = 0.f;
-    } else {
-      alpha = exp2f(m - mnew);  // m = -inf gives 0
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pr[e] = exp2f(z[e] - mnew);
-        psum += pr[e];
-      }
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    lsum = lsum * alpha + psum;
-    m = mnew;
-
-    uint4 pf;  // B operand of O^T += V^T P^T, slot order
-    pf.x = pack_bf16x2(pr[0], pr[1]);
-    pf.y = pack_bf16x2(pr[2], pr[3]);
-    pf.z = pack_bf16x2(pr[4], pr[5]);
-    pf.w = pack_bf16x2(pr[6], pr[7]);
-    const unsigned char* vb = vt + l16 * kVtStride + g * 16;
-#pragma unroll
-    for (int et = 0; et < kVDim / 16; ++et) {
+    for (int et = 0; et < kHalfDims / 16; ++et) {
       const uint4 av = *reinterpret_cast<const uint4*>(vb + et * 16 * kVtStride);
-      o[et] *= alpha;
       o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pf), o[et], 0, 0, 0);
     }
   }
 
-  // o[et][e] = unnormalised output of head h at dim 16 et + 4 g + e
+  // both halves' row sums (the same m in both)
+  if (g == 0) xc->lsum[half][ht][l16] = lsum;
+  __syncthreads();
+  lsum = half ? xc->lsum[0][ht][l16] + lsum : lsum + xc->lsum[1][ht][l16];
+  // o[et][e] = unnormalised output of head h at dim 256 half + 16 et + 4 g + e
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const float lse_v = lsum > 0.f ? m * kLn2 + logf(lsum) : -INFINITY;
+  const int d0 = kHalfDims * half + 4 * g;
   if (p.n_split == 1) {
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)i * p.H + h) * kVDim + 4 * g;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)i * p.H + h) * kVDim + d0;
 #pragma unroll
-    for (int et = 0; et < kVDim / 16; ++et) {
+    for (int et = 0; et < kHalfDims / 16; ++et) {
       uint2 v;
       v.x = pack_bf16x2(o[et][0] * inv, o[et][1] * inv);
       v.y = pack_bf16x2(o[et][2] * inv, o[et][3] * inv);
       *reinterpret_cast<uint2*>(orow + et * 16) = v;
     }
-    if (p.lse && g == 0) p.lse[(int64_t)i * p.H + h] = lse_v;
+    if (p.lse && g == 0 && half == 0) p.lse[(int64_t)i * p.H + h] = lse_v;
   } else {
-    float* prow = p.part_o + (((int64_t)split * p.T + i) * p.H + h) * kVDim + 4 * g;
+    float* prow = p.part_o + (((int64_t)split * p.T + i) * p.H + h) * kVDim + d0;
 #pragma unroll
-    for (int et = 0; et < kVDim / 16; ++et)
+    for (int et = 0; et < kHalfDims / 16; ++et)
       *reinterpret_cast<f32x4*>(prow + et * 16) = o[et] * inv;
-    if (g == 0) p.part_lse[((int64_t)split * p.T + i) * p.H + h] = lse_v;
+    if (g == 0 && half == 0) p.part_lse[((int64_t)split * p.T + i) * p.H + h] = lse_v;
   }
 }
 
 // Merge split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
-// One 64-lane workgroup per (query row, head), 8 dims per lane; the split
-// loop keeps four splits' loads in flight.
+// One thread per (query row, head, 4 output dims), 128 threads per head, so
+// a decode row's merge is spread over the whole chip.  Splits are read 16 at
+// a time with all their loads in flight, folded in with a running maximum
+// (the sum is rescaled when the maximum grows), so the merge costs about one
+// memory round trip per 16 splits.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 16;
+
 template <bool BF16>
-__global__ __launch_bounds__(64) void sfa_combine(SfaParams p) {
-  const int64_t th = blockIdx.x;  // = i * H + h
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
+  const int64_t gt = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  const int64_t th = gt >> 7;            // = i * H + h
+  const int d0 = (int)(gt & 127) * 4;    // first of this thread's 4 dims
   const int64_t stride = (int64_t)p.T * p.H;
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.part_lse[s * stride + th]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (M != -INFINITY) {
-    const float* po = p.part_o + th * kVDim + lane * 8;
-    for (int s0 = 0; s0 < p.n_split; s0 += 4) {
-      float wgt[4];
-      float4 a[4], c[4];
+  if (th >= stride) return;
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* po = p.part_o + th * kVDim + d0;
+  for (int s0 = 0; s0 < p.n_split; s0 += kCombineBatch) {
+    float l[kCombineBatch];
+    float4 o[kCombineBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        const float l = s < p.n_split ? p.part_lse[s * stride + th] : -INFINITY;
-        wgt[j] = l == -INFINITY ? 0.f : expf(l - M);
-        if (s < p.n_split) {
-          a[j] = reinterpret_cast<const float4*>(po + s * stride * kVDim)[0];
-          c[j] = reinterpret_cast<const float4*>(po + s * stride * kVDim)[1];
-        } else {
-          a[j] = c[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        den += wgt[j];
-        acc[0] += wgt[j] * a[j].x; acc[1] += wgt[j] * a[j].y; acc[2] += wgt[j] * a[j].z; acc[3] += wgt[j] * a[j].w;
-        acc[4] += wgt[j] * c[j].x; acc[5] += wgt[j] * c[j].y; acc[6] += wgt[j] * c[j].z; acc[7] += wgt[j] * c[j].w;
-      }
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const int s = s0 + j;
+      l[j] = s < p.n_split ? p.part_lse[s * stride + th] : -INFINITY;
+      o[j] = s < p.n_split ? *reinterpret_cast<const float4*>(po + s * stride * kVDim) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float bm = l[0];
+#pragma unroll
+    for (int j = 1; j < kCombineBatch; ++j) bm = fmaxf(bm, l[j]);
+    if (bm == -INFINITY) continue;  // no selected rows in these splits
+    const float Mn = fmaxf(M, bm);
+    const float r = expf(M - Mn);   // M = -inf gives 0 (acc and den are 0 then)
+    den *= r;
+    acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const float wgt = l[j] == -INFINITY ? 0.f : expf(l[j] - Mn);
+      den += wgt;
+      acc.x += wgt * o[j].x; acc.y += wgt * o[j].y; acc.z += wgt * o[j].z; acc.w += wgt * o[j].w;
+    }
+    M = Mn;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   if (BF16) {
-    uint4 v;
-    v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-    v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + th * kVDim + lane * 8) = v;
+    uint2 v;
+    v.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    v.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + th * kVDim + d0) = v;
   } else {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + th * kVDim + lane * 8);
-    dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + th * kVDim + d0) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  if (p.lse && lane == 0) p.lse[th] = den > 0.f ? M + logf(den) : -INFINITY;
+  if (p.lse && d0 == 0) p.lse[th] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
 // fp32: one workgroup per (query row, head); logits of all selected rows in
@@ -399,7 +433,7 @@ static hipError_t launch_sfa(dim3 grid, size_t lds, hipStream_t s, const SfaPara
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(sfa_bf16<NW>, grid, dim3(NW * 64), lds, s, p);
+  hipLaunchKernelGGL(sfa_bf16<NW>, grid, dim3(NW * 128), lds, s, p);
   return hipGetLastError();
 }
 
@@ -432,7 +466,7 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
     if ((a.n_heads / 16) % c == 0) { nw = c; break; }
   dim3 grid(a.n_split, a.n_heads / (16 * nw), a.num_rows);
   hipError_t e0;
-  const size_t lds = (size_t)kKrowBytes + kVtBytes +
+  const size_t lds = (size_t)kKrowBytes + kVtBytes + sizeof(SfaXchg) +
                      (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
   switch (nw) {
     case 1: e0 = launch_sfa<1>(grid, lds, s, p); break;
@@ -443,6 +477,8 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(sfa_combine<true>, dim3(a.num_rows * a.n_heads), dim3(64), 0, s, p);
+  const int64_t threads = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
+  hipLaunchKernelGGL(sfa_combine<true>, dim3((unsigned)((threads + kCombineThreads - 1) / kCombineThreads)),
+                     dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
