@@ -44,6 +44,7 @@ dsa_status_t check_indexer(const dsa_paged_t* pg, const dsa_indexer_t* x) {
   if (x->n_heads > kMaxIdxHeads || x->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
   if (x->head_dim != 64 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (x->dtype == DSA_F32 && x->n_heads * x->head_dim > 4096) return DSA_ERR_UNSUPPORTED;
+  if ((int64_t)pg->max_ctx_len > (int64_t)dsa_seg_max_segments() * 8192) return DSA_ERR_UNSUPPORTED;
   if (x->dtype == DSA_F32 && (x->flags & DSA_INDEXER_SCORE_ROWS)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
@@ -66,7 +67,8 @@ dsa_status_t check_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) 
 // The first two regions are zero between calls.
 struct IndexerPlan {
   int64_t score_stride;
-  size_t ctrl_off, hist_off, scores_off, total;
+  int cand_cap;
+  size_t ctrl_off, hist_off, scores_off, cand_key_off, cand_pos_off, total;
 };
 
 IndexerPlan plan_indexer(const dsa_paged_t* pg) {
@@ -76,7 +78,10 @@ IndexerPlan plan_indexer(const dsa_paged_t* pg) {
   p.ctrl_off = 0;
   p.hist_off = align_up(4 * (size_t)pg->batch);
   p.scores_off = p.hist_off + align_up(T * dsa::kHistStride * 4);
-  p.total = p.scores_off + align_up(T * p.score_stride * 4);
+  p.cand_cap = dsa_seg_cand_cap(pg->max_ctx_len);
+  p.cand_key_off = p.scores_off + align_up(T * p.score_stride * 4);
+  p.cand_pos_off = p.cand_key_off + align_up(T * (size_t)p.cand_cap * 4);
+  p.total = p.cand_pos_off + align_up(T * (size_t)p.cand_cap * 4);
   return p;
 }
 
@@ -148,6 +153,9 @@ DsaIndexerLaunch indexer_args(const dsa_paged_t* pg, const dsa_indexer_t* x, int
   a.hist = reinterpret_cast<uint32_t*>(ws + plan.hist_off);
   a.scores = reinterpret_cast<float*>(ws + plan.scores_off);
   a.score_stride = plan.score_stride;
+  a.cand_key = reinterpret_cast<uint32_t*>(ws + plan.cand_key_off);
+  a.cand_pos = reinterpret_cast<int32_t*>(ws + plan.cand_pos_off);
+  a.cand_cap = plan.cand_cap;
   a.force_two_pass = (x->flags & (DSA_INDEXER_TWO_PASS | DSA_INDEXER_SCORE_ROWS | DSA_INDEXER_SCORE_POSITIONS)) != 0;
   a.score_route = (x->flags & DSA_INDEXER_SCORE_ROWS) ? 1 : (x->flags & DSA_INDEXER_SCORE_POSITIONS) ? 2 : 0;
   return a;

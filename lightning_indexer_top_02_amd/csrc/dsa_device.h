@@ -98,6 +98,9 @@ struct DsaIndexerLaunch {
   uint32_t* hist;      // [rows][kHistStride] digit histograms (two-pass), zero between calls; null: scores only
   float* scores;       // [rows][score_stride] scores (two-pass) or score keys (fused)
   int64_t score_stride;
+  uint32_t* cand_key;  // [rows][cand_cap] selection candidates (two-pass)
+  int32_t* cand_pos;
+  int cand_cap;
   bool force_two_pass; // skip the fused kernel
   int score_route;     // two-pass scoring: 0 chosen by shape, 1 row-tiled, 2 position-tiled
 };
@@ -126,5 +129,8 @@ hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s)
 // Scoring kernel of the two-pass route alone (a.hist may be null: no histograms).
 hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_indexer_prefill_scores(const DsaIndexerLaunch& a, hipStream_t s);
+hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s);
+int dsa_seg_max_segments();
+int dsa_seg_cand_cap(int max_ctx_len);
 bool dsa_indexer_rows_route(const DsaIndexerLaunch& a);
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s);

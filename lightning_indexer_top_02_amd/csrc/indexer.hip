@@ -16,6 +16,8 @@
 // It writes fp32 scores and a per-row histogram of the top 11 key bits (LDS,
 // then one global atomic per non-empty bin): the first radix level.
 //
+// Selection runs over segments of each row (topk_seg.hip); li_topk takes the
+// rows whose boundary bin holds too many keys for that (heavy ties).
 // li_topk: one 1024-thread workgroup per query row.  It finds the bin holding
 // the K-th largest key, gathers that bin's keys into LDS, resolves the exact
 // K-th key with two more radix levels, then makes one ordered pass keeping
@@ -146,6 +148,7 @@ struct TopkParams {
   uint32_t* hist;
   int K;
   int32_t* out;
+  int only_flagged;  // handle only the rows the segment kernels left (flag word set)
 };
 
 struct TopkShared {
@@ -195,6 +198,7 @@ __global__ __launch_bounds__(kTopkThreads) void li_topk(TopkParams p) {
   const int K = p.K;
   int32_t* out = p.out + (int64_t)i * K;
   uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
+  if (p.only_flagged && (vis <= K || hrow[kHistStride - 1] != 1u)) return;
   if (vis <= K) {  // everything visible is kept
     for (int t = tid; t < K; t += kTopkThreads) out[t] = t < vis ? t : -1;
     for (int c = tid; c < kHistBins; c += kTopkThreads) hrow[c] = 0u;
@@ -374,6 +378,9 @@ hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s)
   hipError_t e = dsa_launch_indexer_scores(a, s);
   if (e != hipSuccess) return e;
 
+  e = dsa_launch_topk_segments(a, s);
+  if (e != hipSuccess) return e;
+  // rows whose boundary bin overflowed the candidate list
   TopkParams tp;
   tp.q_offsets = a.q_offsets;
   tp.ctx_lens = a.ctx_lens;
@@ -383,6 +390,7 @@ hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s)
   tp.hist = a.hist;
   tp.K = a.topk;
   tp.out = a.out_idx;
+  tp.only_flagged = 1;
   hipLaunchKernelGGL(li_topk, dim3(a.num_rows), dim3(kTopkThreads), 0, s, tp);
   return hipGetLastError();
 }

@@ -1,0 +1,349 @@
+// topk_seg.hip -- Top-K selection of the two-pass indexer route, parallel
+// over segments of each score row (gfx950).
+//
+// Selection keeps, per query row, the K highest scores among its visible
+// positions, ties to the lower position, written in ascending position order
+// ("Optimizing Inference for Hybrid Attention Architectures: From Operator
+// Fusion to Sequence Sharding", section "Breaking Down the Computational
+// Path of Hybrid Attention", item 1; the order is the "index rearrangement"
+// of "Optimizing Inference for Hybrid Attention LLMs: Practices for Fast
+// Adaptation", section 3, item 2).
+//
+// The scoring kernel has already left each row's histogram of the top 11
+// key bits in the workspace.  A row is then cut into segments of 8192
+// positions and handled by three kernels:
+//   li_seg_gather  (a workgroup per segment): finds the histogram bin that
+//                  holds the K-th key, counts the segment's keys above it and
+//                  appends the keys of that bin (low 21 bits and position) to
+//                  the row's candidate list;
+//   li_seg_resolve (a workgroup per row): two more radix digits over the
+//                  candidates give the K-th key exactly; if fewer keys equal
+//                  to it are kept than exist, a radix select over their
+//                  positions gives the last kept position; per-segment kept
+//                  counts become output offsets;
+//   li_seg_write   (a workgroup per segment): writes the kept positions of
+//                  its segment at its offset, in order.
+// A row whose boundary bin holds more keys than the candidate list can take
+// (heavy ties) is flagged and left to li_topk, which scans the row in one
+// workgroup.  The per-row state lives in the unused tail of the row's
+// histogram block; the histogram and the candidate counter are zero again
+// when the three kernels are done.
+#include <algorithm>
+
+#include "dsa_device.h"
+#include "radix_select.h"
+
+namespace dsa {
+
+constexpr int kSegLen = 8192;                     // positions per segment
+constexpr int kSegThreads = 256;
+constexpr int kSegPer = kSegLen / kSegThreads;    // positions per thread
+constexpr int kResolveThreads = 1024;
+// words of a row's histogram block (kHistStride) after the level-1 bins
+constexpr int kSegBase = kHistBins;               // per-segment counts, then offsets
+constexpr int kStateCount = kHistStride - 4;      // candidates appended (zero between calls)
+constexpr int kStateKth = kHistStride - 3;        // the K-th key
+constexpr int kStateLimit = kHistStride - 2;      // last kept position among keys equal to it
+constexpr int kStateFlags = kHistStride - 1;      // 1: row left to the one-workgroup path
+constexpr int kMaxSegs = kStateCount - kSegBase;  // longest row: kMaxSegs * kSegLen positions
+
+struct SegParams {
+  const int32_t* q_offsets;
+  const int32_t* ctx_lens;
+  int batch;
+  const float* scores;
+  int64_t score_stride;
+  uint32_t* hist;
+  int K;
+  int32_t* out;
+  uint32_t* cand_key;  // [rows][cand_cap] low 21 key bits
+  int32_t* cand_pos;   // [rows][cand_cap] positions
+  int cand_cap;
+};
+
+__device__ __forceinline__ int visible_of(const SegParams& p, int i) {
+  const int b = request_of_row(p.q_offsets, p.batch, i);
+  const int nb = p.q_offsets[b + 1] - p.q_offsets[b];
+  return p.ctx_lens[b] - nb + (i - p.q_offsets[b]) + 1;
+}
+
+// This thread's kSegPer consecutive keys of segment s (key 0 past vis).
+__device__ __forceinline__ void load_seg_keys(const float* row, int pos0, int vis, uint32_t (&key)[kSegPer]) {
+#pragma unroll
+  for (int c = 0; c < kSegPer; c += 4) {
+    const int t = pos0 + c;
+    if (t + 4 <= vis) {
+      const float4 v = *reinterpret_cast<const float4*>(row + t);
+      key[c] = score_key(v.x);
+      key[c + 1] = score_key(v.y);
+      key[c + 2] = score_key(v.z);
+      key[c + 3] = score_key(v.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[c + j] = t + j < vis ? score_key(row[t + j]) : 0u;
+    }
+  }
+}
+
+// Sum over the workgroup (result valid in every thread).
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int* wsum) {
+  int total;
+  block_excl_scan<NT>(v, total, wsum);
+  return total;
+}
+
+__global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
+  __shared__ __align__(16) int wsum[kSegThreads / 64];
+  __shared__ int sh[3];
+  const int i = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const int vis = visible_of(p, i);
+  const int s0 = seg * kSegLen;
+  if (vis <= p.K || s0 >= vis) return;
+  uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
+  if (tid < 64) {
+    int bin, above, total;
+    kth_bin_wave<32>(hrow, p.K, bin, above, total);
+    if (tid == 0) {
+      sh[0] = bin;
+      sh[1] = (int)hrow[bin];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin1 = (uint32_t)sh[0];
+  const bool gather = sh[1] <= p.cand_cap;
+  uint32_t key[kSegPer];
+  const int pos0 = s0 + tid * kSegPer;
+  load_seg_keys(p.scores + (int64_t)i * p.score_stride, pos0, vis, key);
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int c = 0; c < kSegPer; ++c) {
+    const uint32_t d = key[c] >> kLevelShift[0];
+    ngt += pos0 + c < vis && d > bin1;
+    neq += pos0 + c < vis && d == bin1;
+  }
+  // keys above the boundary bin: a count per segment
+  const int gt_total = block_sum<kSegThreads>(ngt, wsum);
+  if (tid == 0) hrow[kSegBase + seg] = (uint32_t)gt_total;
+  if (!gather) return;
+  // keys of the boundary bin: appended to the row's candidate list
+  int eq_total;
+  const int eq_before = block_excl_scan<kSegThreads>(neq, eq_total, wsum);
+  if (tid == 0) sh[2] = eq_total ? (int)atomicAdd(&hrow[kStateCount], (uint32_t)eq_total) : 0;
+  __syncthreads();
+  int o = sh[2] + eq_before;
+  uint32_t* ck = p.cand_key + (int64_t)i * p.cand_cap;
+  int32_t* cp = p.cand_pos + (int64_t)i * p.cand_cap;
+#pragma unroll
+  for (int c = 0; c < kSegPer; ++c) {
+    if (pos0 + c < vis && (key[c] >> kLevelShift[0]) == bin1) {
+      if (o < p.cand_cap) {
+        ck[o] = key[c] & 0x1fffffu;
+        cp[o] = pos0 + c;
+      }
+      ++o;
+    }
+  }
+}
+
+struct ResolveShared {
+  uint32_t bins[kHistBins];
+  uint32_t segc[kMaxSegs];
+  alignas(16) int wsum[kResolveThreads / 64];
+  int res[2];
+};
+
+// k-th largest bin of the histogram in sh.bins (wave 0), broadcast.
+template <int PER>
+__device__ __forceinline__ void resolve_kth(ResolveShared& sh, int k, int& bin, int& above) {
+  if (threadIdx.x < 64) {
+    int b, a, t;
+    kth_bin_wave<PER>(sh.bins, k, b, a, t);
+    if (threadIdx.x == 0) {
+      sh.res[0] = b;
+      sh.res[1] = a;
+    }
+  }
+  __syncthreads();
+  bin = sh.res[0];
+  above = sh.res[1];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
+  __shared__ ResolveShared sh;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int vis = visible_of(p, i);
+  uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
+  if (vis <= p.K) {  // every visible position is kept (written by li_seg_write)
+    for (int c = tid; c < kHistBins; c += kResolveThreads) hrow[c] = 0u;
+    return;
+  }
+  const int K = p.K;
+  for (int c = tid; c < kHistBins; c += kResolveThreads) sh.bins[c] = hrow[c];
+  __syncthreads();
+  int bin1, above;
+  resolve_kth<32>(sh, K, bin1, above);
+  const int ncand = (int)sh.bins[bin1];
+  __syncthreads();  // every thread has read it before the bins are reused
+  if (ncand > p.cand_cap) {  // left to li_topk, which also clears the histogram
+    if (tid == 0) hrow[kStateFlags] = 1u;
+    return;
+  }
+  int need = K - above;  // keys still needed from bin1 (>= 1)
+  const uint32_t* ck = p.cand_key + (int64_t)i * p.cand_cap;
+  const int32_t* cp = p.cand_pos + (int64_t)i * p.cand_cap;
+
+  // key bits 20..10, then 9..0, over the candidates
+  for (int c = tid; c < kHistBins; c += kResolveThreads) sh.bins[c] = 0u;
+  __syncthreads();
+  for (int c = tid; c < ncand; c += kResolveThreads) atomicAdd(&sh.bins[ck[c] >> 10], 1u);
+  __syncthreads();
+  int b2, a2;
+  resolve_kth<32>(sh, need, b2, a2);
+  need -= a2;
+  for (int c = tid; c < kHistBins; c += kResolveThreads) sh.bins[c] = 0u;
+  __syncthreads();
+  for (int c = tid; c < ncand; c += kResolveThreads) {
+    const uint32_t k = ck[c];
+    if ((k >> 10) == (uint32_t)b2) atomicAdd(&sh.bins[k & 1023u], 1u);
+  }
+  __syncthreads();
+  int b3, a3;
+  resolve_kth<16>(sh, need, b3, a3);
+  need -= a3;
+  const uint32_t low = ((uint32_t)b2 << 10) | (uint32_t)b3;  // low 21 bits of the K-th key
+  const int n_eq = (int)sh.bins[b3];
+  __syncthreads();
+
+  // the last kept position among the n_eq keys equal to the K-th: the
+  // need-th smallest of their positions, i.e. the (n_eq - need + 1)-th
+  // largest, found 11, 11 and 9 bits at a time
+  int limit = 0x7fffffff;
+  if (need < n_eq) {
+    int kk = n_eq - need + 1;
+    uint32_t pprefix = 0u;
+    for (int level = 0; level < 3; ++level) {
+      const int shift = level == 0 ? 20 : (level == 1 ? 9 : 0);
+      const int pshift = level == 1 ? 20 : 9;  // the previous level's shift
+      const uint32_t mask = level == 2 ? 511u : 2047u;
+      for (int c = tid; c < kHistBins; c += kResolveThreads) sh.bins[c] = 0u;
+      __syncthreads();
+      for (int c = tid; c < ncand; c += kResolveThreads) {
+        const uint32_t pos = (uint32_t)cp[c];
+        const bool match = ck[c] == low && (level == 0 || (pos >> pshift) == pprefix);
+        if (match) atomicAdd(&sh.bins[(pos >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      int pb, pa;
+      if (level == 2) resolve_kth<8>(sh, kk, pb, pa);
+      else resolve_kth<32>(sh, kk, pb, pa);
+      kk -= pa;
+      pprefix = level == 0 ? (uint32_t)pb : ((pprefix << (level == 1 ? 11 : 9)) | (uint32_t)pb);
+    }
+    limit = (int)pprefix;
+  }
+
+  // kept candidates per segment, plus the keys above bin1: output offsets
+  const int nseg = (vis + kSegLen - 1) / kSegLen;
+  for (int s = tid; s < nseg; s += kResolveThreads) sh.segc[s] = hrow[kSegBase + s];
+  __syncthreads();
+  for (int c = tid; c < ncand; c += kResolveThreads) {
+    const uint32_t k = ck[c];
+    const int pos = cp[c];
+    if (k > low || (k == low && pos <= limit)) atomicAdd(&sh.segc[pos / kSegLen], 1u);
+  }
+  __syncthreads();
+  constexpr int kPerT = (kMaxSegs + kResolveThreads - 1) / kResolveThreads;
+  int v[kPerT], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPerT; ++j) {
+    const int s = tid * kPerT + j;
+    v[j] = s < nseg ? (int)sh.segc[s] : 0;
+    sum += v[j];
+  }
+  int total;
+  int run = block_excl_scan<kResolveThreads>(sum, total, sh.wsum);
+#pragma unroll
+  for (int j = 0; j < kPerT; ++j) {
+    const int s = tid * kPerT + j;
+    if (s < nseg) hrow[kSegBase + s] = (uint32_t)run;
+    run += v[j];
+  }
+  if (tid == 0) {
+    hrow[kStateKth] = ((uint32_t)bin1 << 21) | low;
+    hrow[kStateLimit] = (uint32_t)limit;
+    hrow[kStateFlags] = 0u;
+    hrow[kStateCount] = 0u;
+  }
+  for (int c = tid; c < kHistBins; c += kResolveThreads) hrow[c] = 0u;
+}
+
+__global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
+  __shared__ __align__(16) int wsum[kSegThreads / 64];
+  const int i = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const int vis = visible_of(p, i);
+  const int K = p.K;
+  int32_t* out = p.out + (int64_t)i * K;
+  if (vis <= K) {
+    for (int t = seg * kSegLen + tid; t < min(K, (seg + 1) * kSegLen); t += kSegThreads) out[t] = t < vis ? t : -1;
+    return;
+  }
+  const uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
+  const int s0 = seg * kSegLen;
+  if (s0 >= vis || (hrow[kStateFlags] & 1u)) return;
+  const uint32_t kth = hrow[kStateKth];
+  const int limit = (int)hrow[kStateLimit];
+  const int off = (int)hrow[kSegBase + seg];
+  uint32_t key[kSegPer];
+  const int pos0 = s0 + tid * kSegPer;
+  load_seg_keys(p.scores + (int64_t)i * p.score_stride, pos0, vis, key);
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < kSegPer; ++c) {
+    const bool valid = pos0 + c < vis;
+    n += valid && (key[c] > kth || (key[c] == kth && pos0 + c <= limit));
+  }
+  int total;
+  int o = off + block_excl_scan<kSegThreads>(n, total, wsum);
+#pragma unroll
+  for (int c = 0; c < kSegPer; ++c) {
+    const bool valid = pos0 + c < vis;
+    if (valid && (key[c] > kth || (key[c] == kth && pos0 + c <= limit))) {
+      if (o < K) out[o] = pos0 + c;
+      ++o;
+    }
+  }
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+int dsa_seg_max_segments() { return kMaxSegs; }
+int dsa_seg_cand_cap(int max_ctx_len) { return std::min((max_ctx_len + 255) / 256 * 256, 8192); }
+
+// The three segment kernels; rows they leave flagged go to li_topk (run by the caller).
+hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s) {
+  SegParams p;
+  p.q_offsets = a.q_offsets;
+  p.ctx_lens = a.ctx_lens;
+  p.batch = a.batch;
+  p.scores = a.scores;
+  p.score_stride = a.score_stride;
+  p.hist = a.hist;
+  p.K = a.topk;
+  p.out = a.out_idx;
+  p.cand_key = a.cand_key;
+  p.cand_pos = a.cand_pos;
+  p.cand_cap = a.cand_cap;
+  const int nseg = (a.max_ctx_len + kSegLen - 1) / kSegLen;
+  const dim3 grid(nseg, a.num_rows);
+  hipLaunchKernelGGL(li_seg_gather, grid, dim3(kSegThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(li_seg_resolve, dim3(a.num_rows), dim3(kResolveThreads), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(li_seg_write, grid, dim3(kSegThreads), 0, s, p);
+  return hipGetLastError();
+}
