@@ -49,6 +49,7 @@ struct FusedParams {
   uint32_t* keys;       // [rows][key_stride] score keys
   int64_t key_stride;
   uint32_t* counters;   // [batch] arrival counters, zero between calls
+  uint32_t* hist;       // [rows][kHistStride]: top-11-bit key histogram at offset 0, zero between calls
 };
 
 constexpr int kFusedThreads = 1024;
@@ -82,10 +83,17 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
   if (any_select && c0 <= pos_max) {
     unsigned char* qs = smem;
     float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * Gm::QSTRIDE);
+    // this workgroup's share of each row's histogram of the top 11 key bits
+    uint32_t* lh = reinterpret_cast<uint32_t*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad));
     stage_queries<DT, D, kFusedThreads>(qs, wsm, p.q, p.q_scale, p.w, q0, nb, p.H, p.Hpad);
+    for (int c = tid; c < nb * kHistBins; c += kFusedThreads) lh[c] = 0u;
     __syncthreads();
     auto emit = [&](int r, int pos, float s) {
-      if (pos <= first_pos + r) p.keys[(int64_t)(q0 + r) * p.key_stride + pos] = score_key(s);
+      if (pos <= first_pos + r) {
+        const uint32_t k = score_key(s);
+        p.keys[(int64_t)(q0 + r) * p.key_stride + pos] = k;
+        atomicAdd(&lh[r * kHistBins + (k >> kLevelShift[0])], 1u);
+      }
     };
     const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
     if (DT == 0) {
@@ -114,6 +122,20 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
         if (t0 + G * kFusedChunk <= pos_max) load(nxt, t0 + G * kFusedChunk);
         score_key_tiles<DT, D, 1>(qs, wsm, p.Hpad, nb, cur, t0 & 63,
                                   [&](int r, int slot, float s) { emit(r, (t0 & ~63) + slot, s); });
+      }
+    }
+  }
+
+  // ---- the histograms go to the workspace (their sums are complete when the
+  // last workgroup arrives)
+  if (any_select && c0 <= pos_max) {
+    const uint32_t* lh = reinterpret_cast<const uint32_t*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad));
+    __syncthreads();
+    for (int c = tid; c < nb * kHistBins; c += kFusedThreads) {
+      const uint32_t v = lh[c];
+      if (v) {
+        const int r = c / kHistBins;
+        atomicAdd(&p.hist[(int64_t)(q0 + r) * kHistStride + (c - r * kHistBins)], v);
       }
     }
   }
@@ -166,7 +188,26 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
         for (int j = 0; j < 4; ++j) key[c + j] = t + j < vis ? grow[t + j] : 0u;
       }
     }
-    select_in_regs<kFusedThreads, kKeysPerThread>(key, vis, K, out, hist, wsum, res);
+    // the first digit of the K-th key from the row's whole histogram
+    uint32_t* grow_hist = p.hist + (int64_t)(q0 + r) * kHistStride;
+    if (wave == 0) {
+      int bin, above, total;
+      kth_bin_wave<32>(grow_hist, K, bin, above, total);
+      if ((tid & 63) == 0) {
+        res[0] = bin;
+        res[1] = above;
+      }
+    }
+    __syncthreads();
+    const uint32_t bin1 = (uint32_t)res[0];
+    const int need = K - res[1];
+    __syncthreads();
+    select_from_level1<kFusedThreads, kKeysPerThread>(key, vis, K, bin1, need, out, hist, wsum, res);
+  }
+  // leave every row's histogram zero for the next call
+  for (int c = tid; c < nb * kHistBins; c += kFusedThreads) {
+    const int r = c / kHistBins;
+    p.hist[(int64_t)(q0 + r) * kHistStride + (c - r * kHistBins)] = 0u;
   }
 }
 
@@ -184,7 +225,8 @@ hipError_t launch_fused(FusedParams p, int batch, int max_ctx, hipStream_t s) {
   const int chunks = (max_ctx + kFusedChunk - 1) / kFusedChunk;
   p.G = std::max(1, std::min(chunks, (kFusedTargetWGs + batch - 1) / batch));
   p.row_cap = std::min(max_ctx, kFusedMaxRow);
-  const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad), (size_t)kHistBins * 4);
+  const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4,
+                              (size_t)kHistBins * 4);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(li_fused<DT, D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -223,6 +265,7 @@ hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s) {
   p.keys = reinterpret_cast<uint32_t*>(a.scores);
   p.key_stride = a.score_stride;
   p.counters = a.counters;
+  p.hist = a.hist;
   const bool d64 = a.head_dim == 64;
   switch (a.dtype) {
     case 0: return d64 ? launch_fused<0, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<0, 128>(p, a.batch, a.max_ctx_len, s);

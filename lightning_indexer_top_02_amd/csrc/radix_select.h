@@ -243,4 +243,65 @@ __device__ void select_in_regs(const uint32_t (&key)[KPT], int vis, int K, int32
   __syncthreads();
 }
 
+
+// select_in_regs when the first digit is already known: bin1 is the top-11-
+// bit bin of the K-th key (from a histogram of the whole row built
+// elsewhere) and `need` the number of keys still to take from it.  Runs the
+// two remaining digits and the ordered output over the register-resident keys.
+template <int NT, int KPT>
+__device__ void select_from_level1(const uint32_t (&key)[KPT], int vis, int K, uint32_t bin1, int need,
+                                   int32_t* out, uint32_t* hist, int* wsum, int* res) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = tid * KPT;
+  const bool active = base < vis;
+  uint32_t prefix = bin1;
+  for (int level = 1; level < 3; ++level) {
+    const int nbins = kLevelBins[level], shift = kLevelShift[level], pshift = kLevelShift[level - 1];
+    for (int c = tid; c < nbins; c += NT) hist[c] = 0u;
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < KPT; ++c) {
+        const uint32_t k = key[c];
+        if ((k >> pshift) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int bin, above;
+      kth_bin_wave(hist, nbins, need, bin, above);
+      if (lane == 0) {
+        res[0] = bin;
+        res[1] = above;
+      }
+    }
+    __syncthreads();
+    prefix = (prefix << (level == 1 ? 11 : 10)) | (uint32_t)res[0];
+    need -= res[1];
+    __syncthreads();
+  }
+  const uint32_t kth = prefix;
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    ngt += key[c] > kth;
+    neq += key[c] == kth;
+  }
+  int packed_total;
+  const int packed_before = block_excl_scan<NT>(ngt | (neq << 16), packed_total, wsum);
+  const int gt_before = packed_before & 0xffff, eq_before = packed_before >> 16;
+  int o = gt_before + min(eq_before, need);
+  int er = eq_before;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool e = key[c] == kth;
+    if (key[c] > kth || (e && er < need)) {
+      if (o < K) out[o] = base + c;
+      ++o;
+    }
+    er += e;
+  }
+  __syncthreads();
+}
+
 }  // namespace dsa
