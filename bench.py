@@ -229,6 +229,33 @@ def time_steps(fn, steps, stream):
     return start.elapsed_time(end) / steps
 
 
+def time_graph(fn, steps, warmup):
+    """Capture `steps` calls of fn into one HIP graph (on a side stream) and
+    time one replay with events on the replay stream; the host then issues a
+    single launch for the whole timed region."""
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        for s in range(max(1, warmup)):
+            fn(s, cs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        for s in range(steps):
+            fn(s, cs)
+    torch.cuda.synchronize()
+    g.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end) / steps
+
+
 def stage_breakdown(step: Step, steps, stream):
     """Average duration of each stage, from HIP events around each call."""
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -318,6 +345,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to exceed 512 MB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from the host instead of replaying a captured HIP graph")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="steps of the chunked-prefill scoring measurement (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -348,8 +377,15 @@ def main():
     for s in range(args.warmup):
         step.fused(s, stream)
     torch.cuda.synchronize()
-    ms = time_steps(step.fused, args.steps, stream)
-    t_idx, t_sfa = stage_breakdown(step, args.steps, stream)
+    ms_eager = time_steps(step.fused, args.steps, stream)
+    if args.eager:
+        ms = ms_eager
+        t_idx, t_sfa = stage_breakdown(step, args.steps, stream)
+    else:
+        # the whole timed region as one HIP graph: no host launch gaps between steps
+        ms = time_graph(step.fused, args.steps, args.warmup)
+        t_idx = time_graph(step.indexer, args.steps, 1)
+        t_sfa = time_graph(step.sparse_attn, args.steps, 1)
 
     T = case.num_tokens
     tokens_per_s = T / (ms * 1e-3)
@@ -383,7 +419,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["desc"].format(batch=case.batch), "name": case.name, "batch": case.batch,
                    "query_tokens": T, "max_context": case.max_ctx, "topk": case.topk,
-                   "cache_replicas": R, "parallelism": "single GPU"},
+                   "cache_replicas": R, "parallelism": "single GPU",
+                   "launch": "eager" if args.eager else "hip_graph"},
+        "ms_per_step_eager": ms_eager,
         "hbm_gbs_step": ab["total"] / (ms * 1e-3) / 1e9,
         "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa, **kernels_ms},

@@ -6,6 +6,9 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "../../include/dsa.h"
 #include "dsa_device.h"
@@ -196,6 +199,21 @@ __global__ void zero_words(uint32_t* x, size_t n) {
 }
 
 }  // namespace
+
+hipError_t dsa_allow_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> done;  // (device, kernel) -> bytes allowed
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = done.find({dev, kernel});
+  if (it != done.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[{dev, kernel}] = bytes;
+  return e;
+}
 
 extern "C" {
 

@@ -124,6 +124,11 @@ struct DsaSfaLaunch {
   float* part_lse;     // [n_split][rows][H]
 };
 
+// Let `kernel` use `bytes` of dynamic LDS on the current device (above the
+// default 64 KB).  The attribute is set once per (device, kernel, size) and
+// remembered, so launches do not pay for it every call.
+hipError_t dsa_allow_lds(const void* kernel, size_t bytes);
+
 hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s);
 // Scoring kernel of the two-pass route alone (a.hist may be null: no histograms).

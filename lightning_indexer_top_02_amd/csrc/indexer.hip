@@ -321,9 +321,8 @@ using namespace dsa;
 
 template <typename Kern, typename P>
 static hipError_t launch_dyn(Kern kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const P& p) {
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(kernel), lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kernel, grid, block, lds, s, p);

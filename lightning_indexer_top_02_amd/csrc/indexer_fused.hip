@@ -227,9 +227,8 @@ hipError_t launch_fused(FusedParams p, int batch, int max_ctx, hipStream_t s) {
   p.row_cap = std::min(max_ctx, kFusedMaxRow);
   const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4,
                               (size_t)kHistBins * 4);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(li_fused<DT, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(li_fused<DT, D>), lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((li_fused<DT, D>), dim3(p.G * batch), dim3(kFusedThreads), lds, s, p);

@@ -281,9 +281,8 @@ template <int DT, int D>
 static hipError_t launch_prefill(const PrefillParams& p, dim3 grid, hipStream_t s) {
   using Gm = IdxGeom<DT, D>;
   const size_t lds = (size_t)kPfTile * (D * Gm::ES + 16) + kPfTile * 4 + (size_t)kPfRows * kHistBins * 4;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(li_prefill<DT, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(li_prefill<DT, D>), lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((li_prefill<DT, D>), grid, dim3(kPfThreads), lds, s, p);

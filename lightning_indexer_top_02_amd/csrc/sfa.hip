@@ -428,9 +428,8 @@ using namespace dsa;
 
 template <int NW>
 static hipError_t launch_sfa(dim3 grid, size_t lds, hipStream_t s, const SfaParams& p) {
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sfa_bf16<NW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(sfa_bf16<NW>), lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(sfa_bf16<NW>, grid, dim3(NW * 128), lds, s, p);

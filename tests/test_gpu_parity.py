@@ -253,3 +253,44 @@ def test_workspace_reuse_across_calls(name):
     assert int(ctrl.abs().sum()) == 0, "arrival counters not back to zero"
     for flags in parity.indexer_routes(case).values():
         assert torch.equal(first, parity.gpu_indexer_topk(case, flags=flags))
+
+
+# --- HIP graph capture: replays equal the eager result ------------------------
+@pytest.mark.parametrize("flags", [0, 1], ids=["default_route", "two_pass"])
+def test_graph_replays_match_eager(flags):
+    """The step captured into a HIP graph and replayed several times, with
+    eager calls on the same workspace and synchronisations between replays,
+    gives the eager result every time (the workspace counters, histograms and
+    candidate lists must be back to zero after each call)."""
+    from lightning_indexer_top_02_amd import dsa
+    case = parity.to_device(inputs.make_case(name="graph", seed=95, ctx_lens=[32768, 9000, 20000], n_q=[1, 1, 4],
+                                             idx_dtype="bf16", n_heads_idx=64, head_dim_idx=128, topk=2048,
+                                             sfa_dtype="bf16", n_heads_sfa=64))
+    paged, idx = parity.paged_of(case), parity.indexer_of(case, flags=flags)
+    out, lse = parity.sfa_tensors(case)
+    sfa = dsa.make_sfa(case.q_sfa, case.kv_cache, out, case.scale, case.sfa_dtype, lse=lse)
+    ws = dsa.new_workspace(dsa.fused_decode_workspace_size(paged, idx, sfa), "cuda")
+    ii = torch.empty((case.num_tokens, case.topk), dtype=torch.int32, device="cuda")
+    dsa.fused_decode(paged, idx, sfa, topk_idx=ii, workspace=ws)
+    torch.cuda.synchronize()
+    ref = (ii.clone(), out.clone(), lse.clone())
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        dsa.fused_decode(paged, idx, sfa, topk_idx=ii, workspace=ws, stream=cs)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        ii.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ii, ref[0]), f"replay {rep}: indices differ"
+        assert torch.equal(out, ref[1]) and torch.equal(lse, ref[2]), f"replay {rep}: outputs differ"
+        dsa.fused_decode(paged, idx, sfa, topk_idx=ii, workspace=ws)  # eager call between replays
+        torch.cuda.synchronize()
+        assert torch.equal(ii, ref[0]), f"eager call after replay {rep} differs"
+    ctrl = ws[: 4 * case.batch].view(torch.int32)
+    assert int(ctrl.abs().sum()) == 0, "arrival counters not back to zero"
