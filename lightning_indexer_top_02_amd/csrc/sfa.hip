@@ -9,22 +9,23 @@
 // row per position (512 latent + 64 rope) used whole as the key and by its
 // first 512 entries as the value.
 //
-// bf16 kernel (sfa_bf16): a workgroup owns one query row, 16 heads per wave,
-// and one contiguous slice of the row's index list.  The slice's pool rows
-// are looked up through the block table once; the rows are then gathered in
+// bf16 kernel (sfa_bf16): a workgroup owns one query row, 16 NW heads, and
+// one contiguous slice of the row's index list.  The slice's pool rows are
+// looked up through the block table once; the rows are then gathered in
 // chunks of 32 into LDS (the scattered reads become 1152-byte row reads,
 // "aggregating random small reads", "Optimizing Inference for Hybrid
 // Attention LLMs: Practices for Fast Adaptation", section 3, item 2), the
 // next chunk's loads in flight in registers while the current chunk is
-// computed (the same page's "overlapping gather and compute"), and every wave
-// of the workgroup reuses them.  Per chunk and wave, MFMA computes S^T = K Q^T (32 rows x 16 heads,
-// contraction 576), an online softmax updates the running max and sum per
-// head, and MFMA accumulates O^T += V^T P^T (512 dims x 16 heads,
-// contraction over the 32 rows).  Computing the transposed products keeps
-// each head's softmax state in one lane column, so the probabilities feed the
-// second product straight from the first's accumulators.  When the index list
-// is split over several workgroups (small batches), each writes a normalised
-// partial output and its log-sum-exp, and sfa_combine merges them.
+// computed (the same page's "overlapping gather and compute").  Each 16-head
+// tile has two waves: per chunk, each computes S^T = K Q^T for half of the
+// chunk's rows (16 rows x 16 heads, contraction 576) with MFMA, the two
+// exchange their row maxima and probabilities through LDS, and each
+// accumulates O^T += V^T P^T for half of the value dims (256 dims x 16
+// heads, contraction over the 32 rows).  Computing the transposed products
+// keeps each head's softmax state in one lane column, so the probabilities
+// feed the second product straight from the first's accumulators.  When the
+// index list is split over several workgroups (small batches), each writes a
+// normalised partial output and its log-sum-exp, and sfa_combine merges them.
 //
 // fp32 kernel (sfa_f32): VALU, one workgroup per (query row, head).
 #include <algorithm>
@@ -61,42 +62,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
-// LDS layout of one staged chunk of 32 rows:
-//   krow: row-major copy of the whole 576-wide rows (the A operand of
-//         S^T = K Q^T), 1168-byte rows;
-//   vt:   the value part (dims 0..511) transposed, vt[dim][slot], 80 bytes
-//         per dim, where slot 8g + e holds row r(g, e) = 4g + e (e < 4) or
-//         16 + 4g + e - 4 (e >= 4): the rows a lane of lane group g holds in
-//         its S^T accumulators, so the probabilities are the B operand of
-//         O^T += V^T P^T as they come out of the softmax and the A operand
-//         is one 16-byte read.
-//   The paddings make the MFMA operand reads and the staging writes
-//   conflict-free (or at most 2-way) across the 64 LDS banks.
-constexpr int kVtStride = 80;
+// LDS layout of one staged chunk of 32 rows: krow, a row-major copy of the
+// whole 576-wide rows, 1168-byte rows (the padding spreads the MFMA operand
+// reads over the LDS banks).  It is the A operand of S^T = K Q^T as it is,
+// and gives the A operand of O^T += V^T P^T through gfx950's transposing LDS
+// read (ds_read_b64_tr_b16): within each 16-lane group, lane L supplies 4
+// consecutive 16-bit elements and lane i receives the i-th column of the 4 x
+// 16 block the group supplied.  A lane of lane group g needs V^T[dim][slots
+// 8g .. 8g + 7], where slot 8g + e holds row 4g + e (e < 4, the first half's
+// S rows) or 16 + 4g + e - 4 (e >= 4, the second half's): the rows whose
+// probabilities the lane holds, so P^T is the B operand as it comes out of
+// the softmax.  Two transposing reads of rows 4g .. 4g + 3 and 16 + 4g ..
+// 16 + 4g + 3 give those 8 elements.
 constexpr int kKrowBytes = kSfaRows * kRowStride;
-constexpr int kVtBytes = kVDim * kVtStride;
+constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chunk
 
-__device__ __forceinline__ int slot_row(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Stage the 8 rows of lane group g (slot order), 8 value dims starting at
-// dim 8 dc, into krow and (transposed) into vt.
-__device__ __forceinline__ void stage_vblock(unsigned char* krow, unsigned char* vt, int g, int dc,
-                                             const uint4 (&a)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    *reinterpret_cast<uint4*>(krow + slot_row(g, e) * kRowStride + dc * 16) = a[e];
-  // 8 x 8 transpose of 16-bit elements: t[j] holds dim 8 dc + j of the 8 rows
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int k = j >> 1;
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    uint4 t;
-    t.x = __builtin_amdgcn_perm(((const uint32_t*)&a[1])[k], ((const uint32_t*)&a[0])[k], sel);
-    t.y = __builtin_amdgcn_perm(((const uint32_t*)&a[3])[k], ((const uint32_t*)&a[2])[k], sel);
-    t.z = __builtin_amdgcn_perm(((const uint32_t*)&a[5])[k], ((const uint32_t*)&a[4])[k], sel);
-    t.w = __builtin_amdgcn_perm(((const uint32_t*)&a[7])[k], ((const uint32_t*)&a[6])[k], sel);
-    *reinterpret_cast<uint4*>(vt + (dc * 8 + j) * kVtStride + g * 16) = t;
-  }
+// 4 value elements of rows r0 .. r0 + 3 at one dim, per lane: see above.
+__device__ __forceinline__ uint2 read_vt4(const unsigned char* krow, int r0, int d0) {
+  const int L = threadIdx.x & 15;
+  const unsigned char* a = krow + (r0 + (L >> 2)) * kRowStride + (d0 + 4 * (L & 3)) * 2;
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) unsigned char*)a);
+  return __builtin_bit_cast(uint2, v);
 }
 
 // Exchange area between the two waves of a head tile (LDS, after the chunk
@@ -111,16 +101,12 @@ struct SfaXchg {
 template <int NW>
 __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   constexpr int NT = NW * 128;
-  constexpr int kBlocks = 4 * (kVDim / 8);              // (lane group, 8-dim chunk) blocks per chunk
-  constexpr int kRope = kSfaRows * ((kQkDim - kVDim) / 8);  // 16-byte rope pieces per chunk
-  constexpr int BPT = (kBlocks + NT - 1) / NT;            // value blocks per thread
-  constexpr int RPT = (kRope + NT - 1) / NT;               // rope pieces per thread
+  constexpr int PPT = (kPieces + NT - 1) / NT;  // 16-byte pieces per thread per chunk
   constexpr int kHalfDims = kVDim / 2;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* krow = smem;
-  unsigned char* vt = smem + kKrowBytes;
-  SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + kKrowBytes + kVtBytes);
-  int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + kVtBytes + sizeof(SfaXchg));  // pool row, -1 = none
+  SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + kKrowBytes);
+  int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + sizeof(SfaXchg));  // pool row, -1 = none
 
   const int split = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
   const int b = request_of_row(p.q_offsets, p.batch, i);
@@ -157,39 +143,24 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   const float zscale = p.scale * kLog2e;
   __syncthreads();
 
-  // gather of one chunk into registers: BPT value blocks and RPT rope pieces
-  uint4 va[BPT][8], ra[RPT];
+  // gather of one chunk into registers: PPT 16-byte pieces of its rows
+  uint4 va[PPT];
   auto gather = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int blk = tid + j * NT;
-      const int gg = blk & 3, dc = blk >> 2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = blk < kBlocks ? rowidx[c0 + slot_row(gg, e)] : -1;
-        va[j][e] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + dc * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      // rope pieces go to the threads past the value blocks first
-      const int it = (tid + kBlocks + j * NT) % (RPT * NT);
-      const int row = it < kRope ? rowidx[c0 + (it >> 3)] : -1;
-      ra[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + kVDim + (it & 7) * 8)
+    for (int j = 0; j < PPT; ++j) {
+      const int it = tid + j * NT;
+      const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
+      const int row = it < kPieces ? rowidx[c0 + r] : -1;
+      va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + part * 8)
                        : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int blk = tid + j * NT;
-      if (blk < kBlocks) stage_vblock(krow, vt, blk & 3, blk >> 2, va[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int it = (tid + kBlocks + j * NT) % (RPT * NT);
-      if (it < kRope) *reinterpret_cast<uint4*>(krow + (it >> 3) * kRowStride + kVDim * 2 + (it & 7) * 16) = ra[j];
+    for (int j = 0; j < PPT; ++j) {
+      const int it = tid + j * NT;
+      const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
+      if (it < kPieces) *reinterpret_cast<uint4*>(krow + r * kRowStride + part * 16) = va[j];
     }
   };
 
@@ -254,10 +225,11 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
     pf.y = half ? other.y : mine.y;
     pf.z = half ? mine.x : other.x;
     pf.w = half ? mine.y : other.y;
-    const unsigned char* vb = vt + (kHalfDims * half + l16) * kVtStride + g * 16;
 #pragma unroll
     for (int et = 0; et < kHalfDims / 16; ++et) {
-      const uint4 av = *reinterpret_cast<const uint4*>(vb + et * 16 * kVtStride);
+      const int d0 = kHalfDims * half + 16 * et;
+      const uint2 lo = read_vt4(krow, 4 * g, d0), hi = read_vt4(krow, 16 + 4 * g, d0);
+      const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
       o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pf), o[et], 0, 0, 0);
     }
   }
@@ -465,7 +437,7 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
     if ((a.n_heads / 16) % c == 0) { nw = c; break; }
   dim3 grid(a.n_split, a.n_heads / (16 * nw), a.num_rows);
   hipError_t e0;
-  const size_t lds = (size_t)kKrowBytes + kVtBytes + sizeof(SfaXchg) +
+  const size_t lds = (size_t)kKrowBytes + sizeof(SfaXchg) +
                      (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
   switch (nw) {
     case 1: e0 = launch_sfa<1>(grid, lds, s, p); break;
