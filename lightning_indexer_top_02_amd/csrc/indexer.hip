@@ -11,8 +11,8 @@
 // Performance Optimization for New LLM Architectures", section III, 3.1).
 //
 // li_score: one workgroup = 4 waves, stepping 4 cache pages (256 positions)
-// at a time through one request for up to 4 of its query rows (the rows share
-// one read of the keys).
+// at a time through its share of all requests' chunks, for up to 4 query rows
+// of the request at hand (the rows share one read of the keys).
 // It writes fp32 scores and a per-row histogram of the top 11 key bits (LDS,
 // then one global atomic per non-empty bin): the first radix level.
 //
@@ -54,82 +54,159 @@ constexpr int kScoreThreads = 256;  // 4 waves, one page each
 constexpr int kChunk = 256;         // positions per workgroup and step
 constexpr int kScoreTargetWGs = 2048;  // workgroups the scoring grid aims for
 
-struct BlockRows {
-  int b, q0, nb, r0, nrows, first_pos, pos_max;
-};
-
-__device__ __forceinline__ bool block_rows(const LiParams& p, BlockRows& br) {
-  br.b = blockIdx.z;
-  br.q0 = p.q_offsets[br.b];
-  br.nb = p.q_offsets[br.b + 1] - br.q0;
-  br.r0 = blockIdx.y * kRowsPerBlock;
-  if (br.r0 >= br.nb) return false;
-  br.nrows = min(kRowsPerBlock, br.nb - br.r0);
-  br.first_pos = p.ctx_lens[br.b] - br.nb;          // position of the request's first query row
-  br.pos_max = br.first_pos + br.r0 + br.nrows - 1;  // last position any row here may see
-  return (int)blockIdx.x * kChunk <= br.pos_max;
+// Chunks of 256 positions row group y (rows 4y .. 4y + 3) of request b
+// covers: every position its last row sees, 0 when the request has no such
+// rows.
+__device__ __forceinline__ int chunks_of(const LiParams& p, int b, int r0) {
+  const int nb = p.q_offsets[b + 1] - p.q_offsets[b];
+  if (r0 >= nb) return 0;
+  const int pos_max = p.ctx_lens[b] - nb + r0 + min(kRowsPerBlock, nb - r0) - 1;
+  return pos_max / kChunk + 1;
 }
 
-// Workgroup x of a (request, row group) takes chunks x, x + gridDim.x, ...:
-// the queries are staged once, the histogram collects every chunk, and each
-// wave loads its next page while it scores the current one.
+// The chunks of all requests (for one row group) form one list, split evenly
+// over the workgroups of the grid's x dimension, so requests of different
+// lengths cost their share and no workgroup waits on a long one.  A
+// workgroup walks its range in order: it stages the request's query rows
+// (and starts its histogram) when it enters a request, flushes the histogram
+// when it leaves, and each wave loads its page of the next chunk while it
+// scores the current one.
 template <int DT, int D>
 __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
-  BlockRows br;
-  if (!block_rows(p, br)) return;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ __align__(16) int wsum[kScoreThreads / 64];
+  __shared__ int s_b0, s_base0;
+  using Gm = IdxGeom<DT, D>;
   unsigned char* qs = smem;
-  float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * IdxGeom<DT, D>::QSTRIDE);
+  float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * Gm::QSTRIDE);
   uint32_t* hl = reinterpret_cast<uint32_t*>(wsm + p.rcap * p.Hpad);
-  stage_queries<DT, D, kScoreThreads>(qs, wsm, p.q, p.q_scale, p.w, br.q0 + br.r0, br.nrows, p.H, p.Hpad);
-  for (int c = threadIdx.x; c < br.nrows * kHistBins; c += kScoreThreads) hl[c] = 0u;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int r0 = blockIdx.y * kRowsPerBlock;
+
+  // total chunks and the request holding this workgroup's first one
+  const int per = (p.batch + kScoreThreads - 1) / kScoreThreads;
+  const int blo = min(p.batch, tid * per), bhi = min(p.batch, blo + per);
+  int local = 0;
+  for (int b = blo; b < bhi; ++b) local += chunks_of(p, b, r0);
+  int total;
+  const int excl = block_excl_scan<kScoreThreads>(local, total, wsum);
+  const int f0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
+  const int f1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+  if (f0 >= f1) return;
+  if (excl <= f0 && f0 < excl + local) {
+    int b = blo, acc = excl;
+    while (acc + chunks_of(p, b, r0) <= f0) acc += chunks_of(p, b++, r0);
+    s_b0 = b;
+    s_base0 = acc;
+  }
   __syncthreads();
 
-  auto emit = [&](int r, int pos, float s) {
-    if (pos <= br.first_pos + br.r0 + r) {
-      p.scores[(int64_t)(br.q0 + br.r0 + r) * p.score_stride + pos] = s;
-      atomicAdd(&hl[r * kHistBins + (score_key(s) >> kLevelShift[0])], 1u);
+  // the request being scored
+  int b = s_b0, base = s_base0, q0 = 0, nb = 0, nrows = 0, first_pos = 0, pos_max = -1, nchunks = 0;
+  auto enter = [&](int nbq) {
+    b = nbq;
+    q0 = p.q_offsets[b];
+    nb = p.q_offsets[b + 1] - q0;
+    nrows = min(kRowsPerBlock, nb - r0);
+    first_pos = p.ctx_lens[b] - nb;
+    pos_max = first_pos + r0 + nrows - 1;
+    nchunks = pos_max / kChunk + 1;
+    stage_queries<DT, D, kScoreThreads>(qs, wsm, p.q, p.q_scale, p.w, q0 + r0, nrows, p.H, p.Hpad);
+    for (int c = tid; c < nrows * kHistBins; c += kScoreThreads) hl[c] = 0u;
+    __syncthreads();
+  };
+  auto leave = [&]() {
+    __syncthreads();
+    if (!p.hist) return;
+    for (int c = tid; c < nrows * kHistBins; c += kScoreThreads) {
+      const uint32_t v = hl[c];
+      if (v) {
+        const int r = c / kHistBins, bin = c - r * kHistBins;
+        atomicAdd(&p.hist[(int64_t)(q0 + r0 + r) * kHistStride + bin], v);
+      }
     }
   };
-  const int wave = threadIdx.x >> 6;
-  const int step = gridDim.x * kChunk;
-  const int32_t* btrow = p.bt + (int64_t)br.b * p.bt_stride;
+  auto emit = [&](int r, int pos, float sc) {
+    if (pos <= first_pos + r0 + r) {
+      p.scores[(int64_t)(q0 + r0 + r) * p.score_stride + pos] = sc;
+      atomicAdd(&hl[r * kHistBins + (score_key(sc) >> kLevelShift[0])], 1u);
+    }
+  };
+  enter(b);
+
   if (DT == 0) {
-    for (int c0 = blockIdx.x * kChunk; c0 <= br.pos_max; c0 += step) {
-      const int pos = c0 + threadIdx.x;
-      if (pos <= br.pos_max) {
+    for (int f = f0; f < f1; ++f) {
+      if (f - base >= nchunks) {
+        leave();
+        base += nchunks;
+        int nbq = b + 1;
+        while (chunks_of(p, nbq, r0) == 0) ++nbq;
+        enter(nbq);
+      }
+      const int pos = (f - base) * kChunk + tid;
+      if (pos <= pos_max) {
+        const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
         const float* krow = static_cast<const float*>(p.k) + ((int64_t)btrow[pos >> 6] * kPage + (pos & 63)) * D;
-        score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, br.nrows, krow,
-                         [&](int r, float s) { emit(r, pos, s); });
+        score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, nrows, krow,
+                         [&](int r, float sc) { emit(r, pos, sc); });
       }
     }
   } else {
     const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
-    auto load = [&](KeyTiles<DT, D, 4>& t, int pg) {
-      const int phys = btrow[pg];
-      load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * IdxGeom<DT, D>::ES,
+    // look-ahead cursor: the request, its first flat chunk and page limit of chunk fn
+    int nb_req = b, nb_base = base, nb_chunks = nchunks, nb_posmax = pos_max;
+    auto advance_to = [&](int fn) {
+      while (fn - nb_base >= nb_chunks) {
+        nb_base += nb_chunks;
+        ++nb_req;
+        nb_chunks = chunks_of(p, nb_req, r0);
+        if (nb_chunks) {
+          const int nbb = p.q_offsets[nb_req + 1] - p.q_offsets[nb_req];
+          nb_posmax = p.ctx_lens[nb_req] - nbb + r0 + min(kRowsPerBlock, nbb - r0) - 1;
+        }
+      }
+    };
+    auto load = [&](KeyTiles<DT, D, 4>& t, int req, int pg) {
+      const int phys = p.bt[(int64_t)req * p.bt_stride + pg];
+      load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
                                DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, 0);
     };
     KeyTiles<DT, D, 4> cur, nxt;
-    int pg = blockIdx.x * (kChunk / kPage) + wave;  // logical page handled by this wave
-    const int pstep = step / kPage;
-    if (pg * kPage <= br.pos_max) load(nxt, pg);
-    for (; pg * kPage <= br.pos_max; pg += pstep) {
+    bool have = false;
+    {
+      const int pg = (f0 - base) * (kChunk / kPage) + wave;
+      if (pg * kPage <= pos_max) {
+        load(nxt, b, pg);
+        have = true;
+      }
+    }
+    for (int f = f0; f < f1; ++f) {
+      if (f - base >= nchunks) {
+        leave();
+        base += nchunks;
+        int nbq = b + 1;
+        while (chunks_of(p, nbq, r0) == 0) ++nbq;
+        enter(nbq);
+      }
       cur = nxt;
-      if ((pg + pstep) * kPage <= br.pos_max) load(nxt, pg + pstep);
-      score_key_tiles<DT, D, 4>(qs, wsm, p.Hpad, br.nrows, cur, 0,
-                                [&](int r, int slot, float s) { emit(r, pg * kPage + slot, s); });
+      const bool have_cur = have;
+      have = false;
+      if (f + 1 < f1) {  // next chunk's page for this wave
+        advance_to(f + 1);
+        const int pgn = (f + 1 - nb_base) * (kChunk / kPage) + wave;
+        if (pgn * kPage <= nb_posmax) {
+          load(nxt, nb_req, pgn);
+          have = true;
+        }
+      }
+      if (have_cur) {
+        const int pg = (f - base) * (kChunk / kPage) + wave;
+        score_key_tiles<DT, D, 4>(qs, wsm, p.Hpad, nrows, cur, 0,
+                                  [&](int r, int slot, float sc) { emit(r, pg * kPage + slot, sc); });
+      }
     }
   }
-  __syncthreads();
-  if (!p.hist) return;
-  for (int c = threadIdx.x; c < br.nrows * kHistBins; c += kScoreThreads) {
-    const uint32_t v = hl[c];
-    if (v) {
-      const int r = c / kHistBins, bin = c - r * kHistBins;
-      atomicAdd(&p.hist[(int64_t)(br.q0 + br.r0 + r) * kHistStride + bin], v);
-    }
-  }
+  leave();
 }
 
 // ---------------------------------------------------------------------------
@@ -358,11 +435,10 @@ hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s) {
   if (dsa_indexer_rows_route(a)) {
     e = dsa_launch_indexer_prefill_scores(a, s);
   } else {
-    // chunks per (request, row group), spread so the grid is a few workgroups per compute unit
+    // one list of chunks over all requests per row group, split over gx workgroups
     const int chunks = (a.max_ctx_len + kChunk - 1) / kChunk;
-    const int groups = a.batch * ((a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock);
-    const int gx = std::max(1, std::min(chunks, (kScoreTargetWGs + groups - 1) / groups));
-    const dim3 grid(gx, (a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock, a.batch);
+    const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(kScoreTargetWGs, (int64_t)chunks * a.batch));
+    const dim3 grid(gx, (a.max_q_per_req + kRowsPerBlock - 1) / kRowsPerBlock);
     const bool d64 = a.head_dim == 64;
     switch (a.dtype) {
       case 0: e = d64 ? launch_score<0, 64>(p, grid, s) : launch_score<0, 128>(p, grid, s); break;

@@ -37,6 +37,16 @@ struct IdxGeom {
   static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);   // bytes per element
   static constexpr int QSTRIDE = DT == 0 ? D * 4 : D * ES + 16;  // LDS bytes per (row, head)
   using frag_t = typename std::conditional<DT == 1, uint4, uint2>::type;
+  // Byte offset, within a row of D elements, of the 8 elements lane group g
+  // feeds to the MFMA at contraction step ks.  Any assignment of the row's
+  // elements to (ks, g) gives the same dot product as long as the query and
+  // key fragments use the same one; bf16 takes elements 32 ks + 8g .. + 8.
+  // fp8 pairs the steps so that lane group g reads 16 contiguous bytes at
+  // 16g + 64 j (steps 2j and 2j + 1): each load instruction then covers 64
+  // contiguous bytes of every key row instead of 32.
+  static __host__ __device__ constexpr int frag_byte(int ks, int g) {
+    return DT == 2 ? 16 * g + 8 * (ks & 1) + 64 * (ks >> 1) : (32 * ks + 8 * g) * ES;
+  }
 };
 
 // LDS bytes for the staged queries and weights of `rows` rows.
@@ -76,7 +86,7 @@ __device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, cons
 
 // Key fragments of NPT tiles of 16 positions of one page (slots slot0 ..
 // slot0 + 16 NPT - 1), in the B-operand layout: kf[pt][ks] holds 8 elements
-// of position slot0 + pt*16 + l16 starting at dim ks*32 + 8g; kscale[pt] its
+// of position slot0 + pt*16 + l16 at byte frag_byte(ks, g); kscale[pt] its
 // fp8 scale (1 otherwise).
 template <int DT, int D, int NPT>
 struct KeyTiles {
@@ -95,7 +105,7 @@ __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const un
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
       t.kf[pt][ks] =
-          *reinterpret_cast<const frag_t*>(kpage + ((slot0 + pt * 16 + l16) * D + ks * 32 + g * 8) * G::ES);
+          *reinterpret_cast<const frag_t*>(kpage + (slot0 + pt * 16 + l16) * D * G::ES + G::frag_byte(ks, g));
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt) t.kscale[pt] = (DT == 2) ? kscale_page[slot0 + pt * 16 + l16] : 1.f;
 }
@@ -117,10 +127,10 @@ __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const f
       f32x4 acc[NPT];
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const unsigned char* qrow = qs + (r * Hpad + ht * 16 + l16) * G::QSTRIDE + g * 8 * G::ES;
+      const unsigned char* qrow = qs + (r * Hpad + ht * 16 + l16) * G::QSTRIDE;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const frag_t a = *reinterpret_cast<const frag_t*>(qrow + ks * 32 * G::ES);
+        const frag_t a = *reinterpret_cast<const frag_t*>(qrow + G::frag_byte(ks, g));
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, t.kf[pt][ks], acc[pt]);
       }

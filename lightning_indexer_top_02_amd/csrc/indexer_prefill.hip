@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
 
   for (int c = tid; c < kPfRows * kHistBins; c += kPfThreads) lhist[c] = 0u;
 
-  // this wave's query row as A fragments: qf[mt][ks] = q[row][mt*16 + l16][ks*32 + g*8 ..]
+  // this wave's query row as A fragments: qf[mt][ks] = q[row][mt*16 + l16] at byte frag_byte(ks, g)
   frag_t qf[MT][KS];
   float wl[MT][4];  // weights of heads mt*16 + 4g + i (times the q scale for fp8)
   {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         frag_t v{};
         if (row_ok && h < p.H)
-          v = *reinterpret_cast<const frag_t*>(qg + ((int64_t)row * p.H + h) * (D * ES) + (ks * 32 + g * 8) * ES);
+          v = *reinterpret_cast<const frag_t*>(qg + ((int64_t)row * p.H + h) * (D * ES) + Gm::frag_byte(ks, g));
         qf[mt][ks] = v;
       }
 #pragma unroll
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   auto load_b = [&](frag_t (&bf)[2], int sub, int ks) {
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
-      bf[pt] = *reinterpret_cast<const frag_t*>(ktile + (sub * kPfSub + pt * 16 + l16) * KROW + (ks * 32 + g * 8) * ES);
+      bf[pt] = *reinterpret_cast<const frag_t*>(ktile + (sub * kPfSub + pt * 16 + l16) * KROW + Gm::frag_byte(ks, g));
   };
   // The MFMAs of one sub-tile.  bf holds its first step's fragments on entry;
   // every step loads the next step's fragments (the next sub-tile's first one
