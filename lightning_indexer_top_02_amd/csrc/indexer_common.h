@@ -19,9 +19,15 @@
 
 namespace dsa {
 
-// ReLU that lets NaN through (NaN < 0 is false), so a stray read of poisoned
-// cache data shows up in the result instead of vanishing.
-__device__ __forceinline__ float relu_keep_nan(float v) { return v < 0.f ? 0.f : v; }
+// ReLU as one integer max on the bit pattern: a set sign bit reads as a
+// negative int32, so every negative value (and -0) becomes +0, while positive
+// values, +Inf and NaNs with a clear sign bit (the kind arithmetic on a NaN
+// produces) pass unchanged, so a stray read of poisoned cache data still shows
+// up in the result.  A compare and select would cost two vector instructions
+// per logit, and the ReLU runs once for every (head, position) pair.
+__device__ __forceinline__ float relu_keep_nan(float v) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, v), 0));
+}
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
