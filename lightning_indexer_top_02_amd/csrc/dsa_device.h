@@ -118,6 +118,7 @@ struct DsaSfaLaunch {
   int topk;
   void* out;
   float* lse;
+  int nw;  // 16-head tiles per bf16 workgroup (1..4, dividing n_heads / 16)
   // split-KV partials (used when n_split > 1)
   int n_split, rows_per_split;
   float* part_o;       // [n_split][rows][H][512]

@@ -435,10 +435,8 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL(sfa_f32, dim3(a.n_heads, a.num_rows), dim3(kF32Threads), 0, s, p);
     return hipGetLastError();
   }
-  // waves per workgroup: 16 heads each, up to 4, dividing the head count
-  int nw = 1;
-  for (int c = 4; c > 1; --c)
-    if ((a.n_heads / 16) % c == 0) { nw = c; break; }
+  const int nw = a.nw;  // 16-head tiles per workgroup
+  if (nw < 1 || nw > 4 || (a.n_heads / 16) % nw != 0) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.n_heads / (16 * nw), a.num_rows);
   hipError_t e0;
   const size_t lds = (size_t)kKrowBytes + sizeof(SfaXchg) +
