@@ -59,6 +59,14 @@ constexpr int kFusedMaxRow = 32768;            // longest row the selection hold
 constexpr int kFusedMaxRows = 4;               // query rows per request
 constexpr int kKeysPerThread = kFusedMaxRow / kFusedThreads;
 
+// Slot of position p in a row's key array.  The selecting workgroup holds
+// positions 32 t .. 32 t + 31 in thread t and loads them 4 at a time; keys
+// are stored in groups of 4 positions, transposed so that group j of every
+// thread is contiguous: slot = j S + 4 t + p % 4 with j = (p % 32) / 4,
+// t = p / 32 and S = 4 ceil(row_cap / 32).  Those loads are then coalesced
+// (a wave reads 1 KB in one piece instead of 64 lines 128 bytes apart).
+__device__ __forceinline__ int key_slot(int p, int S) { return ((p & 31) >> 2) * S + ((p >> 5) << 2) + (p & 3); }
+
 template <int DT, int D>
 __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
   using Gm = IdxGeom<DT, D>;
@@ -75,6 +83,7 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
   const int c0 = m * kFusedChunk;
   const int tid = threadIdx.x, wave = tid >> 6;
   const bool any_select = pos_max + 1 > K;   // the last row sees the most positions
+  const int key_group_stride = 4 * ((p.row_cap + 31) / 32);
 
   // ---- scoring: one 16-position tile per wave per chunk ----------------------
   // Workgroup m of a request takes chunks m, m + G, m + 2G, ... (G is chosen
@@ -85,38 +94,39 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
     float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * Gm::QSTRIDE);
     // this workgroup's share of each row's histogram of the top 11 key bits
     uint32_t* lh = reinterpret_cast<uint32_t*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad));
+    const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
+    const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
+    auto load = [&](KeyTiles<DT, D, 1>& t, int t0) {
+      const int phys = btrow[t0 >> 6];
+      load_key_tiles<DT, D, 1>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
+                               DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, t0 & 63);
+    };
+    KeyTiles<DT, D, 1> cur, nxt;
+    int t0 = c0 + wave * 16;
+    // the first key tile is in flight while the queries are staged
+    if (DT != 0 && t0 <= pos_max) load(nxt, t0);
     stage_queries<DT, D, kFusedThreads>(qs, wsm, p.q, p.q_scale, p.w, q0, nb, p.H, p.Hpad);
     for (int c = tid; c < nb * kHistBins; c += kFusedThreads) lh[c] = 0u;
     __syncthreads();
     auto emit = [&](int r, int pos, float s) {
       if (pos <= first_pos + r) {
         const uint32_t k = score_key(s);
-        p.keys[(int64_t)(q0 + r) * p.key_stride + pos] = k;
+        p.keys[(int64_t)(q0 + r) * p.key_stride + key_slot(pos, key_group_stride)] = k;
         atomicAdd(&lh[r * kHistBins + (k >> kLevelShift[0])], 1u);
       }
     };
-    const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
     if (DT == 0) {
       const int lane = tid & 63;
       for (int c = c0; c <= pos_max; c += G * kFusedChunk) {
-        const int t0 = c + wave * 16;
-        if (lane < 16 && t0 + lane <= pos_max) {
-          const int pos = t0 + lane;
+        const int tp = c + wave * 16;
+        if (lane < 16 && tp + lane <= pos_max) {
+          const int pos = tp + lane;
           const float* krow = static_cast<const float*>(p.k) + ((int64_t)btrow[pos >> 6] * kPage + (pos & 63)) * D;
           score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, nb, krow,
                            [&](int r, float s) { emit(r, pos, s); });
         }
       }
     } else {
-      const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
-      auto load = [&](KeyTiles<DT, D, 1>& t, int t0) {
-        const int phys = btrow[t0 >> 6];
-        load_key_tiles<DT, D, 1>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
-                                 DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, t0 & 63);
-      };
-      KeyTiles<DT, D, 1> cur, nxt;
-      int t0 = c0 + wave * 16;
-      if (t0 <= pos_max) load(nxt, t0);
       for (; t0 <= pos_max; t0 += G * kFusedChunk) {
         cur = nxt;
         if (t0 + G * kFusedChunk <= pos_max) load(nxt, t0 + G * kFusedChunk);
@@ -170,29 +180,35 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
       for (int t = tid; t < K; t += kFusedThreads) out[t] = t < vis ? t : -1;
       continue;
     }
-    // the row's keys in registers, kKeysPerThread consecutive ones per thread
+    // the row's histogram (two bins per thread, on their way to LDS) and its
+    // keys in registers (kKeysPerThread consecutive ones per thread), all
+    // loads in flight together
+    static_assert(kHistBins == 2 * kFusedThreads, "two histogram bins per thread");
+    const uint2 hbins = reinterpret_cast<const uint2*>(p.hist + (int64_t)(q0 + r) * kHistStride)[tid];
     const uint32_t* grow = p.keys + (int64_t)(q0 + r) * p.key_stride;
     const int pos0 = tid * kKeysPerThread;
     uint32_t key[kKeysPerThread];
 #pragma unroll
     for (int c = 0; c < kKeysPerThread; c += 4) {
       const int t = pos0 + c;
+      const uint32_t* g4 = grow + key_slot(t, key_group_stride);
       if (t + 4 <= vis) {
-        const uint4 v = *reinterpret_cast<const uint4*>(grow + t);
+        const uint4 v = *reinterpret_cast<const uint4*>(g4);
         key[c] = v.x;
         key[c + 1] = v.y;
         key[c + 2] = v.z;
         key[c + 3] = v.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) key[c + j] = t + j < vis ? grow[t + j] : 0u;
+        for (int j = 0; j < 4; ++j) key[c + j] = t + j < vis ? g4[j] : 0u;
       }
     }
     // the first digit of the K-th key from the row's whole histogram
-    uint32_t* grow_hist = p.hist + (int64_t)(q0 + r) * kHistStride;
+    reinterpret_cast<uint2*>(hist)[tid] = hbins;
+    __syncthreads();
     if (wave == 0) {
       int bin, above, total;
-      kth_bin_wave<32>(grow_hist, K, bin, above, total);
+      kth_bin_wave<kHistBins / 64>(hist, K, bin, above, total);
       if ((tid & 63) == 0) {
         res[0] = bin;
         res[1] = above;

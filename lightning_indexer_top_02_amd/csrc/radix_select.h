@@ -21,11 +21,9 @@ constexpr int kLevelBins[3] = {2048, 2048, 1024};
 // for lane 0) with 16-byte LDS loads, so the bins are read once, in parallel.
 // If the bins hold fewer than k keys it returns bin 0, above 0.
 template <int PER>
-__device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& bin, int& above, int& total) {
+__device__ __forceinline__ void load_bins_wave(const uint32_t* bins, uint32_t (&v)[PER]) {
   constexpr int nbins = PER * 64;
-  const int lane = threadIdx.x & 63;
-  const int lo = nbins - (lane + 1) * PER;  // lane owns bins [lo, lo + PER)
-  uint32_t v[PER];
+  const int lo = nbins - ((threadIdx.x & 63) + 1) * PER;  // lane owns bins [lo, lo + PER)
 #pragma unroll
   for (int j = 0; j < PER; j += 4) {
     const uint4 q = *reinterpret_cast<const uint4*>(bins + lo + j);
@@ -34,6 +32,14 @@ __device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& b
     v[j + 2] = q.z;
     v[j + 3] = q.w;
   }
+}
+
+// kth_bin_wave on bins a wave has already read with load_bins_wave.
+template <int PER>
+__device__ __forceinline__ void kth_bin_loaded(const uint32_t (&v)[PER], int k, int& bin, int& above, int& total) {
+  constexpr int nbins = PER * 64;
+  const int lane = threadIdx.x & 63;
+  const int lo = nbins - (lane + 1) * PER;
   int local = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) local += (int)v[j];
@@ -45,20 +51,20 @@ __device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& b
   }
   total = __shfl(incl, 63);
   const int before = incl - local;
-  int rb = -1, ra = 0;
+  // the lane whose bins cross k walks them from the top; selects with
+  // constant j keep the walk free of per-bin registers and branches
+  int fj = -1, ra = 0;
   if (before < k && incl >= k) {
     int acc = before;
-    bool done = false;
 #pragma unroll
     for (int j = PER - 1; j >= 0; --j) {
-      if (!done && acc + (int)v[j] >= k) {
-        rb = lo + j;
-        ra = acc;
-        done = true;
-      }
+      const bool hit = fj < 0 && acc + (int)v[j] >= k;
+      fj = hit ? j : fj;
+      ra = hit ? acc : ra;
       acc += (int)v[j];
     }
   }
+  const int rb = fj >= 0 ? lo + fj : -1;
   const uint64_t found = __ballot(rb >= 0);
   if (found == 0) {
     bin = 0;
@@ -68,6 +74,13 @@ __device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& b
   const int src = __ffsll((long long)found) - 1;
   bin = __shfl(rb, src);
   above = __shfl(ra, src);
+}
+
+template <int PER>
+__device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& bin, int& above, int& total) {
+  uint32_t v[PER];
+  load_bins_wave<PER>(bins, v);
+  kth_bin_loaded<PER>(v, k, bin, above, total);
 }
 
 __device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int nbins, int k, int& bin, int& above) {
