@@ -16,10 +16,12 @@
 //     m, for all of that request's query rows, and write the scores as
 //     order-preserving 32-bit keys to the workspace (G = all chunks for a
 //     single request; fewer, each looping, for a batch);
-//   * it then counts itself done on the request's arrival counter; the last
-//     workgroup to arrive loads each row's keys (at most 32768, 32 per
-//     thread) into registers and runs the whole radix select there
-//     (select_in_regs), writing the indices in ascending order.
+//   * each workgroup adds its share of each row's histogram of the top 11
+//     key bits to the workspace and counts itself done on the request's
+//     arrival counter; the last workgroup to arrive loads each row's keys
+//     (at most 32768, 32 per thread) into registers, takes the first digit
+//     of the K-th key from the finished histogram and runs the two remaining
+//     radix digits and the ordered write there (select_from_level1).
 // The keys make one round trip through the L2/Infinity Cache (4 bytes per
 // position against the 128-256 bytes of key read per position).  Rows longer
 // than 32768 positions take the two-pass route (indexer.hip).

@@ -134,133 +134,24 @@ namespace dsa {
 
 // Top-K of one row of `vis` <= NT * KPT keys held in registers, written to
 // out[0..K) in ascending position order; ties at the K-th key go to the lower
-// positions (rows with vis <= K are the caller's business).
+// positions (rows with vis <= K are the caller's business).  The first digit
+// is already known: bin1 is the top-11-bit bin of the K-th key (from a
+// histogram of the whole row built elsewhere) and `need` the number of keys
+// still to take from it.
 //
 // Layout: thread t holds key[c] = key of position KPT * t + c, so position
 // order is thread order.  Slots at or past `vis` must hold key 0, which lies
-// below the key of every finite score (only negative NaN patterns map under
-// it), so it is never above, equal to or at the K-th key of a row with
-// vis > K.
+// below the key of every finite score, so it is never above, equal to or at
+// the K-th key of a row with vis > K.
 //
-// Digits: the K-th key is found 11, 11 and 10 bits at a time with LDS
-// histograms (`hist`, kHistBins words) of the keys matching the digits found
-// so far.  The first digit only counts keys at or above a lower bound taken
-// from a sample (the first key of every thread, binned; the bin holding about
-// twice the sample rank the K-th key should have): when at least K keys clear
-// the bound, the K-th key is among them and its digit is exact from their
-// histogram alone; otherwise the digit is recounted over every key.  This
-// keeps the LDS atomics, which serialise on the busy bins, to a few thousand.
-//
+// The two remaining digits (11 and 10 bits) come from LDS histograms
+// (`hist`, kHistBins words) of the keys matching the digits found so far.
 // Output: the kept keys are the keys above the K-th plus the first `need`
-// keys equal to it, so one scan of per-thread (above, equal) counts gives
-// every thread its output offset, above_before + min(equal_before, need).
-// `wsum` holds NT / 64 ints, `res` 2.
-template <int NT, int KPT>
-__device__ void select_in_regs(const uint32_t (&key)[KPT], int vis, int K, int32_t* out, uint32_t* hist,
-                               int* wsum, int* res) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int base = tid * KPT;  // position of key[0]
-  const bool active = base < vis;
-
-  // ---- lower bound for the first digit from one sample key per thread ------
-  for (int c = tid; c < kHistBins; c += NT) hist[c] = 0u;
-  __syncthreads();
-  if (active) atomicAdd(&hist[key[0] >> kLevelShift[0]], 1u);
-  __syncthreads();
-  const int nsamp = min(NT, (vis + KPT - 1) / KPT);
-  const int srank = min(nsamp, (int)(((int64_t)2 * K * nsamp + vis - 1) / vis) + 8);
-  if (wave == 0) {
-    int bin, above;
-    kth_bin_wave(hist, kHistBins, srank, bin, above);
-    if (lane == 0) res[0] = bin;
-  }
-  __syncthreads();
-  const uint32_t lo_bin = (uint32_t)res[0];
-  __syncthreads();
-
-  uint32_t prefix = 0u;
-  int need = K;
-  for (int level = 0; level < 3; ++level) {
-    const int nbins = kLevelBins[level], shift = kLevelShift[level];
-    for (int c = tid; c < nbins; c += NT) hist[c] = 0u;
-    __syncthreads();
-    if (level == 0) {
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-          const uint32_t d = key[c] >> shift;
-          if (d >= lo_bin) atomicAdd(&hist[d], 1u);
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        int bin, above, total;
-        kth_bin_wave<32>(hist, K, bin, above, total);
-        if (lane == 0) res[0] = total;
-      }
-      __syncthreads();
-      if (res[0] < K) {  // the sample bound was too high: count every key
-        for (int c = tid; c < nbins; c += NT) hist[c] = 0u;
-        __syncthreads();
-        if (active) {
-#pragma unroll
-          for (int c = 0; c < KPT; ++c) atomicAdd(&hist[key[c] >> shift], 1u);
-        }
-      }
-    } else {
-      const int pshift = kLevelShift[level - 1];
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-          const uint32_t k = key[c];
-          if ((k >> pshift) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int bin, above;
-      kth_bin_wave(hist, nbins, need, bin, above);
-      if (lane == 0) {
-        res[0] = bin;
-        res[1] = above;
-      }
-    }
-    __syncthreads();
-    prefix = level == 0 ? (uint32_t)res[0] : ((prefix << (level == 1 ? 11 : 10)) | (uint32_t)res[0]);
-    need -= res[1];
-    __syncthreads();
-  }
-  const uint32_t kth = prefix;  // the K-th largest key; `need` keys equal to it are kept
-
-  int ngt = 0, neq = 0;
-#pragma unroll
-  for (int c = 0; c < KPT; ++c) {
-    ngt += key[c] > kth;
-    neq += key[c] == kth;
-  }
-  int packed_total;
-  const int packed_before = block_excl_scan<NT>(ngt | (neq << 16), packed_total, wsum);
-  const int gt_before = packed_before & 0xffff, eq_before = packed_before >> 16;
-  int o = gt_before + min(eq_before, need);
-  int er = eq_before;
-#pragma unroll
-  for (int c = 0; c < KPT; ++c) {
-    const bool e = key[c] == kth;
-    if (key[c] > kth || (e && er < need)) {
-      if (o < K) out[o] = base + c;
-      ++o;
-    }
-    er += e;
-  }
-  __syncthreads();
-}
-
-
-// select_in_regs when the first digit is already known: bin1 is the top-11-
-// bit bin of the K-th key (from a histogram of the whole row built
-// elsewhere) and `need` the number of keys still to take from it.  Runs the
-// two remaining digits and the ordered output over the register-resident keys.
+// keys equal to it.  Each thread builds bit masks of its keys above and equal
+// to the K-th; one scan of the per-thread counts gives every thread its
+// output offset, above_before + min(equal_before, need), and the thread
+// writes the positions of its mask bits in order.  `wsum` holds NT / 64
+// ints, `res` 2.
 template <int NT, int KPT>
 __device__ void select_from_level1(const uint32_t (&key)[KPT], int vis, int K, uint32_t bin1, int need,
                                    int32_t* out, uint32_t* hist, int* wsum, int* res) {
@@ -293,26 +184,29 @@ __device__ void select_from_level1(const uint32_t (&key)[KPT], int vis, int K, u
     need -= res[1];
     __syncthreads();
   }
+  static_assert(KPT <= 32, "one mask bit per key");
   const uint32_t kth = prefix;
-  int ngt = 0, neq = 0;
+  uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    ngt += key[c] > kth;
-    neq += key[c] == kth;
+    gtm |= key[c] > kth ? (1u << c) : 0u;
+    eqm |= key[c] == kth ? (1u << c) : 0u;
   }
   int packed_total;
-  const int packed_before = block_excl_scan<NT>(ngt | (neq << 16), packed_total, wsum);
+  const int packed_before = block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), packed_total, wsum);
   const int gt_before = packed_before & 0xffff, eq_before = packed_before >> 16;
+  // the first (need - eq_before) of this thread's keys equal to the K-th stay
+  uint32_t sel = gtm, e = eqm;
+  for (int take = need - eq_before; take > 0 && e != 0u; --take) {
+    sel |= e & (0u - e);
+    e &= e - 1u;
+  }
   int o = gt_before + min(eq_before, need);
-  int er = eq_before;
-#pragma unroll
-  for (int c = 0; c < KPT; ++c) {
-    const bool e = key[c] == kth;
-    if (key[c] > kth || (e && er < need)) {
-      if (o < K) out[o] = base + c;
-      ++o;
-    }
-    er += e;
+  while (sel != 0u) {
+    const int c = __builtin_ctz(sel);
+    if (o < K) out[o] = base + c;
+    ++o;
+    sel &= sel - 1u;
   }
   __syncthreads();
 }
