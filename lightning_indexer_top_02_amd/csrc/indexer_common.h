@@ -118,40 +118,58 @@ __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const un
 
 // One wave scores NPT loaded key tiles for `nrows` staged rows.  emit(r,
 // slot, score) runs on lanes 0..15 for slots slot0 + pt * 16 + lane.
-template <int DT, int D, int NPT, class Emit>
+// NR > 0 and MT > 0 fix the row count and Hpad / 16 at compile time: the
+// row and head-tile loops are then fully unrolled, so no loop reads the key
+// registers (a loop that does makes the compiler wait for every outstanding
+// vector load before entering it, prefetched tiles included).  The sums are
+// formed in the same order either way.
+template <int DT, int D, int NPT, int NR = 0, int MT = 0, class Emit>
 __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
                                                 const KeyTiles<DT, D, NPT>& t, int slot0, Emit&& emit) {
   using G = IdxGeom<DT, D>;
   using frag_t = typename G::frag_t;
   constexpr int KS = D / 32;  // contraction steps
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  for (int r = 0; r < nrows; ++r) {
+  const int hp = MT > 0 ? 16 * MT : Hpad;
+  auto head_tile = [&](int r, int ht, float (&sacc)[NPT]) {
+    f32x4 acc[NPT];
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const unsigned char* qrow = qs + (r * hp + ht * 16 + l16) * G::QSTRIDE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const frag_t a = *reinterpret_cast<const frag_t*>(qrow + G::frag_byte(ks, g));
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, t.kf[pt][ks], acc[pt]);
+    }
+    // acc[pt][i] = logit of head ht*16 + 4g + i at slot slot0 + pt*16 + l16
+    const float* wr = wsm + r * hp + ht * 16 + 4 * g;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[pt] += wr[i] * relu_keep_nan(acc[pt][i]);
+  };
+  auto row = [&](int r) {
     float sacc[NPT];
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) sacc[pt] = 0.f;
-    for (int ht = 0; ht < Hpad / 16; ++ht) {
-      f32x4 acc[NPT];
+    if constexpr (MT > 0) {
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const unsigned char* qrow = qs + (r * Hpad + ht * 16 + l16) * G::QSTRIDE;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const frag_t a = *reinterpret_cast<const frag_t*>(qrow + G::frag_byte(ks, g));
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, t.kf[pt][ks], acc[pt]);
-      }
-      // acc[pt][i] = logit of head ht*16 + 4g + i at slot slot0 + pt*16 + l16
-      const float* wr = wsm + r * Hpad + ht * 16 + 4 * g;
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[pt] += wr[i] * relu_keep_nan(acc[pt][i]);
+      for (int ht = 0; ht < MT; ++ht) head_tile(r, ht, sacc);
+    } else {
+      for (int ht = 0; ht < Hpad / 16; ++ht) head_tile(r, ht, sacc);
     }
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
       const float s = group4_sum(sacc[pt]);
       if (g == 0) emit(r, slot0 + pt * 16 + l16, s * t.kscale[pt]);
     }
+  };
+  if constexpr (NR > 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) row(r);
+  } else {
+    for (int r = 0; r < nrows; ++r) row(r);
   }
 }
 

@@ -52,6 +52,7 @@ struct FusedParams {
   int64_t key_stride;
   uint32_t* counters;   // [batch] arrival counters, zero between calls
   uint32_t* hist;       // [rows][kHistStride]: top-11-bit key histogram at offset 0, zero between calls
+  int kbuf_stride;      // > 0: keys are staged in LDS, this many per row (0: stored as they are made)
 };
 
 constexpr int kFusedThreads = 1024;
@@ -60,6 +61,8 @@ constexpr int kFusedChunk = kFusedWaves * 16;  // positions per workgroup
 constexpr int kFusedMaxRow = 32768;            // longest row the selection holds in LDS
 constexpr int kFusedMaxRows = 4;               // query rows per request
 constexpr int kKeysPerThread = kFusedMaxRow / kFusedThreads;
+constexpr int kFusedMaxPages = kFusedMaxRow / kFusedChunk * (kFusedChunk / kPage);  // pages one workgroup scores
+constexpr int kFusedKeyBuf = 16384;  // keys a workgroup may stage in LDS (64 KB)
 
 // Slot of position p in a row's key array.  The selecting workgroup holds
 // positions 32 t .. 32 t + 31 in thread t and loads them 4 at a time; keys
@@ -69,7 +72,13 @@ constexpr int kKeysPerThread = kFusedMaxRow / kFusedThreads;
 // (a wave reads 1 KB in one piece instead of 64 lines 128 bytes apart).
 __device__ __forceinline__ int key_slot(int p, int S) { return ((p & 31) >> 2) * S + ((p >> 5) << 2) + (p & 3); }
 
-template <int DT, int D>
+// MODE 0: few chunks per workgroup (small batches): latency first.
+// MODE 1: many chunks per workgroup: block-table entries in LDS, three key
+//         tiles in rotation, keys staged in LDS and written out at the end.
+// MODE 2: MODE 1 where every request has one query row and 64 heads (the
+//         decode shape): the scoring has no inner loops over rows and head
+//         tiles, which keeps the prefetched key tiles in flight.
+template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
   using Gm = IdxGeom<DT, D>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -98,28 +107,63 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
     uint32_t* lh = reinterpret_cast<uint32_t*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad));
     const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
     const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
-    auto load = [&](KeyTiles<DT, D, 1>& t, int t0) {
-      const int phys = btrow[t0 >> 6];
+    const int step = G * kFusedChunk;
+    int* wg_pages = reinterpret_cast<int*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad) +
+                                           (size_t)p.rcap * kHistBins * 4);
+    uint32_t* kbuf = reinterpret_cast<uint32_t*>(wg_pages + kFusedMaxPages);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int t0 = c0 + wave_u * 16;
+    const int last_j = t0 <= pos_max ? (pos_max - t0) / step : -1;  // this wave's last chunk
+    KeyTiles<DT, D, 1> ring[3];
+    auto load_at = [&](KeyTiles<DT, D, 1>& t, int phys, int tpos) {
       load_key_tiles<DT, D, 1>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
-                               DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, t0 & 63);
+                               DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, tpos & 63);
     };
-    KeyTiles<DT, D, 1> cur, nxt;
-    int t0 = c0 + wave * 16;
-    // the first key tile is in flight while the queries are staged
-    if (DT != 0 && t0 <= pos_max) load(nxt, t0);
+    if constexpr (MODE == 0) {
+      // few chunks per workgroup (small batches): the first key tile is in
+      // flight while the queries are staged
+      if (DT != 0 && last_j >= 0) load_at(ring[0], btrow[t0 >> 6], t0);
+    } else {
+      // Many chunks per workgroup: the block-table entries of every page it
+      // scores go to LDS first (entry 4 j + i: page i of its j-th chunk), so a
+      // key tile's load waits only on LDS, never on the vector loads of the
+      // tiles in flight.  Three key tiles rotate: two chunks ahead are in
+      // flight while one is scored.  Every step issues its loads (past the
+      // wave's last chunk, that chunk again), so the wait for a tile always
+      // has the two later tiles' loads behind it and leaves them in flight.
+      const int n_pages = ((pos_max - c0) / step + 1) * (kFusedChunk / kPage);
+      for (int i = tid; i < n_pages; i += kFusedThreads) {
+        const int pg = c0 / kPage + (i / (kFusedChunk / kPage)) * (step / kPage) + i % (kFusedChunk / kPage);
+        wg_pages[i] = pg <= pos_max / kPage ? btrow[pg] : 0;
+      }
+      __syncthreads();
+      if (last_j >= 0) {
+        load_at(ring[0], wg_pages[wave_u / (kPage / 16)], t0);
+        load_at(ring[1], wg_pages[min(1, last_j) * (kFusedChunk / kPage) + wave_u / (kPage / 16)], t0);
+      }
+    }
     stage_queries<DT, D, kFusedThreads>(qs, wsm, p.q, p.q_scale, p.w, q0, nb, p.H, p.Hpad);
     for (int c = tid; c < nb * kHistBins; c += kFusedThreads) lh[c] = 0u;
     __syncthreads();
+    // In the batched modes keys go to LDS when they fit (chunk j's 256 keys
+    // at j * 256 of the row's stretch) and are written out in whole lines
+    // once the workgroup is done: stores among the scoring loads would make
+    // every wait for a key tile also wait for them.
     auto emit = [&](int r, int pos, float s) {
       if (pos <= first_pos + r) {
         const uint32_t k = score_key(s);
-        p.keys[(int64_t)(q0 + r) * p.key_stride + key_slot(pos, key_group_stride)] = k;
+        if (MODE != 0 && p.kbuf_stride > 0) {
+          const int j = (pos - c0) / step;
+          kbuf[r * p.kbuf_stride + j * kFusedChunk + (pos - c0 - j * step)] = k;
+        } else {
+          p.keys[(int64_t)(q0 + r) * p.key_stride + key_slot(pos, key_group_stride)] = k;
+        }
         atomicAdd(&lh[r * kHistBins + (k >> kLevelShift[0])], 1u);
       }
     };
     if (DT == 0) {
       const int lane = tid & 63;
-      for (int c = c0; c <= pos_max; c += G * kFusedChunk) {
+      for (int c = c0; c <= pos_max; c += step) {
         const int tp = c + wave * 16;
         if (lane < 16 && tp + lane <= pos_max) {
           const int pos = tp + lane;
@@ -128,21 +172,60 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
                            [&](int r, float s) { emit(r, pos, s); });
         }
       }
-    } else {
-      for (; t0 <= pos_max; t0 += G * kFusedChunk) {
-        cur = nxt;
-        if (t0 + G * kFusedChunk <= pos_max) load(nxt, t0 + G * kFusedChunk);
-        score_key_tiles<DT, D, 1>(qs, wsm, p.Hpad, nb, cur, t0 & 63,
+    } else if constexpr (MODE == 0) {
+      for (; t0 <= pos_max; t0 += step) {
+        ring[1] = ring[0];
+        if (t0 + step <= pos_max) load_at(ring[0], btrow[(t0 + step) >> 6], t0 + step);
+        score_key_tiles<DT, D, 1>(qs, wsm, p.Hpad, nb, ring[1], t0 & 63,
                                   [&](int r, int slot, float s) { emit(r, (t0 & ~63) + slot, s); });
+      }
+    } else {
+      auto load = [&](KeyTiles<DT, D, 1>& t, int j) {  // this wave's tile of chunk j
+        load_at(t, wg_pages[j * (kFusedChunk / kPage) + wave_u / (kPage / 16)], t0);
+      };
+      auto score = [&](const KeyTiles<DT, D, 1>& kt, int tc) {
+        auto em = [&](int r, int slot, float s) { emit(r, (tc & ~63) + slot, s); };
+        if constexpr (MODE == 2)  // one row of 64 heads: no inner loops
+          score_key_tiles<DT, D, 1, 1, 4>(qs, wsm, 64, 1, kt, tc & 63, em);
+        else
+          score_key_tiles<DT, D, 1>(qs, wsm, p.Hpad, nb, kt, tc & 63, em);
+      };
+      for (int j = 0; j <= last_j; j += 3) {
+        load(ring[2], min(j + 2, last_j));
+        score(ring[0], t0 + j * step);
+        if (j + 1 > last_j) break;
+        load(ring[0], min(j + 3, last_j));
+        score(ring[1], t0 + (j + 1) * step);
+        if (j + 2 > last_j) break;
+        load(ring[1], min(j + 4, last_j));
+        score(ring[2], t0 + (j + 2) * step);
       }
     }
   }
 
-  // ---- the histograms go to the workspace (their sums are complete when the
-  // last workgroup arrives)
+  // ---- staged keys and the histograms go to the workspace (the histogram
+  // sums are complete when the last workgroup arrives)
   if (any_select && c0 <= pos_max) {
     const uint32_t* lh = reinterpret_cast<const uint32_t*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad));
     __syncthreads();
+    if (MODE != 0 && p.kbuf_stride > 0) {
+      // item i: row r, chunk j, line L of the chunk's 8 slot lines, word k;
+      // 32 consecutive items fill one 128-byte line of the key array
+      const int step = G * kFusedChunk;
+      const int n_ch = (pos_max - c0) / step + 1;
+      const uint32_t* kbuf = reinterpret_cast<const uint32_t*>(smem + query_lds_bytes<DT, D>(p.rcap, p.Hpad) +
+                                                               (size_t)p.rcap * kHistBins * 4 + kFusedMaxPages * 4);
+      for (int i = tid; i < nb * n_ch * kFusedChunk; i += kFusedThreads) {
+        const int r = i / (n_ch * kFusedChunk), rest = i - r * n_ch * kFusedChunk;
+        const int j = rest / kFusedChunk, w = rest - j * kFusedChunk;
+        const int L = w >> 5, k = w & 31;
+        const int cs = c0 + j * step;                 // the chunk's first position
+        const int pos = cs + 32 * (k >> 2) + 4 * L + (k & 3);
+        if (pos <= first_pos + r)
+          p.keys[(int64_t)(q0 + r) * p.key_stride + key_slot(pos, key_group_stride)] =
+              kbuf[r * p.kbuf_stride + j * kFusedChunk + (pos - cs)];
+      }
+    }
     for (int c = tid; c < nb * kHistBins; c += kFusedThreads) {
       const uint32_t v = lh[c];
       if (v) {
@@ -235,22 +318,39 @@ using namespace dsa;
 
 namespace {
 
-// Workgroups a batch should fill: a few per compute unit.
-constexpr int kFusedTargetWGs = 512;
+// Workgroups a batch should fill: one per compute unit (a 1024-thread
+// workgroup at ~128 VGPRs per thread fills one; a larger grid only queues a
+// second round behind the first: 157 us against 139 us for 64 rows at 32K).
+constexpr int kFusedTargetWGs = 256;
+
+template <int DT, int D, int MODE>
+hipError_t launch_fused_as(const FusedParams& p, int batch, size_t lds, hipStream_t s) {
+  {
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(li_fused<DT, D, MODE>), lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((li_fused<DT, D, MODE>), dim3(p.G * batch), dim3(kFusedThreads), lds, s, p);
+  return hipGetLastError();
+}
 
 template <int DT, int D>
 hipError_t launch_fused(FusedParams p, int batch, int max_ctx, hipStream_t s) {
   const int chunks = (max_ctx + kFusedChunk - 1) / kFusedChunk;
   p.G = std::max(1, std::min(chunks, (kFusedTargetWGs + batch - 1) / batch));
   p.row_cap = std::min(max_ctx, kFusedMaxRow);
-  const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4,
+  // chunks per workgroup decide the mode: with one or two the scoring is one
+  // latency chain; with more, throughput (prefetch depth, no stores among
+  // the loads) decides
+  const int max_ch = (chunks + p.G - 1) / p.G;
+  const int mode = max_ch < 3 ? 0 : (DT != 0 && p.rcap == 1 && p.Hpad == 64 ? 2 : 1);
+  // batched modes stage a workgroup's keys in LDS when they fit
+  p.kbuf_stride = mode != 0 && p.rcap * max_ch * kFusedChunk <= kFusedKeyBuf ? max_ch * kFusedChunk : 0;
+  const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4 +
+                                  (size_t)kFusedMaxPages * 4 + (size_t)p.rcap * p.kbuf_stride * 4,
                               (size_t)kHistBins * 4);
-  {
-    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(li_fused<DT, D>), lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((li_fused<DT, D>), dim3(p.G * batch), dim3(kFusedThreads), lds, s, p);
-  return hipGetLastError();
+  if (mode == 0) return launch_fused_as<DT, D, 0>(p, batch, lds, s);
+  if (mode == 1) return launch_fused_as<DT, D, 1>(p, batch, lds, s);
+  return launch_fused_as<DT, D, 2>(p, batch, lds, s);
 }
 
 }  // namespace

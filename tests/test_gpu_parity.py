@@ -187,6 +187,45 @@ def test_batched_fp8_full(wide):
     _full(case, rows)
 
 
+# --- batched decode through the single-kernel indexer ---------------------------
+# Many 256-position chunks per workgroup switch the fused kernel to its
+# throughput modes (block-table entries in LDS, three key tiles in flight,
+# keys staged in LDS when they fit); each case checks the indices against the
+# two-pass route bit for bit and against the oracle on sampled rows.
+def _fused_b24():
+    rng = np.random.default_rng(91)
+    lens = rng.integers(5000, 32769, size=24).tolist()
+    n_q = [1 + (i % 3 == 0) for i in range(24)]
+    return inputs.make_case(name="fused_b24_fp8_48h", seed=91, ctx_lens=lens, n_q=n_q, idx_dtype="fp8",
+                            n_heads_idx=48, head_dim_idx=128, topk=2048, sfa_dtype=None, device="cuda")
+
+
+FUSED_BATCHED = {
+    # 64 one-row requests at 32768, 64 heads: the one-row 64-head mode, keys staged
+    "b64_bf16": lambda: inputs.decode_32k(batch=64, device="cuda", sfa_dtype=None),
+    # 24 requests of 1-2 rows, 48 fp8 heads, ragged lengths: the general batched mode
+    "b24_fp8_48h": _fused_b24,
+    # 300 requests: one workgroup each, more keys than LDS staging holds
+    "b300_fp8_d64": lambda: inputs.make_case(name="fused_b300_fp8_d64", seed=92, ctx_lens=[20000] * 300, n_q=1,
+                                             idx_dtype="fp8", n_heads_idx=64, head_dim_idx=64, topk=2048,
+                                             sfa_dtype=None, device="cuda"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_BATCHED))
+def test_fused_batched_modes(name):
+    case = FUSED_BATCHED[name]()
+    print(f"\n[case] {case.name} seed={case.seed} B={case.batch} T={case.num_tokens} "
+          f"max_ctx={case.max_ctx} K={case.topk}", flush=True)
+    idx = parity.gpu_indexer_topk(case)
+    two = parity.gpu_indexer_topk(case, flags=parity.dsa.INDEXER_TWO_PASS)
+    assert torch.equal(idx, two), "fused and two-pass indices differ"
+    T = case.num_tokens
+    rows = sorted({0, 1, T // 3, T // 2, T - 2, T - 1})
+    stats = parity.check_rows(case, idx, None, rows)
+    print(f"[ok] {case.name}: {stats}", flush=True)
+
+
 def test_causal_planted_future_keys_never_selected():
     """Keys after a row's position made huge must never be selected."""
     case = inputs.spec_verify(batch=1, ctx=3000, exact=True)
