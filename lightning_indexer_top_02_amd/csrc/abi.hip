@@ -112,7 +112,11 @@ SfaPlan plan_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int topk) {
   if (s->dtype == DSA_BF16) {
     p.nw = sfa_waves(s->n_heads, pg->num_q_tokens);
     const int64_t blocks = (int64_t)pg->num_q_tokens * (s->n_heads / (16 * p.nw));
-    int64_t splits = (2 * kNominalCUs + blocks - 1) / blocks;
+    // about one workgroup per compute unit: a bf16 SFA workgroup of four
+    // tiles holds ~230 VGPRs per lane, so a compute unit runs one at a time
+    // and a larger grid only queues a second round (64 decode rows at 32K:
+    // 107.6 us with two rounds, 94.2 us with one)
+    int64_t splits = (kNominalCUs + blocks - 1) / blocks;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (topk + 63) / 64));
     p.rows_per_split = (int)round_up((topk + splits - 1) / splits, 32);
     p.n_split = (topk + p.rows_per_split - 1) / p.rows_per_split;
