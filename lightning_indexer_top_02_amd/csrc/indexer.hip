@@ -166,20 +166,29 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
         }
       }
     };
-    auto load = [&](KeyTiles<DT, D, 4>& t, int req, int pg) {
-      const int phys = p.bt[(int64_t)req * p.bt_stride + pg];
+    auto load = [&](KeyTiles<DT, D, 4>& t, int phys) {
       load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
                                DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, 0);
+    };
+    // block-table entry of this wave's page of chunk fn (-1: none); read one
+    // chunk ahead of the tile load that needs it, so the tile loads never wait
+    // on a block-table read
+    auto page_of = [&](int fn) {
+      if (fn >= f1) return -1;
+      advance_to(fn);
+      const int pgn = (fn - nb_base) * (kChunk / kPage) + wave;
+      return pgn * kPage <= nb_posmax ? p.bt[(int64_t)nb_req * p.bt_stride + pgn] : -1;
     };
     KeyTiles<DT, D, 4> cur, nxt;
     bool have = false;
     {
       const int pg = (f0 - base) * (kChunk / kPage) + wave;
       if (pg * kPage <= pos_max) {
-        load(nxt, b, pg);
+        load(nxt, p.bt[(int64_t)b * p.bt_stride + pg]);
         have = true;
       }
     }
+    int ph1 = page_of(f0 + 1);
     for (int f = f0; f < f1; ++f) {
       if (f - base >= nchunks) {
         leave();
@@ -190,19 +199,21 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
       }
       cur = nxt;
       const bool have_cur = have;
-      have = false;
-      if (f + 1 < f1) {  // next chunk's page for this wave
-        advance_to(f + 1);
-        const int pgn = (f + 1 - nb_base) * (kChunk / kPage) + wave;
-        if (pgn * kPage <= nb_posmax) {
-          load(nxt, nb_req, pgn);
-          have = true;
-        }
-      }
+      have = ph1 >= 0;
+      if (have) load(nxt, ph1);  // next chunk's page for this wave
+      ph1 = page_of(f + 2);
       if (have_cur) {
         const int pg = (f - base) * (kChunk / kPage) + wave;
-        score_key_tiles<DT, D, 4>(qs, wsm, p.Hpad, nrows, cur, 0,
-                                  [&](int r, int slot, float sc) { emit(r, pg * kPage + slot, sc); });
+        // one or four rows of 64 heads (decode, speculative verify) with
+        // the row and head-tile loops unrolled, anything else through the
+        // general loops; the sums are formed in the same order either way
+        auto em = [&](int r, int slot, float sc) { emit(r, pg * kPage + slot, sc); };
+        if (nrows == 4 && p.Hpad == 64)
+          score_key_tiles<DT, D, 4, 4, 4>(qs, wsm, 64, 4, cur, 0, em);
+        else if (nrows == 1 && p.Hpad == 64)
+          score_key_tiles<DT, D, 4, 1, 4>(qs, wsm, 64, 1, cur, 0, em);
+        else
+          score_key_tiles<DT, D, 4>(qs, wsm, p.Hpad, nrows, cur, 0, em);
       }
     }
   }
