@@ -67,21 +67,43 @@ __device__ __forceinline__ int visible_of(const SegParams& p, int i) {
   return p.ctx_lens[b] - nb + (i - p.q_offsets[b]) + 1;
 }
 
-// This thread's kSegPer consecutive keys of segment s (key 0 past vis).
-__device__ __forceinline__ void load_seg_keys(const float* row, int pos0, int vis, uint32_t (&key)[kSegPer]) {
+// A segment's scores pass through LDS so that the global reads are
+// coalesced (float4 q of the segment from thread q % kSegThreads) while each
+// thread still ends up with kSegPer consecutive keys (position order is
+// thread order).  Rows are padded by 4 floats every 32, so the per-thread
+// 16-byte reads of a 16-lane group start 36 floats apart and fill all banks.
+constexpr int kSegBufFloats = kSegLen + kSegLen / 8;
+
+// Issue the segment's reads into the LDS buffer (s0: first position).
+__device__ __forceinline__ void fetch_seg_scores(const float* row, int s0, int vis, float* buf) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kSegPer / 4; ++j) {
+    const int q = j * kSegThreads + tid;  // float4 of the segment
+    const int t = s0 + 4 * q;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t + 4 <= vis) {
+      v = *reinterpret_cast<const float4*>(row + t);
+    } else {
+      if (t < vis) v.x = row[t];
+      if (t + 1 < vis) v.y = row[t + 1];
+      if (t + 2 < vis) v.z = row[t + 2];
+    }
+    *reinterpret_cast<float4*>(buf + 4 * q + 4 * (q >> 3)) = v;
+  }
+}
+
+// This thread's kSegPer consecutive keys from the buffer (key 0 past vis);
+// the caller has synchronised the workgroup after fetch_seg_scores.
+__device__ __forceinline__ void seg_keys_from_lds(const float* buf, int pos0, int vis, uint32_t (&key)[kSegPer]) {
+  const float* mine = buf + threadIdx.x * (kSegPer + kSegPer / 8);
 #pragma unroll
   for (int c = 0; c < kSegPer; c += 4) {
-    const int t = pos0 + c;
-    if (t + 4 <= vis) {
-      const float4 v = *reinterpret_cast<const float4*>(row + t);
-      key[c] = score_key(v.x);
-      key[c + 1] = score_key(v.y);
-      key[c + 2] = score_key(v.z);
-      key[c + 3] = score_key(v.w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) key[c + j] = t + j < vis ? score_key(row[t + j]) : 0u;
-    }
+    const float4 v = *reinterpret_cast<const float4*>(mine + c);
+    key[c] = pos0 + c < vis ? score_key(v.x) : 0u;
+    key[c + 1] = pos0 + c + 1 < vis ? score_key(v.y) : 0u;
+    key[c + 2] = pos0 + c + 2 < vis ? score_key(v.z) : 0u;
+    key[c + 3] = pos0 + c + 3 < vis ? score_key(v.w) : 0u;
   }
 }
 
@@ -96,11 +118,14 @@ __device__ __forceinline__ int block_sum(int v, int* wsum) {
 __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   __shared__ __align__(16) int wsum[kSegThreads / 64];
   __shared__ int sh[3];
+  __shared__ __align__(16) float buf[kSegBufFloats];
   const int i = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int vis = visible_of(p, i);
   const int s0 = seg * kSegLen;
   if (vis <= p.K || s0 >= vis) return;
   uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
+  // the segment's scores are in flight while wave 0 reads the histogram
+  fetch_seg_scores(p.scores + (int64_t)i * p.score_stride, s0, vis, buf);
   if (tid < 64) {
     int bin, above, total;
     kth_bin_wave<32>(hrow, p.K, bin, above, total);
@@ -114,7 +139,7 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   const bool gather = sh[1] <= p.cand_cap;
   uint32_t key[kSegPer];
   const int pos0 = s0 + tid * kSegPer;
-  load_seg_keys(p.scores + (int64_t)i * p.score_stride, pos0, vis, key);
+  seg_keys_from_lds(buf, pos0, vis, key);
   int ngt = 0, neq = 0;
 #pragma unroll
   for (int c = 0; c < kSegPer; ++c) {
@@ -281,6 +306,7 @@ __global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
 
 __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   __shared__ __align__(16) int wsum[kSegThreads / 64];
+  __shared__ __align__(16) float buf[kSegBufFloats];
   const int i = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int vis = visible_of(p, i);
   const int K = p.K;
@@ -291,13 +317,17 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   }
   const uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
   const int s0 = seg * kSegLen;
-  if (s0 >= vis || (hrow[kStateFlags] & 1u)) return;
+  if (s0 >= vis) return;
+  // the segment's scores are in flight while the row's state is read
+  fetch_seg_scores(p.scores + (int64_t)i * p.score_stride, s0, vis, buf);
+  if (hrow[kStateFlags] & 1u) return;  // (uniform) the row is left to li_topk
   const uint32_t kth = hrow[kStateKth];
   const int limit = (int)hrow[kStateLimit];
   const int off = (int)hrow[kSegBase + seg];
+  __syncthreads();
   uint32_t key[kSegPer];
   const int pos0 = s0 + tid * kSegPer;
-  load_seg_keys(p.scores + (int64_t)i * p.score_stride, pos0, vis, key);
+  seg_keys_from_lds(buf, pos0, vis, key);
   int n = 0;
 #pragma unroll
   for (int c = 0; c < kSegPer; ++c) {
