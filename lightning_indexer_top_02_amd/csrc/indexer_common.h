@@ -173,25 +173,6 @@ __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const f
   }
 }
 
-// One wave scores NPT tiles of 16 positions of one page (slots slot0 ..
-// slot0 + 16 NPT - 1) for `nrows` staged rows.
-template <int DT, int D, int NPT, class Emit>
-__device__ __forceinline__ void score_tiles_mfma(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
-                                                 const unsigned char* kpage, const float* kscale_page,
-                                                 int slot0, Emit&& emit) {
-  KeyTiles<DT, D, NPT> t;
-  load_key_tiles<DT, D, NPT>(t, kpage, kscale_page, slot0);
-  score_key_tiles<DT, D, NPT>(qs, wsm, Hpad, nrows, t, slot0, emit);
-}
-
-// One wave scores the 64 positions of one page.
-template <int DT, int D, class Emit>
-__device__ __forceinline__ void score_page_mfma(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
-                                                const unsigned char* kpage, const float* kscale_page,
-                                                Emit&& emit) {
-  score_tiles_mfma<DT, D, 4>(qs, wsm, Hpad, nrows, kpage, kscale_page, 0, emit);
-}
-
 // One thread scores one fp32 key row for `nrows` staged rows.
 template <int D, class Emit>
 __device__ __forceinline__ void score_pos_f32(const float* qs, const float* wsm, int H, int nrows,
