@@ -266,30 +266,36 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
 }
 
 // Merge split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
-// One thread per (query row, head, 4 output dims), 128 threads per head, so
-// a decode row's merge is spread over the whole chip.  Splits are read 16 at
-// a time with all their loads in flight, folded in with a running maximum
-// (the sum is rescaled when the maximum grows), so the merge costs about one
-// memory round trip per 16 splits.
+// G threads per (query row, head, 4 output dims), 128 G threads per head, so
+// a decode row's merge is spread over the whole chip.  Thread g of a group
+// takes splits g, g + G, ..., reading them 16 at a time with all their loads
+// in flight and folding them in with a running maximum (the sum is rescaled
+// when the maximum grows); the G partial merges are then combined across
+// neighbouring lanes, lower lane first, so every lane of a group forms the
+// same result.  With G = 4 a merge of up to 64 splits is one memory round
+// trip (few rows, many splits); G = 1 keeps the grid small for large batches.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineBatch = 16;
 
-template <bool BF16>
+template <bool BF16, int G>
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
   const int64_t gt = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
-  const int64_t th = gt >> 7;            // = i * H + h
-  const int d0 = (int)(gt & 127) * 4;    // first of this thread's 4 dims
+  const int sg = (int)(gt % G);
+  const int64_t rest = gt / G;
+  const int64_t th = rest >> 7;           // = i * H + h
+  const int d0 = (int)(rest & 127) * 4;   // first of this group's 4 dims
   const int64_t stride = (int64_t)p.T * p.H;
-  if (th >= stride) return;
+  // (whole groups are in range or out of it: the grid is a multiple of G)
+  const bool ok = th < stride;
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* po = p.part_o + th * kVDim + d0;
-  for (int s0 = 0; s0 < p.n_split; s0 += kCombineBatch) {
+  const float* po = p.part_o + (ok ? th : 0) * kVDim + d0;
+  for (int s0 = 0; ok && s0 * G < p.n_split; s0 += kCombineBatch) {
     float l[kCombineBatch];
     float4 o[kCombineBatch];
 #pragma unroll
     for (int j = 0; j < kCombineBatch; ++j) {
-      const int s = s0 + j;
+      const int s = (s0 + j) * G + sg;
       l[j] = s < p.n_split ? p.part_lse[s * stride + th] : -INFINITY;
       o[j] = s < p.n_split ? *reinterpret_cast<const float4*>(po + s * stride * kVDim) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -309,6 +315,22 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
     }
     M = Mn;
   }
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) {
+    const float Mo = __shfl_xor(M, off), deno = __shfl_xor(den, off);
+    const float4 acco = make_float4(__shfl_xor(acc.x, off), __shfl_xor(acc.y, off), __shfl_xor(acc.z, off),
+                                    __shfl_xor(acc.w, off));
+    const bool upper = (sg & off) != 0;  // this lane's partial goes second
+    const float Ma = upper ? Mo : M, Mb = upper ? M : Mo;
+    const float da = upper ? deno : den, db = upper ? den : deno;
+    const float4 aa = upper ? acco : acc, ab = upper ? acc : acco;
+    const float Mn = fmaxf(Ma, Mb);
+    const float ra = Ma == -INFINITY ? 0.f : expf(Ma - Mn), rb = Mb == -INFINITY ? 0.f : expf(Mb - Mn);
+    den = da * ra + db * rb;
+    acc = make_float4(aa.x * ra + ab.x * rb, aa.y * ra + ab.y * rb, aa.z * ra + ab.z * rb, aa.w * ra + ab.w * rb);
+    M = Mn;
+  }
+  if (!ok || sg != 0) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
   if (BF16) {
     uint2 v;
@@ -450,8 +472,12 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  const int64_t threads = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
-  hipLaunchKernelGGL(sfa_combine<true>, dim3((unsigned)((threads + kCombineThreads - 1) / kCombineThreads)),
-                     dim3(kCombineThreads), 0, s, p);
+  const int64_t groups = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
+  if (a.n_split >= 8)
+    hipLaunchKernelGGL((sfa_combine<true, 4>), dim3((unsigned)((4 * groups + kCombineThreads - 1) / kCombineThreads)),
+                       dim3(kCombineThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((sfa_combine<true, 1>), dim3((unsigned)((groups + kCombineThreads - 1) / kCombineThreads)),
+                       dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
