@@ -112,7 +112,15 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + kKrowBytes);
   int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + sizeof(SfaXchg));  // pool row, -1 = none
 
-  const int split = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
+  // XCD-aware order: consecutive workgroups go to the eight XCDs in turn,
+  // so the head groups of one (split, row) are given ids 8 apart and land on
+  // one XCD, where the later ones find the gathered rows in its L2
+  const int n_hg = p.H / (16 * NW);
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int hg = slot % n_hg;
+  const int rs = (slot / n_hg) * 8 + xcd;  // (split, row) pair
+  if (rs >= p.n_split * p.T) return;
+  const int split = rs % p.n_split, i = rs / p.n_split;
   const int b = request_of_row(p.q_offsets, p.batch, i);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   // wave = (half, head tile): the tile's 16 heads; S for rows 16 half .. +16 of
@@ -459,7 +467,13 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   }
   const int nw = a.nw;  // 16-head tiles per workgroup
   if (nw < 1 || nw > 4 || (a.n_heads / 16) % nw != 0) return hipErrorInvalidValue;
-  dim3 grid(a.n_split, a.n_heads / (16 * nw), a.num_rows);
+  // one dimension: (split, row) pairs in groups of eight, each group's head
+  // groups 8 workgroups apart (see sfa_bf16)
+  const int64_t pairs = (int64_t)a.n_split * a.num_rows;
+  const int64_t wgs = (pairs + 7) / 8 * 8 * (a.n_heads / (16 * nw));
+  // the work-item count of one grid dimension has to fit 32 bits
+  if (wgs * nw * 128 > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
   hipError_t e0;
   const size_t lds = (size_t)kKrowBytes + sizeof(SfaXchg) +
                      (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
