@@ -65,6 +65,45 @@ __device__ __forceinline__ float group4_max(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Wave scans through DPP (the VALU's data-parallel-primitive operand
+// routing of the GFX9 family) instead of LDS shuffles.  update_dpp(0, x, ...)
+// hands each lane the routed value of x, or 0 where the route has no source
+// lane or the lane's row is masked off.
+//   row_shr:n (0x110 + n)  lane l of a 16-lane row gets lane l - n of that row
+//   row_bcast:15 (0x142)   every lane of row r gets lane 15 of row r - 1
+//   row_bcast:31 (0x143)   every lane of rows 2 and 3 gets lane 31
+// All 64 lanes must be active.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_route(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: a Hillis-Steele scan
+// inside each 16-lane row, then the totals of rows 0 and 2 added to rows 1
+// and 3, then the total of rows 0-1 added to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_route<0x111>(x);
+  x += dpp_route<0x112>(x);
+  x += dpp_route<0x114>(x);
+  x += dpp_route<0x118>(x);
+  x += dpp_route<0x142, 0xa>(x);
+  x += dpp_route<0x143, 0xc>(x);
+  return x;
+}
+
+// x of lane l ^ off within each group of four lanes (off = 1 or 2), with a
+// quad_perm route: 0xB1 sends lanes (1, 0, 3, 2) to (0, 1, 2, 3), 0x4E sends
+// lanes (2, 3, 0, 1).
+__device__ __forceinline__ float quad_xor(float x, int off) {
+  const int v = __float_as_int(x);
+  return __int_as_float(off == 1 ? dpp_route<0xB1>(v) : dpp_route<0x4E>(v));
+}
+
+// Value of x on lane `src` (wave-uniform), through a scalar register.
+__device__ __forceinline__ int wave_read_lane(int x, int src) { return __builtin_amdgcn_readlane(x, src); }
+
+// ---------------------------------------------------------------------------
 // Request lookup: the request that owns query row i (q_offsets is sorted).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int request_of_row(const int32_t* q_offsets, int batch, int i) {

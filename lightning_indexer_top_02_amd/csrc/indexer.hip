@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kTopkThreads) void li_topk(TopkParams p) {
         int base = 0;
         if (n) {
           if (lane == 0) base = atomicAdd(&sh.ncand, n);
-          base = __shfl(base, 0);
+          base = wave_read_lane(base, 0);  // lane 0 is active whenever any lane is
         }
         const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
         if (pred && slot < kCandCap) sh.cand[slot] = key[e] & 0x1fffffu;

@@ -43,13 +43,8 @@ __device__ __forceinline__ void kth_bin_loaded(const uint32_t (&v)[PER], int k, 
   int local = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) local += (int)v[j];
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  total = __shfl(incl, 63);
+  const int incl = wave_incl_scan(local);
+  total = wave_read_lane(incl, 63);
   const int before = incl - local;
   // the lane whose bins cross k walks them from the top; selects with
   // constant j keep the walk free of per-bin registers and branches
@@ -72,8 +67,8 @@ __device__ __forceinline__ void kth_bin_loaded(const uint32_t (&v)[PER], int k, 
     return;
   }
   const int src = __ffsll((long long)found) - 1;
-  bin = __shfl(rb, src);
-  above = __shfl(ra, src);
+  bin = wave_read_lane(rb, src);
+  above = wave_read_lane(ra, src);
 }
 
 template <int PER>
@@ -95,12 +90,7 @@ template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int& total, int* wsum) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
+  const int incl = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();

@@ -287,6 +287,7 @@ constexpr int kCombineBatch = 16;
 
 template <bool BF16, int G>
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
+  static_assert(G == 1 || G == 2 || G == 4, "lane groups within a quad");
   const int64_t gt = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
   const int sg = (int)(gt % G);
   const int64_t rest = gt / G;
@@ -324,10 +325,10 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
     M = Mn;
   }
 #pragma unroll
-  for (int off = 1; off < G; off <<= 1) {
-    const float Mo = __shfl_xor(M, off), deno = __shfl_xor(den, off);
-    const float4 acco = make_float4(__shfl_xor(acc.x, off), __shfl_xor(acc.y, off), __shfl_xor(acc.z, off),
-                                    __shfl_xor(acc.w, off));
+  for (int off = 1; off < G; off <<= 1) {  // (every lane of the wave is here)
+    const float Mo = quad_xor(M, off), deno = quad_xor(den, off);
+    const float4 acco = make_float4(quad_xor(acc.x, off), quad_xor(acc.y, off), quad_xor(acc.z, off),
+                                    quad_xor(acc.w, off));
     const bool upper = (sg & off) != 0;  // this lane's partial goes second
     const float Ma = upper ? Mo : M, Mb = upper ? M : Mo;
     const float da = upper ? deno : den, db = upper ? den : deno;
