@@ -23,14 +23,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even binary32 -> bfloat16 (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
 // Order-preserving 32-bit key of an fp32 score: a larger score gives a larger
 // unsigned key; -0 and +0 map to the same key, so equal scores tie exactly.
 __device__ __forceinline__ uint32_t score_key(float s) {

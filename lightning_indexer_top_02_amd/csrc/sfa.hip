@@ -58,8 +58,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.f;  // log2 headroom before the running maximum is moved
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16 and packed (lo in the low
+// half) by gfx950's one-instruction conversion, v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 // LDS layout of one staged chunk of 32 rows: krow, a row-major copy of the
@@ -218,10 +223,14 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
       }
       m = mnew;
     }
+    // exponentials with the bare hardware exp2 (v_exp_f32: exp2(-inf) = 0,
+    // results below 2^-126 flush to 0, far below the row's largest term, 1);
+    // m is -inf only while every row so far has been padding
+    const float mref = m == -INFINITY ? 0.f : m;
     float pr[4], psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pr[e] = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m);
+      pr[e] = __builtin_amdgcn_exp2f(z[e] - mref);
       psum += pr[e];
     }
     lsum += group4_sum(psum);  // this half's rows only; the halves are added at the end
