@@ -14,9 +14,10 @@
 // looked up through the block table once; the rows are then gathered in
 // chunks of 32 into LDS (the scattered reads become 1152-byte row reads,
 // "aggregating random small reads", "Optimizing Inference for Hybrid
-// Attention LLMs: Practices for Fast Adaptation", section 3, item 2), the
-// next chunk's loads in flight in registers while the current chunk is
-// computed (the same page's "overlapping gather and compute").  Each 16-head
+// Attention LLMs: Practices for Fast Adaptation", section 3, item 2): while
+// chunk c is computed from one LDS buffer, chunk c + 1 is written into the
+// other and chunk c + 2's loads are in flight in registers (the same page's
+// "overlapping gather and compute").  Each 16-head
 // tile has two waves: per chunk, each computes S^T = K Q^T for half of the
 // chunk's rows (16 rows x 16 heads, contraction 576) with MFMA, the two
 // exchange their row maxima and probabilities through LDS, and each
@@ -113,9 +114,8 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   constexpr int PPT = (kPieces + NT - 1) / NT;  // 16-byte pieces per thread per chunk
   constexpr int kHalfDims = kVDim / 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* krow = smem;
-  SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + kKrowBytes);
-  int* rowidx = reinterpret_cast<int*>(smem + kKrowBytes + sizeof(SfaXchg));  // pool row, -1 = none
+  SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + 2 * kKrowBytes);
+  int* rowidx = reinterpret_cast<int*>(smem + 2 * kKrowBytes + sizeof(SfaXchg));  // pool row, -1 = none
 
   // XCD-aware order: consecutive workgroups go to the eight XCDs in turn,
   // so the head groups of one (split, row) are given ids 8 apart and land on
@@ -172,21 +172,26 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
                        : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](unsigned char* kb) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int it = tid + j * NT;
       const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
-      if (it < kPieces) *reinterpret_cast<uint4*>(krow + r * kRowStride + part * 16) = va[j];
+      if (it < kPieces) *reinterpret_cast<uint4*>(kb + r * kRowStride + part * 16) = va[j];
     }
   };
 
-  if (nrows > 0) gather(0);
+  // two chunk buffers: chunk c is read from buffer c % 2 while chunk c + 1
+  // is written into the other (after this chunk's S^T, its loads having had
+  // a whole chunk to arrive) and chunk c + 2's loads are issued
+  if (nrows > 0) {
+    gather(0);
+    stage(smem);
+  }
+  if (nrows > kSfaRows) gather(kSfaRows);
   for (int c0 = 0; c0 < nrows; c0 += kSfaRows) {
-    __syncthreads();  // the previous chunk is no longer read
-    stage();
-    __syncthreads();
-    if (c0 + kSfaRows < nrows) gather(c0 + kSfaRows);  // in flight during this chunk's math
+    __syncthreads();  // chunk c is staged; the other buffer (chunk c - 1) is no longer read
+    const unsigned char* krow = smem + ((c0 / kSfaRows) & 1) * kKrowBytes;
 
     // S^T tile of this half: s[e] = S[head l16][row 16 half + 4g + e]; two
     // accumulators (even and odd contraction steps) halve the dependent chain
@@ -200,6 +205,10 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s2 + 1]), sb, 0, 0, 0);
     }
     sa += sb;
+    if (c0 + kSfaRows < nrows) {
+      stage(smem + (((c0 / kSfaRows) + 1) & 1) * kKrowBytes);
+      if (c0 + 2 * kSfaRows < nrows) gather(c0 + 2 * kSfaRows);
+    }
     float z[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] = rowidx[c0 + 16 * half + 4 * g + e] >= 0 ? sa[e] * zscale : -INFINITY;
@@ -485,7 +494,7 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   if (wgs * nw * 128 > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
   hipError_t e0;
-  const size_t lds = (size_t)kKrowBytes + sizeof(SfaXchg) +
+  const size_t lds = (size_t)2 * kKrowBytes + sizeof(SfaXchg) +
                      (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
   switch (nw) {
     case 1: e0 = launch_sfa<1>(grid, lds, s, p); break;
