@@ -7,10 +7,13 @@
 // fp8 route: q_h . k_t = (q̂_h . k̂_t) * sq_h * sk_t with positive scales, so
 // sq_h is folded into w_h and sk_t applied after the head sum.
 //
-// bf16/fp8 keys use MFMA 16x16x32: logits D[m = head][n = position] with the
-// query rows as A (from LDS) and the keys as B, loaded straight from the page
-// in HBM (each lane reads 8 consecutive elements of one key row).  fp32 keys
-// use VALU, one thread per position.
+// bf16/fp8 keys use MFMA: logits D[m = head][n = position] with the query
+// rows as A (from LDS) and the keys as B, loaded straight from the page in
+// HBM.  bf16 and 64-dim fp8 take 16x16x32 steps (each lane reads 8
+// consecutive elements of one key row); 128-dim fp8 takes one 16x16x128
+// step, gfx950's only fp8 MFMA that runs at twice the bf16 rate (a 16x16x32
+// fp8 MFMA takes as long as a bf16 one).  fp32 keys use VALU, one thread per
+// position.
 #pragma once
 
 #include <type_traits>
@@ -29,12 +32,26 @@ __device__ __forceinline__ float relu_keep_nan(float v) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, v), 0));
 }
 
-__device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
+// 32 fp8 elements per lane: the operand of one 16x16x128 step.
+struct Frag8 {
+  uint4 lo, hi;
+};
+
+// One contraction step of a 16x16 tile: D = A B + C.
+__device__ __forceinline__ f32x4 mfma_step(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_16x16x32(uint2 a, uint2 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_step(uint2 a, uint2 b, f32x4 c) {
   long la = __builtin_bit_cast(long, a), lb = __builtin_bit_cast(long, b);
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(la, lb, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_step(const Frag8& a, const Frag8& b, f32x4 c) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i va = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w, (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
+  const v8i vb = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w, (int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w};
+  // formats 0, 0: both operands fp8 e4m3; zero scale operands select the
+  // unscaled instruction (v_mfma_f32_16x16x128_f8f6f4)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Storage geometry of one indexer variant: DT 0 = fp32, 1 = bf16, 2 = fp8.
@@ -42,16 +59,27 @@ template <int DT, int D>
 struct IdxGeom {
   static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);   // bytes per element
   static constexpr int QSTRIDE = DT == 0 ? D * 4 : D * ES + 16;  // LDS bytes per (row, head)
-  using frag_t = typename std::conditional<DT == 1, uint4, uint2>::type;
+  static constexpr bool K128 = DT == 2 && D == 128;             // one 16x16x128 fp8 step
+  static constexpr int KS = K128 ? 1 : D / 32;                  // contraction steps
+  using frag_t = typename std::conditional<K128, Frag8, typename std::conditional<DT == 1, uint4, uint2>::type>::type;
   // Byte offset, within a row of D elements, of the 8 elements lane group g
   // feeds to the MFMA at contraction step ks.  Any assignment of the row's
   // elements to (ks, g) gives the same dot product as long as the query and
   // key fragments use the same one; bf16 takes elements 32 ks + 8g .. + 8.
   // fp8 pairs the steps so that lane group g reads 16 contiguous bytes at
   // 16g + 64 j (steps 2j and 2j + 1): each load instruction then covers 64
-  // contiguous bytes of every key row instead of 32.
+  // contiguous bytes of every key row instead of 32.  The 16x16x128 step
+  // takes the same 32 bytes per lane group at once (16g .. and 64 + 16g ..).
   static __host__ __device__ constexpr int frag_byte(int ks, int g) {
     return DT == 2 ? 16 * g + 8 * (ks & 1) + 64 * (ks >> 1) : (32 * ks + 8 * g) * ES;
+  }
+  // The fragment of contraction step ks for lane group g of the row at `row`.
+  static __device__ __forceinline__ frag_t load_frag(const unsigned char* row, int ks, int g) {
+    if constexpr (K128) {
+      return Frag8{*reinterpret_cast<const uint4*>(row + 16 * g), *reinterpret_cast<const uint4*>(row + 64 + 16 * g)};
+    } else {
+      return *reinterpret_cast<const frag_t*>(row + frag_byte(ks, g));
+    }
   }
 };
 
@@ -96,7 +124,7 @@ __device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, cons
 // fp8 scale (1 otherwise).
 template <int DT, int D, int NPT>
 struct KeyTiles {
-  typename IdxGeom<DT, D>::frag_t kf[NPT][D / 32];
+  typename IdxGeom<DT, D>::frag_t kf[NPT][IdxGeom<DT, D>::KS];
   float kscale[NPT];
 };
 
@@ -104,14 +132,11 @@ template <int DT, int D, int NPT>
 __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const unsigned char* kpage,
                                                const float* kscale_page, int slot0) {
   using G = IdxGeom<DT, D>;
-  using frag_t = typename G::frag_t;
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      t.kf[pt][ks] =
-          *reinterpret_cast<const frag_t*>(kpage + (slot0 + pt * 16 + l16) * D * G::ES + G::frag_byte(ks, g));
+    for (int ks = 0; ks < G::KS; ++ks) t.kf[pt][ks] = G::load_frag(kpage + (slot0 + pt * 16 + l16) * D * G::ES, ks, g);
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt) t.kscale[pt] = (DT == 2) ? kscale_page[slot0 + pt * 16 + l16] : 1.f;
 }
@@ -127,8 +152,7 @@ template <int DT, int D, int NPT, int NR = 0, int MT = 0, class Emit>
 __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
                                                 const KeyTiles<DT, D, NPT>& t, int slot0, Emit&& emit) {
   using G = IdxGeom<DT, D>;
-  using frag_t = typename G::frag_t;
-  constexpr int KS = D / 32;  // contraction steps
+  constexpr int KS = G::KS;  // contraction steps
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int hp = MT > 0 ? 16 * MT : Hpad;
   auto head_tile = [&](int r, int ht, float (&sacc)[NPT]) {
@@ -138,9 +162,9 @@ __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const f
     const unsigned char* qrow = qs + (r * hp + ht * 16 + l16) * G::QSTRIDE;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const frag_t a = *reinterpret_cast<const frag_t*>(qrow + G::frag_byte(ks, g));
+      const typename G::frag_t a = G::load_frag(qrow, ks, g);
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_16x16x32(a, t.kf[pt][ks], acc[pt]);
+      for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_step(a, t.kf[pt][ks], acc[pt]);
     }
     // acc[pt][i] = logit of head ht*16 + 4g + i at slot slot0 + pt*16 + l16
     const float* wr = wsm + r * hp + ht * 16 + 4 * g;

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   using Gm = IdxGeom<DT, D>;
   using frag_t = typename Gm::frag_t;
   constexpr int ES = Gm::ES;
-  constexpr int KS = D / 32;                     // contraction steps
+  constexpr int KS = Gm::KS;                     // contraction steps
   constexpr int MT = kPfHeads / 16;              // head tiles
   constexpr int NSUB = kPfTile / kPfSub;         // sub-tiles per tile
   constexpr int KROW = D * ES + 16;              // padded LDS bytes per key row
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
 
   for (int c = tid; c < kPfRows * kHistBins; c += kPfThreads) lhist[c] = 0u;
 
-  // this wave's query row as A fragments: qf[mt][ks] = q[row][mt*16 + l16] at byte frag_byte(ks, g)
+  // this wave's query row as A fragments: qf[mt][ks] = step ks of q[row][mt*16 + l16] for lane group g
   frag_t qf[MT][KS];
   float wl[MT][4];  // weights of heads mt*16 + 4g + i (times the q scale for fp8)
   {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         frag_t v{};
         if (row_ok && h < p.H)
-          v = *reinterpret_cast<const frag_t*>(qg + ((int64_t)row * p.H + h) * (D * ES) + Gm::frag_byte(ks, g));
+          v = Gm::load_frag(qg + ((int64_t)row * p.H + h) * (D * ES), ks, g);
         qf[mt][ks] = v;
       }
 #pragma unroll
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   auto load_b = [&](frag_t (&bf)[2], int sub, int ks) {
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
-      bf[pt] = *reinterpret_cast<const frag_t*>(ktile + (sub * kPfSub + pt * 16 + l16) * KROW + Gm::frag_byte(ks, g));
+      bf[pt] = Gm::load_frag(ktile + (sub * kPfSub + pt * 16 + l16) * KROW, ks, g);
   };
   // The MFMAs of one sub-tile.  bf holds its first step's fragments on entry;
   // every step loads the next step's fragments (the next sub-tile's first one
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) a[mt][pt] = mfma_16x16x32(qf[mt][ks], cur[pt], a[mt][pt]);
+        for (int pt = 0; pt < 2; ++pt) a[mt][pt] = mfma_step(qf[mt][ks], cur[pt], a[mt][pt]);
     }
     // the scale of the position this lane ends up holding (lanes g < 2)
     if (DT == 2) kscale = ksc[sub * kPfSub + (g & 1) * 16 + l16];
