@@ -13,11 +13,14 @@
 // A workgroup owns 8 query rows of one request, one per wave.  A wave keeps
 // its row's whole query (64 heads x D) in registers as the MFMA A operand and
 // walks the request's positions in tiles of 128, which the eight waves share
-// through LDS (the next tile's keys are in flight in registers while the
-// current one is used, and its block-table entries one tile further ahead).
+// through two LDS buffers: while tile t is used, tile t + 1 is written into
+// the other buffer (after t's first sub-tile; one barrier per tile), tile
+// t + 2's keys are in flight in registers and their block-table entries one
+// tile further ahead.
 //
 // Within a tile a wave takes 32 positions at a time: 64 heads x 32 positions
-// x D as 16x16x32 MFMAs into 4 x 2 accumulator tiles, with the key fragments
+// x D as MFMAs (one 16x16x128 step for 128-dim fp8, else 16x16x32 steps)
+// into 4 x 2 accumulator tiles, with the key fragments
 // of each contraction step read from LDS one step ahead.  The epilogue of a
 // sub-tile (ReLU, weights, the 64-head sum, the store) is issued together
 // with the MFMAs of the next one, on a second accumulator set, so the vector
@@ -73,9 +76,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   constexpr int VPT = TILE_BYTES / 16 / kPfThreads;  // 16-byte loads per thread per tile
   static_assert(NSUB % 2 == 0, "sub-tiles alternate between two accumulator sets");
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* ktile = smem;                                              // [kPfTile][KROW]
-  float* ksc = reinterpret_cast<float*>(smem + kPfTile * KROW);             // [kPfTile] fp8 scales
-  uint32_t* lhist = reinterpret_cast<uint32_t*>(ksc + kPfTile);             // [kPfRows][kHistBins]
+  // two key tiles: tile t is read from buffer t % 2 while tile t + 1 is
+  // written into the other
+  unsigned char* const kbuf = smem;                                         // [2][kPfTile][KROW]
+  float* const kscb = reinterpret_cast<float*>(smem + 2 * kPfTile * KROW);  // [2][kPfTile] fp8 scales
+  uint32_t* lhist = reinterpret_cast<uint32_t*>(kscb + 2 * kPfTile);        // [kPfRows][kHistBins]
+  const unsigned char* ktile = kbuf;                                        // the tile being read
+  const float* ksc = kscb;
 
   const int b = blockIdx.y;
   const int q0 = p.q_offsets[b], nb = p.q_offsets[b + 1] - q0;
@@ -157,15 +164,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
       pre_s = phys >= 0 ? p.k_scale[(int64_t)phys * kPage + (tid & 63)] : 0.f;
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
+    unsigned char* kt = kbuf + buf * kPfTile * KROW;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int c = tid + j * kPfThreads;
       const int pos = c / PPR;
       const int part = c - pos * PPR;
-      *reinterpret_cast<uint4*>(ktile + pos * KROW + part * 16) = pre[j];
+      *reinterpret_cast<uint4*>(kt + pos * KROW + part * 16) = pre[j];
     }
-    if (DT == 2 && tid < kPfTile) ksc[tid] = pre_s;
+    if (DT == 2 && tid < kPfTile) kscb[buf * kPfTile + tid] = pre_s;
   };
 
   // Two accumulator sets: the MFMAs of a sub-tile go to one while the
@@ -239,17 +247,34 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
 
   int ph_next[PAGES];
   load_phys(0, ph_next);
-  if (ntiles > 0) fetch(ph_next);
+  if (ntiles > 0) {
+    fetch(ph_next);
+    stage(0);
+  }
   load_phys(1, ph_next);
+  if (ntiles > 1) {
+    fetch(ph_next);
+    load_phys(2, ph_next);
+  }
   for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();  // the previous tile is no longer read
-    stage();
-    __syncthreads();
-    if (tile + 1 < ntiles) {
-      fetch(ph_next);
-      load_phys(tile + 2, ph_next);
+    __syncthreads();  // tile is staged; the other buffer (tile - 1) is no longer read
+    ktile = kbuf + (tile & 1) * kPfTile * KROW;
+    ksc = kscb + (tile & 1) * kPfTile;
+    // tile + 1 goes into the other buffer after this tile's first sub-tile
+    // (its loads have had a whole tile to arrive), and tile + 2's loads start
+    auto next_tile = [&]() {
+      if (tile + 1 < ntiles) {
+        stage((tile + 1) & 1);
+        if (tile + 2 < ntiles) {
+          fetch(ph_next);
+          load_phys(tile + 3, ph_next);
+        }
+      }
+    };
+    if (tile * kPfTile >= myvis) {  // (also every wave without a row)
+      next_tile();
+      continue;
     }
-    if (tile * kPfTile >= myvis) continue;  // (also every wave without a row)
     frag_t bf[2];
     load_b(bf, 0, 0);
 #pragma unroll
@@ -258,6 +283,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
       // the previous sub-tile (the last one of the previous tile when sub == 0)
       const int prev_pos = sub == 0 ? pending : tile * kPfTile + (sub - 1) * kPfSub;
       mfma_sub(acc[cur], sc_k[cur], sub, bf);
+      if (sub == 0) next_tile();  // (before this sub-tile's score stores, which it would wait for)
       const float s = epilogue(acc[cur ^ 1], sc_k[cur ^ 1]);
       if (prev_pos >= 0) emit(s, prev_pos + (g & 1) * 16 + l16);
     }
@@ -280,7 +306,7 @@ using namespace dsa;
 template <int DT, int D>
 static hipError_t launch_prefill(const PrefillParams& p, dim3 grid, hipStream_t s) {
   using Gm = IdxGeom<DT, D>;
-  const size_t lds = (size_t)kPfTile * (D * Gm::ES + 16) + kPfTile * 4 + (size_t)kPfRows * kHistBins * 4;
+  const size_t lds = 2 * ((size_t)kPfTile * (D * Gm::ES + 16) + kPfTile * 4) + (size_t)kPfRows * kHistBins * 4;
   {
     const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(li_prefill<DT, D>), lds);
     if (e != hipSuccess) return e;
