@@ -92,11 +92,11 @@ IndexerPlan plan_indexer(const dsa_paged_t* pg) {
 // head count.  A workgroup of 4 tiles shares each gathered row among 64
 // heads, which decides throughput once the batch fills the chip; when the
 // whole batch is at most 8 tiles (one 128-head row), the step is latency-bound
-// and 2-tile workgroups finish their chunks sooner (measured at the 32K
-// single-row decode: 18.8 us against 21.6 us with 4 tiles).
+// and 1-tile workgroups finish their chunks sooner (measured at the 32K
+// single-row decode: 18.3 us against 18.6 with 2 tiles and 21.6 with 4).
 int sfa_waves(int n_heads, int64_t num_rows) {
   const int hq = n_heads / 16;
-  const int cap = num_rows * hq <= 8 ? 2 : 4;
+  const int cap = num_rows * hq <= 8 ? 1 : 4;
   for (int nw = cap; nw > 1; --nw)
     if (hq % nw == 0) return nw;
   return 1;
