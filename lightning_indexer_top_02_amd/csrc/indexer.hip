@@ -16,14 +16,7 @@
 // It writes fp32 scores and a per-row histogram of the top 11 key bits (LDS,
 // then one global atomic per non-empty bin): the first radix level.
 //
-// Selection runs over segments of each row (topk_seg.hip); li_topk takes the
-// rows whose boundary bin holds too many keys for that (heavy ties).
-// li_topk: one 1024-thread workgroup per query row.  It finds the bin holding
-// the K-th largest key, gathers that bin's keys into LDS, resolves the exact
-// K-th key with two more radix levels, then makes one ordered pass keeping
-// every larger key and the lowest-position keys equal to the K-th (the tie
-// rule), writing positions in ascending order.  It zeroes its histogram row
-// on the way out, so the workspace stays ready for the next call.
+// Selection runs over segments of each row (topk_seg.hip).
 #include <algorithm>
 
 #include "dsa_device.h"
@@ -224,189 +217,6 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
   leave();
 }
 
-// ---------------------------------------------------------------------------
-// Selection
-// ---------------------------------------------------------------------------
-constexpr int kTopkThreads = 1024;
-constexpr int kCandCap = 12288;
-constexpr int kItems = 4;  // consecutive positions per thread per pass
-
-struct TopkParams {
-  const int32_t* q_offsets;
-  const int32_t* ctx_lens;
-  int batch;
-  const float* scores;
-  int64_t score_stride;
-  uint32_t* hist;
-  int K;
-  int32_t* out;
-  int only_flagged;  // handle only the rows the segment kernels left (flag word set)
-};
-
-struct TopkShared {
-  uint32_t bins[kHistBins];
-  uint32_t cand[kCandCap];
-  alignas(16) int wsum[kTopkThreads / 64];
-  int ncand;
-  int res_bin, res_above;
-};
-
-__device__ __forceinline__ void load_keys(const float* row, int t0, int vis, uint32_t key[kItems],
-                                          bool valid[kItems]) {
-  if (t0 + kItems <= vis) {
-    const float4 v = *reinterpret_cast<const float4*>(row + t0);
-    key[0] = score_key(v.x); key[1] = score_key(v.y); key[2] = score_key(v.z); key[3] = score_key(v.w);
-#pragma unroll
-    for (int e = 0; e < kItems; ++e) valid[e] = true;
-  } else {
-#pragma unroll
-    for (int e = 0; e < kItems; ++e) {
-      valid[e] = (t0 + e) < vis;
-      key[e] = valid[e] ? score_key(row[t0 + e]) : 0u;
-    }
-  }
-}
-
-// Wave 0 finds the bin; the result is broadcast through LDS.
-__device__ __forceinline__ void kth_bin_block(TopkShared& sh, int nbins, int k) {
-  if (threadIdx.x < 64) {
-    int bin, above;
-    kth_bin_wave(sh.bins, nbins, k, bin, above);
-    if (threadIdx.x == 0) {
-      sh.res_bin = bin;
-      sh.res_above = above;
-    }
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kTopkThreads) void li_topk(TopkParams p) {
-  __shared__ TopkShared sh;
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int b = request_of_row(p.q_offsets, p.batch, i);
-  const int nb = p.q_offsets[b + 1] - p.q_offsets[b];
-  const int vis = p.ctx_lens[b] - nb + (i - p.q_offsets[b]) + 1;
-  const int K = p.K;
-  int32_t* out = p.out + (int64_t)i * K;
-  uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
-  if (p.only_flagged && (vis <= K || hrow[kHistStride - 1] != 1u)) return;
-  if (vis <= K) {  // everything visible is kept
-    for (int t = tid; t < K; t += kTopkThreads) out[t] = t < vis ? t : -1;
-    for (int c = tid; c < kHistBins; c += kTopkThreads) hrow[c] = 0u;
-    return;
-  }
-  const float* row = p.scores + (int64_t)i * p.score_stride;
-
-  // level 1 from the scoring kernel's histogram, which is then cleared
-  for (int c = tid; c < kHistBins; c += kTopkThreads) {
-    sh.bins[c] = hrow[c];
-    hrow[c] = 0u;
-  }
-  if (tid == 0) sh.ncand = 0;
-  __syncthreads();
-  kth_bin_block(sh, kHistBins, K);
-  const uint32_t bin1 = sh.res_bin;
-  int need = K - sh.res_above;  // keys still needed from bin1 (>= 1)
-  const bool in_lds = sh.bins[bin1] <= (uint32_t)kCandCap;
-  __syncthreads();
-
-  // gather bin1's keys (low 21 bits) into LDS when they fit
-  if (in_lds) {
-    for (int t0 = tid * kItems; t0 < vis; t0 += kTopkThreads * kItems) {
-      uint32_t key[kItems];
-      bool valid[kItems];
-      load_keys(row, t0, vis, key, valid);
-#pragma unroll
-      for (int e = 0; e < kItems; ++e) {
-        const bool pred = valid[e] && (key[e] >> 21) == bin1;
-        const uint64_t m = __ballot(pred);
-        const int n = __popcll(m);
-        int base = 0;
-        if (n) {
-          if (lane == 0) base = atomicAdd(&sh.ncand, n);
-          base = wave_read_lane(base, 0);  // lane 0 is active whenever any lane is
-        }
-        const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
-        if (pred && slot < kCandCap) sh.cand[slot] = key[e] & 0x1fffffu;
-      }
-    }
-    __syncthreads();
-  }
-  const int ncand = in_lds ? min(sh.ncand, kCandCap) : 0;
-
-  // levels 2 (key bits 20..10) and 3 (bits 9..0) over bin1's keys
-  uint32_t prefix = bin1;  // known high bits of the K-th key
-  for (int level = 1; level < 3; ++level) {
-    const int nbins = kLevelBins[level];
-    const int shift = kLevelShift[level];
-    for (int c = tid; c < nbins; c += kTopkThreads) sh.bins[c] = 0u;
-    __syncthreads();
-    if (in_lds) {
-      for (int c = tid; c < ncand; c += kTopkThreads) {
-        const uint32_t low = sh.cand[c];
-        if (level == 1 || (low >> 10) == (prefix & 2047u)) atomicAdd(&sh.bins[(low >> shift) & (nbins - 1)], 1u);
-      }
-    } else {
-      for (int t0 = tid * kItems; t0 < vis; t0 += kTopkThreads * kItems) {
-        uint32_t key[kItems];
-        bool valid[kItems];
-        load_keys(row, t0, vis, key, valid);
-#pragma unroll
-        for (int e = 0; e < kItems; ++e) {
-          const bool hit = valid[e] && (key[e] >> kLevelShift[level - 1]) == prefix;
-          if (hit) atomicAdd(&sh.bins[(key[e] >> shift) & (nbins - 1)], 1u);
-        }
-      }
-    }
-    __syncthreads();
-    kth_bin_block(sh, nbins, need);
-    prefix = (prefix << (level == 1 ? 11 : 10)) | (uint32_t)sh.res_bin;
-    need -= sh.res_above;
-    __syncthreads();
-  }
-  const uint32_t kth = prefix;  // the K-th largest key; `need` keys equal to it are kept
-
-  // ordered pass: keep keys > kth and the first `need` keys == kth (lowest positions)
-  int eq_run = 0, written = 0;
-  for (int base = 0; base < vis && written < K; base += kTopkThreads * kItems) {
-    const int t0 = base + tid * kItems;
-    uint32_t key[kItems];
-    bool valid[kItems];
-    if (t0 < vis) {
-      load_keys(row, t0, vis, key, valid);
-    } else {
-#pragma unroll
-      for (int e = 0; e < kItems; ++e) {
-        valid[e] = false;
-        key[e] = 0u;
-      }
-    }
-    int neq = 0;
-#pragma unroll
-    for (int e = 0; e < kItems; ++e) neq += (valid[e] && key[e] == kth);
-    int eq_total;
-    int eq_before = block_excl_scan<kTopkThreads>(neq, eq_total, sh.wsum) + eq_run;
-    bool sel[kItems];
-    int nsel = 0;
-#pragma unroll
-    for (int e = 0; e < kItems; ++e) {
-      const bool is_eq = valid[e] && key[e] == kth;
-      sel[e] = (valid[e] && key[e] > kth) || (is_eq && eq_before < need);
-      eq_before += is_eq;
-      nsel += sel[e];
-    }
-    int sel_total;
-    int pos = block_excl_scan<kTopkThreads>(nsel, sel_total, sh.wsum) + written;
-#pragma unroll
-    for (int e = 0; e < kItems; ++e)
-      if (sel[e] && pos < K) out[pos++] = t0 + e;
-    eq_run += eq_total;
-    written += sel_total;
-  }
-  for (int t = written + tid; t < K; t += kTopkThreads) out[t] = -1;  // only on inconsistent input
-}
-
 }  // namespace dsa
 
 using namespace dsa;
@@ -468,19 +278,5 @@ hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s)
   hipError_t e = dsa_launch_indexer_scores(a, s);
   if (e != hipSuccess) return e;
 
-  e = dsa_launch_topk_segments(a, s);
-  if (e != hipSuccess) return e;
-  // rows whose boundary bin overflowed the candidate list
-  TopkParams tp;
-  tp.q_offsets = a.q_offsets;
-  tp.ctx_lens = a.ctx_lens;
-  tp.batch = a.batch;
-  tp.scores = a.scores;
-  tp.score_stride = a.score_stride;
-  tp.hist = a.hist;
-  tp.K = a.topk;
-  tp.out = a.out_idx;
-  tp.only_flagged = 1;
-  hipLaunchKernelGGL(li_topk, dim3(a.num_rows), dim3(kTopkThreads), 0, s, tp);
-  return hipGetLastError();
+  return dsa_launch_topk_segments(a, s);
 }

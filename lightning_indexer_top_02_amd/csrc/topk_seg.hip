@@ -24,10 +24,10 @@
 //   li_seg_write   (a workgroup per segment): writes the kept positions of
 //                  its segment at its offset, in order.
 // A row whose boundary bin holds more keys than the candidate list can take
-// (heavy ties) is flagged and left to li_topk, which scans the row in one
-// workgroup.  The per-row state lives in the unused tail of the row's
-// histogram block; the histogram and the candidate counter are zero again
-// when the three kernels are done.
+// (heavy ties) is flagged and selected whole by li_seg_resolve's workgroup
+// (select_whole_row), and li_seg_write leaves it alone.  The per-row state
+// lives in the unused tail of the row's histogram block; the histogram and
+// the candidate counter are zero again when the three kernels are done.
 #include <algorithm>
 
 #include "dsa_device.h"
@@ -171,6 +171,170 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One-workgroup selection of a whole row
+// ---------------------------------------------------------------------------
+constexpr int kTopkThreads = 1024;
+constexpr int kCandCap = 12288;
+constexpr int kItems = 4;  // consecutive positions per thread per pass
+
+struct TopkShared {
+  uint32_t bins[kHistBins];
+  uint32_t cand[kCandCap];
+  alignas(16) int wsum[kTopkThreads / 64];
+  int ncand;
+  int res_bin, res_above;
+};
+
+__device__ __forceinline__ void load_keys(const float* row, int t0, int vis, uint32_t key[kItems],
+                                          bool valid[kItems]) {
+  if (t0 + kItems <= vis) {
+    const float4 v = *reinterpret_cast<const float4*>(row + t0);
+    key[0] = score_key(v.x); key[1] = score_key(v.y); key[2] = score_key(v.z); key[3] = score_key(v.w);
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) valid[e] = true;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) {
+      valid[e] = (t0 + e) < vis;
+      key[e] = valid[e] ? score_key(row[t0 + e]) : 0u;
+    }
+  }
+}
+
+// Wave 0 finds the bin; the result is broadcast through LDS.
+__device__ __forceinline__ void kth_bin_block(TopkShared& sh, int nbins, int k) {
+  if (threadIdx.x < 64) {
+    int bin, above;
+    kth_bin_wave(sh.bins, nbins, k, bin, above);
+    if (threadIdx.x == 0) {
+      sh.res_bin = bin;
+      sh.res_above = above;
+    }
+  }
+  __syncthreads();
+}
+
+// The whole row in one 1024-thread workgroup (rows whose boundary bin holds
+// more keys than the candidate list takes: heavy ties).  It finds the bin
+// holding the K-th largest key from the row's histogram, gathers that bin's
+// keys into LDS when they fit, resolves the exact K-th key with two more
+// radix levels, then makes one ordered pass keeping every larger key and the
+// lowest-position keys equal to the K-th (the tie rule), writing positions
+// in ascending order.  It zeroes the row's level-1 bins on the way out.
+__device__ void select_whole_row(const float* row, int vis, int K, int32_t* out, uint32_t* hrow,
+                                 TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63;
+
+  // level 1 from the scoring kernel's histogram, which is then cleared
+  for (int c = tid; c < kHistBins; c += kTopkThreads) {
+    sh.bins[c] = hrow[c];
+    hrow[c] = 0u;
+  }
+  if (tid == 0) sh.ncand = 0;
+  __syncthreads();
+  kth_bin_block(sh, kHistBins, K);
+  const uint32_t bin1 = sh.res_bin;
+  int need = K - sh.res_above;  // keys still needed from bin1 (>= 1)
+  const bool in_lds = sh.bins[bin1] <= (uint32_t)kCandCap;
+  __syncthreads();
+
+  // gather bin1's keys (low 21 bits) into LDS when they fit
+  if (in_lds) {
+    for (int t0 = tid * kItems; t0 < vis; t0 += kTopkThreads * kItems) {
+      uint32_t key[kItems];
+      bool valid[kItems];
+      load_keys(row, t0, vis, key, valid);
+#pragma unroll
+      for (int e = 0; e < kItems; ++e) {
+        const bool pred = valid[e] && (key[e] >> 21) == bin1;
+        const uint64_t m = __ballot(pred);
+        const int n = __popcll(m);
+        int base = 0;
+        if (n) {
+          if (lane == 0) base = atomicAdd(&sh.ncand, n);
+          base = wave_read_lane(base, 0);  // lane 0 is active whenever any lane is
+        }
+        const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (pred && slot < kCandCap) sh.cand[slot] = key[e] & 0x1fffffu;
+      }
+    }
+    __syncthreads();
+  }
+  const int ncand = in_lds ? min(sh.ncand, kCandCap) : 0;
+
+  // levels 2 (key bits 20..10) and 3 (bits 9..0) over bin1's keys
+  uint32_t prefix = bin1;  // known high bits of the K-th key
+  for (int level = 1; level < 3; ++level) {
+    const int nbins = kLevelBins[level];
+    const int shift = kLevelShift[level];
+    for (int c = tid; c < nbins; c += kTopkThreads) sh.bins[c] = 0u;
+    __syncthreads();
+    if (in_lds) {
+      for (int c = tid; c < ncand; c += kTopkThreads) {
+        const uint32_t low = sh.cand[c];
+        if (level == 1 || (low >> 10) == (prefix & 2047u)) atomicAdd(&sh.bins[(low >> shift) & (nbins - 1)], 1u);
+      }
+    } else {
+      for (int t0 = tid * kItems; t0 < vis; t0 += kTopkThreads * kItems) {
+        uint32_t key[kItems];
+        bool valid[kItems];
+        load_keys(row, t0, vis, key, valid);
+#pragma unroll
+        for (int e = 0; e < kItems; ++e) {
+          const bool hit = valid[e] && (key[e] >> kLevelShift[level - 1]) == prefix;
+          if (hit) atomicAdd(&sh.bins[(key[e] >> shift) & (nbins - 1)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    kth_bin_block(sh, nbins, need);
+    prefix = (prefix << (level == 1 ? 11 : 10)) | (uint32_t)sh.res_bin;
+    need -= sh.res_above;
+    __syncthreads();
+  }
+  const uint32_t kth = prefix;  // the K-th largest key; `need` keys equal to it are kept
+
+  // ordered pass: keep keys > kth and the first `need` keys == kth (lowest positions)
+  int eq_run = 0, written = 0;
+  for (int base = 0; base < vis && written < K; base += kTopkThreads * kItems) {
+    const int t0 = base + tid * kItems;
+    uint32_t key[kItems];
+    bool valid[kItems];
+    if (t0 < vis) {
+      load_keys(row, t0, vis, key, valid);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kItems; ++e) {
+        valid[e] = false;
+        key[e] = 0u;
+      }
+    }
+    int neq = 0;
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) neq += (valid[e] && key[e] == kth);
+    int eq_total;
+    int eq_before = block_excl_scan<kTopkThreads>(neq, eq_total, sh.wsum) + eq_run;
+    bool sel[kItems];
+    int nsel = 0;
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) {
+      const bool is_eq = valid[e] && key[e] == kth;
+      sel[e] = (valid[e] && key[e] > kth) || (is_eq && eq_before < need);
+      eq_before += is_eq;
+      nsel += sel[e];
+    }
+    int sel_total;
+    int pos = block_excl_scan<kTopkThreads>(nsel, sel_total, sh.wsum) + written;
+#pragma unroll
+    for (int e = 0; e < kItems; ++e)
+      if (sel[e] && pos < K) out[pos++] = t0 + e;
+    eq_run += eq_total;
+    written += sel_total;
+  }
+  for (int t = written + tid; t < K; t += kTopkThreads) out[t] = -1;  // only on inconsistent input
+}
+
 struct ResolveShared {
   uint32_t bins[kHistBins];
   uint32_t segc[kMaxSegs];
@@ -196,7 +360,12 @@ __device__ __forceinline__ void resolve_kth(ResolveShared& sh, int k, int& bin, 
 }
 
 __global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
-  __shared__ ResolveShared sh;
+  static_assert(kResolveThreads == kTopkThreads, "flagged rows are selected by the same workgroup");
+  __shared__ union {
+    ResolveShared r;
+    TopkShared t;
+  } shu;
+  ResolveShared& sh = shu.r;
   const int i = blockIdx.x, tid = threadIdx.x;
   const int vis = visible_of(p, i);
   uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
@@ -211,8 +380,9 @@ __global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
   resolve_kth<32>(sh, K, bin1, above);
   const int ncand = (int)sh.bins[bin1];
   __syncthreads();  // every thread has read it before the bins are reused
-  if (ncand > p.cand_cap) {  // left to li_topk, which also clears the histogram
-    if (tid == 0) hrow[kStateFlags] = 1u;
+  if (ncand > p.cand_cap) {  // the whole row here, in this workgroup (clears the bins)
+    if (tid == 0) hrow[kStateFlags] = 1u;  // (li_seg_write skips the row)
+    select_whole_row(p.scores + (int64_t)i * p.score_stride, vis, K, p.out + (int64_t)i * K, hrow, shu.t);
     return;
   }
   int need = K - above;  // keys still needed from bin1 (>= 1)
@@ -320,7 +490,7 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   if (s0 >= vis) return;
   // the segment's scores are in flight while the row's state is read
   fetch_seg_scores(p.scores + (int64_t)i * p.score_stride, s0, vis, buf);
-  if (hrow[kStateFlags] & 1u) return;  // (uniform) the row is left to li_topk
+  if (hrow[kStateFlags] & 1u) return;  // (uniform) the row was selected whole by li_seg_resolve
   const uint32_t kth = hrow[kStateKth];
   const int limit = (int)hrow[kStateLimit];
   const int off = (int)hrow[kSegBase + seg];
@@ -353,7 +523,7 @@ using namespace dsa;
 int dsa_seg_max_segments() { return kMaxSegs; }
 int dsa_seg_cand_cap(int max_ctx_len) { return std::min((max_ctx_len + 255) / 256 * 256, 8192); }
 
-// The three segment kernels; rows they leave flagged go to li_topk (run by the caller).
+// The three segment kernels (flagged rows are selected inside li_seg_resolve).
 hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s) {
   SegParams p;
   p.q_offsets = a.q_offsets;

@@ -246,6 +246,29 @@ def test_causal_planted_future_keys_never_selected():
         assert {t for t in range(2997, 3000) if t <= pos} <= row
 
 
+def test_all_ties_keep_the_lowest_positions():
+    """Every key equal: each row's scores tie, its boundary bin holds all its
+    positions (more than the segmented selection's candidate list, so the
+    two-pass route selects those rows whole in one workgroup), and the tie
+    rule keeps positions 0 .. K-1 on every route."""
+    import dataclasses
+    case = inputs.decode_32k(ctx_lens=[20000, 9000], n_q=[1, 3], topk=2048, exact=True)
+    ones = torch.ones(case.k_cache.shape, dtype=torch.bfloat16)
+    k = ones if case.k_cache.dtype == torch.bfloat16 else ones.view(case.k_cache.dtype)
+    case = parity.to_device(dataclasses.replace(case, k_cache=k.contiguous()))
+    qo, lens = case.q_offsets.cpu().numpy(), case.ctx_lens.cpu().numpy()
+    K = case.topk
+    for name, flags in {"default": 0, "two_pass": parity.dsa.INDEXER_TWO_PASS}.items():
+        idx = parity.gpu_indexer_topk(case, flags=flags).cpu().numpy()
+        for b in range(len(lens)):
+            n = qo[b + 1] - qo[b]
+            for j in range(n):
+                vis = lens[b] - n + j + 1
+                want = np.where(np.arange(K) < vis, np.arange(K), -1)
+                assert np.array_equal(idx[qo[b] + j], want), f"{name}: request {b} row {j}"
+        print(f"[ok] all ties, {name} route", flush=True)
+
+
 # --- sparse attention alone, on the oracle's indices ---------------------------
 def test_sfa_on_oracle_indices_with_padding():
     case = parity.to_device(inputs.decode_32k(ctx_lens=[9000, 1500, 200], n_q=[1, 2, 1], topk=1024))
