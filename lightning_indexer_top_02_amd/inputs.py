@@ -33,7 +33,7 @@ QK_DIM = 576  # 512 latent + 64 rope
 V_DIM = 512
 FP8_MAX = 448.0
 
-DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3}
 
 
 @dataclasses.dataclass
@@ -59,7 +59,7 @@ class Case:
     q_scale: Optional[torch.Tensor]  # float32 [T][H_I] (fp8 only)
     weights: torch.Tensor  # float32 [T][H_I]
     k_cache: torch.Tensor  # [num_pages][64][D_I] raw storage
-    k_scale: Optional[torch.Tensor]  # float32 [num_pages][64] (fp8 only)
+    k_scale: Optional[torch.Tensor]  # fp8: float32 [num_pages][64]; mxfp8: uint8 E8M0 [num_pages][64][D_I/32]
     # sparse attention
     sfa_dtype: str
     n_heads_sfa: int
@@ -106,6 +106,22 @@ def quantize_e4m3_rows(x: torch.Tensor):
     scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
     codes = (x.float() / scale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
     return codes.view(torch.uint8), scale.squeeze(-1).contiguous()
+
+
+def quantize_mxfp8(x: torch.Tensor):
+    """Producer-side MXFP8 quantization along the last dim (OCP microscaling,
+    blocks of 32 elements): the block's shared exponent is
+    floor(log2(amax)) - 8 (8 = the largest e4m3 exponent), stored biased by
+    127 as an E8M0 byte; codes = saturating round-to-nearest-even e4m3 casts
+    of x / 2^exponent.  Blocks of zeros get exponent 0 (byte 127).  Returns
+    (uint8 codes [..., D], uint8 E8M0 bytes [..., D/32])."""
+    shp = x.shape
+    xb = x.float().reshape(*shp[:-1], shp[-1] // 32, 32)
+    amax = xb.abs().amax(dim=-1, keepdim=True)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 8, torch.zeros_like(amax))
+    e = e.clamp(-127, 127)
+    codes = (xb / torch.exp2(e)).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8).reshape(shp), (e.squeeze(-1) + 127).to(torch.uint8).contiguous()
 
 
 def _draw(gen, shape, device, dist: str, std: float = 1.0, exact: bool = False):
@@ -205,6 +221,16 @@ def make_case(
             q_idx, q_scale = quantize_e4m3_rows(q_val)
             k_cache, k_scale = quantize_e4m3_rows(k_val)
         k_scale = k_scale.clone()
+    elif idx_dtype == "mxfp8":
+        if exact:  # integer codes, unit block scales (E8M0 byte 127)
+            q_idx = q_val.to(torch.float8_e4m3fn).view(torch.uint8)
+            k_cache = k_val.to(torch.float8_e4m3fn).view(torch.uint8)
+            q_scale = torch.full((T, H, D // 32), 127, dtype=torch.uint8, device=device)
+            k_scale = torch.full((num_pages, page_size, D // 32), 127, dtype=torch.uint8, device=device)
+        else:
+            q_idx, q_scale = quantize_mxfp8(q_val)
+            k_cache, k_scale = quantize_mxfp8(k_val)
+        k_scale = k_scale.clone()
     else:
         q_idx, k_cache = _storage(q_val, idx_dtype), _storage(k_val, idx_dtype)
         q_scale = k_scale = None
@@ -222,7 +248,7 @@ def make_case(
     if n_decoy > 0:
         k_cache[poison_pages] = _nan_like_storage(idx_dtype, k_cache[poison_pages].shape, device)
         if k_scale is not None:
-            k_scale[poison_pages] = float("nan")
+            k_scale[poison_pages] = float("nan") if k_scale.dtype == torch.float32 else 255
         if kv_cache is not None:
             kv_cache[poison_pages] = _nan_like_storage(sfa_dtype, kv_cache[poison_pages].shape, device)
     for b in range(B):
@@ -231,7 +257,7 @@ def make_case(
             last = int(bt[b, pages_per_req[b] - 1])
             k_cache[last, tail:] = _nan_like_storage(idx_dtype, k_cache[last, tail:].shape, device)
             if k_scale is not None:
-                k_scale[last, tail:] = float("nan")
+                k_scale[last, tail:] = float("nan") if k_scale.dtype == torch.float32 else 255
             if kv_cache is not None:
                 kv_cache[last, tail:] = _nan_like_storage(sfa_dtype, kv_cache[last, tail:].shape, device)
 

@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     build,
     decode_bf16,
     decode_e4m3,
+    decode_e8m0,
     visible,
     scores,
     select,

@@ -51,14 +51,33 @@ double dsa_oracle_decode_e4m3(uint8_t code)
     return sign ? -v : v;
 }
 
+/* E8M0 (the shared scale of an OCP microscaling block): the byte is a
+ * biased power-of-two exponent, value 2^(code - 127); code 255 is NaN. */
+double dsa_oracle_decode_e8m0(uint8_t code)
+{
+    return code == 255 ? NAN : ldexp(1.0, (int)code - 127);
+}
+
 static double load_elem(const void *base, size_t i, int dtype)
 {
     switch (dtype) {
     case 0: return (double)((const float *)base)[i];
     case 1: return dsa_oracle_decode_bf16(((const uint16_t *)base)[i]);
-    case 2: return dsa_oracle_decode_e4m3(((const uint8_t *)base)[i]);
+    case 2:
+    case 3: return dsa_oracle_decode_e4m3(((const uint8_t *)base)[i]);
     default: return NAN;
     }
+}
+
+/* Scale of element d of a stored vector (row `r` of a scale array): fp8 one
+ * fp32 scale per vector, MXFP8 one E8M0 byte per 32 elements, else 1. */
+static double elem_scale(const void *scale, size_t r, int D, int d, int dtype)
+{
+    if (dtype == 2)
+        return (double)((const float *)scale)[r];
+    if (dtype == 3)
+        return dsa_oracle_decode_e8m0(((const uint8_t *)scale)[r * (size_t)(D / 32) + d / 32]);
+    return 1.0;
 }
 
 static int set_threads(int nthreads)
@@ -116,21 +135,30 @@ int dsa_oracle_visible(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
  * from the paged K cache through the block table ("Day0 Inference Support and
  * Performance Optimization for New LLM Architectures", section III, 3.1).
  * For the fp8 route each stored value is code * scale, with one scale per
- * (query row, head) for q and one per cached token for k.
+ * (query row, head) for q and one per cached token for k.  The MXFP8 route
+ * (q and k quantized in groups of 32 elements that share one scale: "Optimizing
+ * Inference for Hybrid Attention Architectures: From Operator Fusion to
+ * Sequence Sharding", section "Layered Quantization: Distinguishing Precision
+ * Sensitivity"; "Day0 Inference Optimization for Next-Generation
+ * Hybrid-Architecture LLMs Based on CANN", section 3.1) stores e4m3 codes and
+ * one E8M0 byte per 32 consecutive elements of each q and k vector; each
+ * stored value is code * 2^(E - 127).
  * ------------------------------------------------------------------------- */
 int dsa_oracle_scores(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
                       const int32_t *block_table, int bt_stride, int page_size,
                       int H, int D, int dtype,
-                      const void *q, const float *q_scale, const float *w,
-                      const void *k_cache, const float *k_scale,
+                      const void *q, const void *q_scale, const float *w,
+                      const void *k_cache, const void *k_scale,
                       int L_out, double *scores, int nthreads)
 {
     if (B < 0 || H <= 0 || D <= 0 || page_size <= 0 || L_out < 0 || !q_offsets ||
         !ctx_lens || !block_table || !q || !w || !k_cache || !scores)
         return -1;
-    if (dtype < 0 || dtype > 2)
+    if (dtype < 0 || dtype > 3)
         return -1;
-    if (dtype == 2 && (!q_scale || !k_scale))
+    if (dtype >= 2 && (!q_scale || !k_scale))
+        return -1;
+    if (dtype == 3 && D % 32 != 0)
         return -1;
     int T = q_offsets[B];
     int32_t *vis = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
@@ -153,9 +181,9 @@ int dsa_oracle_scores(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
         double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
         double *wd = (double *)malloc(sizeof(double) * (size_t)H);
         for (int h = 0; h < H; ++h) {
-            double qs = (dtype == 2) ? (double)q_scale[(size_t)i * H + h] : 1.0;
             for (int d = 0; d < D; ++d)
-                qd[(size_t)h * D + d] = load_elem(q, ((size_t)i * H + h) * D + d, dtype) * qs;
+                qd[(size_t)h * D + d] = load_elem(q, ((size_t)i * H + h) * D + d, dtype) *
+                                        elem_scale(q_scale, (size_t)i * H + h, D, d, dtype);
             wd[h] = (double)w[(size_t)i * H + h];
         }
         double *row = scores + (size_t)i * L_out;
@@ -168,13 +196,14 @@ int dsa_oracle_scores(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
             }
             int page = block_table[(size_t)b * bt_stride + t / page_size];
             int slot = t % page_size;
-            size_t base = ((size_t)page * page_size + slot) * D;
-            double ks = (dtype == 2) ? (double)k_scale[(size_t)page * page_size + slot] : 1.0;
+            size_t tok = (size_t)page * page_size + slot;
+            size_t base = tok * D;
             double s = 0.0;
             for (int h = 0; h < H; ++h) {
                 double logit = 0.0;
                 for (int d = 0; d < D; ++d)
-                    logit += qd[(size_t)h * D + d] * (load_elem(k_cache, base + d, dtype) * ks);
+                    logit += qd[(size_t)h * D + d] *
+                             (load_elem(k_cache, base + d, dtype) * elem_scale(k_scale, tok, D, d, dtype));
                 s += wd[h] * (logit > 0.0 ? logit : 0.0);
             }
             row[t] = s;
@@ -251,8 +280,8 @@ int dsa_oracle_select(int T, int L_out, const double *scores, const int32_t *vis
 int dsa_oracle_indexer_topk(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
                             const int32_t *block_table, int bt_stride, int page_size,
                             int H, int D, int dtype,
-                            const void *q, const float *q_scale, const float *w,
-                            const void *k_cache, const float *k_scale,
+                            const void *q, const void *q_scale, const float *w,
+                            const void *k_cache, const void *k_scale,
                             int K, int32_t *idx, int L_out, double *scores_out,
                             int nthreads)
 {

@@ -24,7 +24,9 @@
  * Storage conventions (identical to the GPU library's, restated here so the
  * oracle stands alone):
  *   dtype 0 = fp32, 1 = bf16 (raw 16-bit patterns), 2 = fp8 e4m3 (OCP "fn"
- *   encoding, raw bytes; real value = code * fp32 scale).
+ *   encoding, raw bytes; real value = code * fp32 scale), 3 = MXFP8 (e4m3
+ *   codes; one E8M0 scale byte per 32 consecutive elements of a vector, real
+ *   value = code * 2^(E - 127)).
  *   Paged pools are [num_pages][page_size][dim]; block_table is
  *   [B][bt_stride] of physical page ids; request b owns query rows
  *   [q_offsets[b], q_offsets[b+1]) and L_b = ctx_lens[b] cached positions,
@@ -44,6 +46,7 @@ extern "C" {
 /* Decode one stored element to fp64. */
 double dsa_oracle_decode_bf16(uint16_t bits);
 double dsa_oracle_decode_e4m3(uint8_t code);
+double dsa_oracle_decode_e8m0(uint8_t code);
 
 /* Number of positions query row i may see (pos_i + 1), for all rows.
  * vis[T]; T = q_offsets[B]. */
@@ -53,13 +56,14 @@ int dsa_oracle_visible(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
 /* Lightning-indexer scores, fp64.  scores is [T][L_out]; entry [i][t] is the
  * score of position t for query row i when t is visible to row i, and NaN
  * otherwise (and for t >= L_out).  L_out must be >= every row's visible count.
- * q is [T][H][D], q_scale [T][H] (fp8 only), w [T][H] fp32,
- * k_cache [num_pages][page_size][D], k_scale [num_pages][page_size] (fp8 only). */
+ * q is [T][H][D], q_scale [T][H] fp32 (fp8) or [T][H][D/32] E8M0 bytes
+ * (MXFP8), w [T][H] fp32, k_cache [num_pages][page_size][D], k_scale
+ * [num_pages][page_size] fp32 (fp8) or [num_pages][page_size][D/32] bytes. */
 int dsa_oracle_scores(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
                       const int32_t *block_table, int bt_stride, int page_size,
                       int H, int D, int dtype,
-                      const void *q, const float *q_scale, const float *w,
-                      const void *k_cache, const float *k_scale,
+                      const void *q, const void *q_scale, const float *w,
+                      const void *k_cache, const void *k_scale,
                       int L_out, double *scores, int nthreads);
 
 /* Top-K of each row of a score matrix: the first min(K, vis[i]) positions in
@@ -72,8 +76,8 @@ int dsa_oracle_select(int T, int L_out, const double *scores, const int32_t *vis
 int dsa_oracle_indexer_topk(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
                             const int32_t *block_table, int bt_stride, int page_size,
                             int H, int D, int dtype,
-                            const void *q, const float *q_scale, const float *w,
-                            const void *k_cache, const float *k_scale,
+                            const void *q, const void *q_scale, const float *w,
+                            const void *k_cache, const void *k_scale,
                             int K, int32_t *idx, int L_out, double *scores_out,
                             int nthreads);
 

@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Every function takes
 host numpy arrays holding the raw storage of the inputs (fp32 values, bf16 bit
-patterns as uint16, fp8 e4m3 codes as uint8) and returns fp64 results computed
+patterns as uint16, fp8 and MXFP8 e4m3 codes as uint8, MXFP8 E8M0 scales as
+uint8) and returns fp64 results computed
 by the C code; nothing numerical happens here.
 """
 from __future__ import annotations
@@ -17,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3}
 
 _lib = None
 _LIB_PATH = [_LIB]
@@ -49,6 +50,8 @@ def _load():
         _lib.dsa_oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         _lib.dsa_oracle_decode_e4m3.restype = ctypes.c_double
         _lib.dsa_oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+        _lib.dsa_oracle_decode_e8m0.restype = ctypes.c_double
+        _lib.dsa_oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
         _lib.dsa_oracle_visible.argtypes = [I, P, P, P]
         _lib.dsa_oracle_scores.argtypes = [I, P, P, P, I, I, I, I, I, P, P, P, P, P, I, P, I]
         _lib.dsa_oracle_select.argtypes = [I, I, P, P, I, P, I]
@@ -88,7 +91,7 @@ def _f32(a):
 
 
 def _raw(a, dtype):
-    want = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+    want = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp8": np.uint8}[dtype]
     a = np.ascontiguousarray(a)
     if a.dtype != want:
         raise TypeError(f"{dtype} storage must be {np.dtype(want).name}, got {a.dtype}")
@@ -106,6 +109,22 @@ def decode_bf16(bits: int) -> float:
 
 def decode_e4m3(code: int) -> float:
     return _load().dsa_oracle_decode_e4m3(int(code))
+
+
+def decode_e8m0(code: int) -> float:
+    return _load().dsa_oracle_decode_e8m0(int(code))
+
+
+def _scales(a, dtype):
+    """fp8: fp32 scales; MXFP8: E8M0 bytes (uint8); else unused."""
+    if a is None:
+        return None
+    if dtype == "mxfp8":
+        a = np.ascontiguousarray(a)
+        if a.dtype != np.uint8:
+            raise TypeError(f"mxfp8 scales must be uint8 E8M0 bytes, got {a.dtype}")
+        return a
+    return _f32(a)
 
 
 def visible(q_offsets, ctx_lens) -> np.ndarray:
@@ -132,7 +151,7 @@ def scores(q_offsets, ctx_lens, block_table, page_size, dtype, q, q_scale, w, k_
         L_out = int(max(visible(q_offsets, ctx_lens).max(initial=0), 1))
     out = np.empty((T, L_out), dtype=np.float64)
     q, k_cache = _raw(q, dtype), _raw(k_cache, dtype)
-    w, q_scale, k_scale = _f32(w), _f32(q_scale), _f32(k_scale)
+    w, q_scale, k_scale = _f32(w), _scales(q_scale, dtype), _scales(k_scale, dtype)
     rc = _load().dsa_oracle_scores(B, _ptr(q_offsets), _ptr(ctx_lens), _ptr(block_table),
                                    block_table.shape[1], page_size, H, D, DTYPES[dtype],
                                    _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale),
@@ -160,7 +179,7 @@ def indexer_topk(q_offsets, ctx_lens, block_table, page_size, dtype, q, q_scale,
     idx = np.empty((T, K), dtype=np.int32)
     sc = np.empty((T, L_out), dtype=np.float64) if return_scores else None
     q, k_cache = _raw(q, dtype), _raw(k_cache, dtype)
-    w, q_scale, k_scale = _f32(w), _f32(q_scale), _f32(k_scale)
+    w, q_scale, k_scale = _f32(w), _scales(q_scale, dtype), _scales(k_scale, dtype)
     rc = _load().dsa_oracle_indexer_topk(B, _ptr(q_offsets), _ptr(ctx_lens), _ptr(block_table),
                                          block_table.shape[1], page_size, H, D, DTYPES[dtype],
                                          _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache),

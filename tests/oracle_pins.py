@@ -73,6 +73,15 @@ def check_decode_e4m3_all_codes():
     assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok])), "e4m3 sign of zero differs"
 
 
+def check_decode_e8m0_all_codes():
+    """E8M0 (OCP microscaling shared scale): 2^(code - 127), code 255 NaN;
+    against numpy.ldexp."""
+    got = np.array([oracle.decode_e8m0(c) for c in range(256)])
+    assert np.isnan(got[255]) and not np.isnan(got[:255]).any()
+    ref = np.ldexp(1.0, np.arange(255) - 127)
+    assert np.array_equal(got[:255], ref), "E8M0 decode differs from numpy.ldexp"
+
+
 def check_decode_bf16():
     rng = np.random.default_rng(5)
     bits = np.concatenate([rng.integers(0, 65536, 3000), [0, 0x8000, 0x3F80, 0xBF80, 0x7F7F,
@@ -243,6 +252,46 @@ def check_fp8_scales():
     s3 = oracle.scores(**{**a, "q_scale": qs})
     changed_rows = set(np.nonzero(~np.isclose(s3, s8, equal_nan=True))[0].tolist())
     assert changed_rows <= {0} and len(changed_rows) == 1
+
+
+def check_mxfp8_block_scales():
+    """MXFP8 route: value = e4m3 code * 2^(E - 127), one E8M0 byte E per 32
+    consecutive elements of each q (row, head) and each key.  Scores equal the
+    fp32 route's on values decoded with torch's e4m3 cast and numpy.ldexp,
+    bit for bit (the values are exact in fp32 and both routes form the same
+    fp64 products); a block's scale moves only its own 32 products."""
+    c = _small_case(15, dtype="mxfp8", H=3, D=64)
+    a = _np_case(c)
+    assert a["q_scale"].shape == (c.num_tokens, 3, 2) and a["k_scale"].shape[-1] == 2
+    rng = np.random.default_rng(3)  # spread the scales so a misplaced block shows
+    a["q_scale"] = (a["q_scale"].astype(np.int32) + rng.integers(-3, 4, a["q_scale"].shape)).astype(np.uint8)
+    ks = a["k_scale"].astype(np.int32)
+    real = ks != 255
+    ks[real] += rng.integers(-3, 4, int(real.sum()))
+    a["k_scale"] = ks.astype(np.uint8)
+    def dequant(codes, e):
+        v = _decoded(codes, "fp8")
+        blk = np.repeat(e.astype(np.int64), 32, axis=-1)
+        with np.errstate(invalid="ignore"):
+            return np.where(blk == 255, np.nan, np.ldexp(v, blk - 127)).astype(np.float32)
+    qv, kv = dequant(a["q"], a["q_scale"]), dequant(a["k_cache"], a["k_scale"])
+    smx = oracle.scores(**a)
+    s32 = oracle.scores(**{**a, "dtype": "f32", "q": qv, "q_scale": None, "k_cache": kv, "k_scale": None})
+    ok = ~np.isnan(s32)
+    assert np.array_equal(ok, ~np.isnan(smx))
+    assert np.array_equal(smx[ok], s32[ok]), "MXFP8 scores differ from the fp32 route on dequantized values"
+    # raising one key block's exponent by one changes only that key's scores,
+    # and by exactly the block's share: 2^1 on its 32 products
+    b, t = 1, 5
+    p = a["block_table"][b][t // a["page_size"]]
+    k2 = a["k_scale"].copy()
+    k2[p, t % a["page_size"], 1] += 1
+    s2 = oracle.scores(**{**a, "k_scale": k2})
+    diff = np.nonzero(~np.isclose(s2, smx, rtol=0, atol=0, equal_nan=True))
+    assert set(zip(*diff)) <= {(r, t) for r in range(a["q_offsets"][b], a["q_offsets"][b + 1])}
+    kv2 = dequant(a["k_cache"], k2)
+    s2f = oracle.scores(**{**a, "dtype": "f32", "q": qv, "q_scale": None, "k_cache": kv2, "k_scale": None})
+    assert np.array_equal(s2[ok], s2f[ok])
 
 
 def check_causal_visibility():
@@ -447,6 +496,7 @@ def check_sfa_uses_scale():
 
 ALL_CHECKS = [
     check_decode_e4m3_all_codes,
+    check_decode_e8m0_all_codes,
     check_decode_bf16,
     check_hand_examples_indexer,
     check_hand_example_sfa,
@@ -454,6 +504,7 @@ ALL_CHECKS = [
     check_head_weight_linearity,
     check_one_hot_query_reads_key_element,
     check_fp8_scales,
+    check_mxfp8_block_scales,
     check_causal_visibility,
     check_selection_definition,
     check_selection_signed_zero_and_nesting,

@@ -29,10 +29,15 @@ MUTANTS = [
     ("slot_shifted", "int slot = t % page_size;", "int slot = (t + 1) % page_size;"),
     ("physical_position", "int page = block_table[(size_t)b * bt_stride + t / page_size];\n            int slot = t % page_size;",
      "int page = t / page_size;\n            int slot = t % page_size;"),
-    ("k_scale_ignored", "double ks = (dtype == 2) ? (double)k_scale[(size_t)page * page_size + slot] : 1.0;",
-     "double ks = 1.0;"),
-    ("q_scale_per_row", "double qs = (dtype == 2) ? (double)q_scale[(size_t)i * H + h] : 1.0;",
-     "double qs = (dtype == 2) ? (double)q_scale[(size_t)i * H] : 1.0;"),
+    ("k_scale_ignored", "(load_elem(k_cache, base + d, dtype) * elem_scale(k_scale, tok, D, d, dtype))",
+     "load_elem(k_cache, base + d, dtype)"),
+    ("q_scale_per_row", "elem_scale(q_scale, (size_t)i * H + h, D, d, dtype)",
+     "elem_scale(q_scale, (size_t)i * H, D, d, dtype)"),
+    ("mx_block_misplaced", "[r * (size_t)(D / 32) + d / 32]", "[r * (size_t)(D / 32) + (d / 32 + 1) % (D / 32)]"),
+    ("mx_block_of_16", "[r * (size_t)(D / 32) + d / 32]", "[r * (size_t)(D / 32) + (d / 16) % (D / 32)]"),
+    ("mx_scale_rows_not_strided", "[r * (size_t)(D / 32) + d / 32]", "[r + d / 32]"),
+    ("e8m0_bias_126", "ldexp(1.0, (int)code - 127)", "ldexp(1.0, (int)code - 126)"),
+    ("e8m0_no_nan", "return code == 255 ? NAN : ldexp", "return code == 256 ? NAN : ldexp"),
     ("causal_off_by_one", "vis[q_offsets[b] + j] = ctx_lens[b] - n + j + 1;",
      "vis[q_offsets[b] + j] = ctx_lens[b] - n + j;"),
     ("causal_all_rows_see_all", "vis[q_offsets[b] + j] = ctx_lens[b] - n + j + 1;",
