@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 from lightning_indexer_top_02_amd import dsa, inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense, MI355X
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}  # dense, MI355X
 VALU_F32_PEAK_TFLOPS = 157.3  # fp32 routes run on the vector ALUs
 METRIC = "DSA decode tokens/s + HBM GB/s (% peak) at 32K ctx; prefill indexer MFMA util"
 
@@ -58,6 +58,17 @@ WORKLOADS = {
         desc="DSA chunked-prefill step: 4096 query tokens appended to a 61440-token prefix (65536 "
              "positions, causal), indexer 64 heads x 128 bf16, Top-K 2048 per row, sparse attention "
              "128 heads x (512+64) bf16"),
+    "batched_mxfp8_wide": dict(
+        make=lambda dev, batch=64: inputs.batched_decode_fp8(device=dev, batch=batch, wide=True, idx_dtype="mxfp8",
+                                                             name="batched_mxfp8_wide"),
+        desc="DSA decode step: batch {batch}, contexts U[4096,131072], MXFP8 indexer 64 x 128 (e4m3 with one "
+             "E8M0 scale per 32 elements of q and k), Top-K 2048, bf16 sparse attention 128 heads"),
+    "chunked_prefill_mxfp8": dict(
+        make=lambda dev, batch=1, sfa=True: inputs.chunked_prefill(
+            device=dev, idx_dtype="mxfp8", name="prefill_61440+4096_mxfp8", **({} if sfa else {"sfa_dtype": None})),
+        desc="DSA chunked-prefill step: 4096 query tokens appended to a 61440-token prefix (65536 "
+             "positions, causal), MXFP8 indexer 64 heads x 128 (one E8M0 scale per 32 elements), Top-K "
+             "2048 per row, sparse attention 128 heads x (512+64) bf16"),
     "spec_verify": dict(
         make=lambda dev, batch=16: inputs.spec_verify(device=dev, batch=batch),
         desc="DSA speculative-verify step: {batch} requests x 4 causal query tokens at context "
@@ -66,7 +77,12 @@ WORKLOADS = {
 
 
 def elem_bytes(dtype):
-    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[dtype]
+
+
+def scale_bytes(dtype, dim):
+    """Scale bytes per indexer vector (a q (row, head) or a key)."""
+    return {"fp8": 4, "mxfp8": dim // 32}.get(dtype, 0)
 
 
 def visible_per_row(case: inputs.Case):
@@ -80,7 +96,8 @@ def algorithmic_bytes(case: inputs.Case):
     """Bytes (and flops) the method itself needs per step, per stage.
 
     indexer: every visible key once per request (head dim x element size,
-             plus a 4-byte scale for fp8), q, w (and q scales), the block
+             plus its scale bytes: fp8 4, MXFP8 one per 32 elements), q, w
+             (and q scales), the block
              table, and the Top-K indices written; flops = 2 H_I D_I per
              visible (row, position) pair (the logits).
     sparse attention: the indices read, the latent rows gathered (each cached
@@ -92,9 +109,10 @@ def algorithmic_bytes(case: inputs.Case):
     qo = case.q_offsets.cpu().tolist()
     T, K = case.num_tokens, case.topk
     eK = elem_bytes(case.idx_dtype)
-    key_row = case.head_dim_idx * eK + (4 if case.idx_dtype == "fp8" else 0)
+    sb = scale_bytes(case.idx_dtype, case.head_dim_idx)
+    key_row = case.head_dim_idx * eK + sb
     H = case.n_heads_idx
-    idx_bytes = (sum(lens) * key_row + T * H * case.head_dim_idx * eK + T * H * 4 * (2 if case.idx_dtype == "fp8" else 1)
+    idx_bytes = (sum(lens) * key_row + T * H * case.head_dim_idx * eK + T * H * (4 + sb)
                  + sum((L + 63) // 64 for L in lens) * 4 + T * K * 4)
     eS = elem_bytes(case.sfa_dtype) if case.sfa_dtype != "none" else 0
     vis = visible_per_row(case)

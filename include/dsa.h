@@ -69,7 +69,12 @@ typedef enum {
     DSA_ERR_DEVICE = 5             /* no usable gfx950 device current */
 } dsa_status_t;
 
-typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
+/* DSA_MXFP8: e4m3 codes with one E8M0 scale byte (value 2^(E - 127)) per 32
+ * consecutive elements of each q (row, head) and each key, the MXFP8
+ * grouping of the indexer's q and k ("Optimizing Inference for Hybrid
+ * Attention Architectures: From Operator Fusion to Sequence Sharding",
+ * section "Layered Quantization: Distinguishing Precision Sensitivity"). */
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2, DSA_MXFP8 = 3 } dsa_dtype_t;
 
 /* Paging and batch description, shared by both caches (one block table and
  * one page size for the indexer K pool and the latent pool). */
@@ -88,17 +93,20 @@ typedef struct {
 
 /* Lightning indexer.  Supported: dtype F32 with head_dim % 4 == 0 and
  * n_heads*head_dim <= 4096; BF16 or FP8_E4M3 with head_dim in {64, 128};
- * 1 <= n_heads <= 64; 1 <= topk <= 4096. */
+ * MXFP8 with head_dim 128; 1 <= n_heads <= 64; 1 <= topk <= 4096. */
 typedef struct {
     int32_t n_heads;           /* H_I */
     int32_t head_dim;          /* D_I */
     int32_t topk;              /* K */
     int32_t dtype;             /* dsa_dtype_t of q and k_cache */
     const void *q;             /* [T][H_I][D_I] */
-    const float *q_scale;      /* [T][H_I] for FP8_E4M3, else NULL */
+    const void *q_scale;       /* FP8_E4M3: fp32 [T][H_I]; MXFP8: E8M0 bytes
+                                  [T][H_I][D_I/32], 4-byte aligned; else NULL */
     const float *weights;      /* [T][H_I] head-importance weights */
     const void *k_cache;       /* [num_pages][64][D_I] */
-    const float *k_scale;      /* [num_pages][64] for FP8_E4M3, else NULL */
+    const void *k_scale;       /* FP8_E4M3: fp32 [num_pages][64]; MXFP8: E8M0
+                                  bytes [num_pages][64][D_I/32], 4-byte
+                                  aligned; else NULL */
     int32_t flags;             /* 0, or DSA_INDEXER_* flags below */
 } dsa_indexer_t;
 
@@ -110,7 +118,7 @@ typedef struct {
 
 /* Indexer flags: take the two-pass route and pick its scoring kernel.
  * SCORE_ROWS is the row-tiled MFMA kernel (a workgroup per 4 query rows of a
- * request walks all of the request's positions; BF16/FP8 only, FP32 gives
+ * request walks all of the request's positions; BF16/FP8/MXFP8 only, FP32 gives
  * DSA_ERR_UNSUPPORTED); SCORE_POSITIONS is the position-tiled kernel (a
  * workgroup per 256 positions and 4 query rows).  Setting both is
  * DSA_ERR_INVALID_ARG.  Without either the library picks by shape (rows when

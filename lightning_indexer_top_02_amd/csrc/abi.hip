@@ -39,13 +39,21 @@ dsa_status_t check_indexer(const dsa_paged_t* pg, const dsa_indexer_t* x) {
   if (!valid_paged(pg) || !x) return DSA_ERR_INVALID_ARG;
   if (!x->q || !x->weights || !x->k_cache) return DSA_ERR_INVALID_ARG;
   if (x->n_heads < 1 || x->head_dim < 1 || x->topk < 1) return DSA_ERR_INVALID_ARG;
-  if (x->dtype != DSA_F32 && x->dtype != DSA_BF16 && x->dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
-  if (x->dtype == DSA_FP8_E4M3 && (!x->q_scale || !x->k_scale)) return DSA_ERR_INVALID_ARG;
+  if (x->dtype != DSA_F32 && x->dtype != DSA_BF16 && x->dtype != DSA_FP8_E4M3 && x->dtype != DSA_MXFP8)
+    return DSA_ERR_INVALID_ARG;
+  if ((x->dtype == DSA_FP8_E4M3 || x->dtype == DSA_MXFP8) && (!x->q_scale || !x->k_scale))
+    return DSA_ERR_INVALID_ARG;
   constexpr int32_t kRouteFlags = DSA_INDEXER_SCORE_ROWS | DSA_INDEXER_SCORE_POSITIONS;
   if (x->flags & ~(DSA_INDEXER_TWO_PASS | kRouteFlags)) return DSA_ERR_INVALID_ARG;
   if ((x->flags & kRouteFlags) == kRouteFlags) return DSA_ERR_INVALID_ARG;
   if (x->n_heads > kMaxIdxHeads || x->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
   if (x->head_dim != 64 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (x->dtype == DSA_MXFP8) {
+    // the kernels read a (row, head)'s or a key's four scale bytes as one word
+    if ((reinterpret_cast<uintptr_t>(x->q_scale) | reinterpret_cast<uintptr_t>(x->k_scale)) & 3)
+      return DSA_ERR_INVALID_ARG;
+    if (x->head_dim != 128) return DSA_ERR_UNSUPPORTED;  // one 16x16x128 step
+  }
   if (x->dtype == DSA_F32 && x->n_heads * x->head_dim > 4096) return DSA_ERR_UNSUPPORTED;
   if ((int64_t)pg->max_ctx_len > (int64_t)dsa_seg_max_segments() * 8192) return DSA_ERR_UNSUPPORTED;
   if (x->dtype == DSA_F32 && (x->flags & DSA_INDEXER_SCORE_ROWS)) return DSA_ERR_UNSUPPORTED;

@@ -119,10 +119,10 @@ struct DsaIndexerLaunch {
   const int32_t* block_table;
   int n_heads, head_dim, topk, dtype;
   const void* q;
-  const float* q_scale;
+  const void* q_scale;   // fp8: fp32 [T][H]; MXFP8: E8M0 bytes [T][H][D/32]
   const float* weights;
   const void* k_cache;
-  const float* k_scale;
+  const void* k_scale;   // fp8: fp32 [pages][64]; MXFP8: E8M0 bytes [pages][64][D/32]
   int32_t* out_idx;
   // workspace
   uint32_t* counters;  // [batch] arrival counters of the fused kernel, zero between calls

@@ -33,10 +33,10 @@ struct LiParams {
   int H, Hpad;
   int rcap;  // query rows the LDS layout holds (min(4, max rows per request))
   const void* q;
-  const float* q_scale;
+  const void* q_scale;
   const float* w;
   const void* k;
-  const float* k_scale;
+  const void* k_scale;
   float* scores;
   int64_t score_stride;
   uint32_t* hist;  // [rows][kHistStride]; level-1 digit histogram at offset 0 (null: scores only)
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
     };
     auto load = [&](KeyTiles<DT, D, 4>& t, int phys) {
       load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
-                               DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, 0);
+                               page_scales<DT, D>(p.k_scale, phys), 0);
     };
     // block-table entry of this wave's page of chunk fn (-1: none); read one
     // chunk ahead of the tile load that needs it, so the tile loads never wait
@@ -268,7 +268,8 @@ hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s) {
     switch (a.dtype) {
       case 0: e = d64 ? launch_score<0, 64>(p, grid, s) : launch_score<0, 128>(p, grid, s); break;
       case 1: e = d64 ? launch_score<1, 64>(p, grid, s) : launch_score<1, 128>(p, grid, s); break;
-      default: e = d64 ? launch_score<2, 64>(p, grid, s) : launch_score<2, 128>(p, grid, s); break;
+      case 2: e = d64 ? launch_score<2, 64>(p, grid, s) : launch_score<2, 128>(p, grid, s); break;
+      default: e = launch_score<3, 128>(p, grid, s); break;  // MXFP8: 128-dim only
     }
   }
   return e;

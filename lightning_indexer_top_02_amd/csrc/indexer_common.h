@@ -13,7 +13,11 @@
 // consecutive elements of one key row); 128-dim fp8 takes one 16x16x128
 // step, gfx950's only fp8 MFMA that runs at twice the bf16 rate (a 16x16x32
 // fp8 MFMA takes as long as a bf16 one).  fp32 keys use VALU, one thread per
-// position.
+// position.  MXFP8 (128-dim) takes the same 16x16x128 step in its
+// block-scaled form: the fragment layout below feeds element j of a row as
+// contraction index j, the instruction scales contraction indices 32b ..
+// 32b + 31 by the E8M0 operand of lane group b of that row or column, so
+// lane group g passes the scale of its row's block g.
 #pragma once
 
 #include <type_traits>
@@ -45,21 +49,31 @@ __device__ __forceinline__ f32x4 mfma_step(uint2 a, uint2 b, f32x4 c) {
   long la = __builtin_bit_cast(long, a), lb = __builtin_bit_cast(long, b);
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(la, lb, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_step(const Frag8& a, const Frag8& b, f32x4 c) {
+// The 16x16x128 step with E8M0 scales: sa for this lane's A block, sb for
+// its B block (low bytes).
+__device__ __forceinline__ f32x4 mfma_step_mx(const Frag8& a, const Frag8& b, f32x4 c, int sa, int sb) {
   typedef int v8i __attribute__((ext_vector_type(8)));
   const v8i va = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w, (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
   const v8i vb = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w, (int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w};
-  // formats 0, 0: both operands fp8 e4m3; zero scale operands select the
-  // unscaled instruction (v_mfma_f32_16x16x128_f8f6f4)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, c, 0, 0, 0, 0, 0, 0);
+  // formats 0, 0: both operands fp8 e4m3
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, c, 0, 0, 0, sa, 0, sb);
+}
+__device__ __forceinline__ f32x4 mfma_step(const Frag8& a, const Frag8& b, f32x4 c) {
+  // zero scale operands select the unscaled instruction (v_mfma_f32_16x16x128_f8f6f4)
+  return mfma_step_mx(a, b, c, 0, 0);
 }
 
-// Storage geometry of one indexer variant: DT 0 = fp32, 1 = bf16, 2 = fp8.
+// Storage geometry of one indexer variant: DT 0 = fp32, 1 = bf16, 2 = fp8,
+// 3 = MXFP8 (128-dim only).
 template <int DT, int D>
 struct IdxGeom {
   static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);   // bytes per element
-  static constexpr int QSTRIDE = DT == 0 ? D * 4 : D * ES + 16;  // LDS bytes per (row, head)
-  static constexpr bool K128 = DT == 2 && D == 128;             // one 16x16x128 fp8 step
+  // LDS bytes per (row, head); MXFP8 keeps the D/32 block scales of the
+  // (row, head) in the 16 bytes after its codes
+  static constexpr int QSTRIDE = DT == 0 ? D * 4 : D * ES + 16;
+  static constexpr bool MX = DT == 3;
+  static_assert(!MX || D == 128, "MXFP8 takes one 16x16x128 step");
+  static constexpr bool K128 = DT >= 2 && D == 128;             // one 16x16x128 fp8 step
   static constexpr int KS = K128 ? 1 : D / 32;                  // contraction steps
   using frag_t = typename std::conditional<K128, Frag8, typename std::conditional<DT == 1, uint4, uint2>::type>::type;
   // Byte offset, within a row of D elements, of the 8 elements lane group g
@@ -71,7 +85,7 @@ struct IdxGeom {
   // contiguous bytes of every key row instead of 32.  The 16x16x128 step
   // takes the same 32 bytes per lane group at once (16g .. and 64 + 16g ..).
   static __host__ __device__ constexpr int frag_byte(int ks, int g) {
-    return DT == 2 ? 16 * g + 8 * (ks & 1) + 64 * (ks >> 1) : (32 * ks + 8 * g) * ES;
+    return DT >= 2 ? 16 * g + 8 * (ks & 1) + 64 * (ks >> 1) : (32 * ks + 8 * g) * ES;
   }
   // The fragment of contraction step ks for lane group g of the row at `row`.
   static __device__ __forceinline__ frag_t load_frag(const unsigned char* row, int ks, int g) {
@@ -90,9 +104,10 @@ __host__ __device__ constexpr size_t query_lds_bytes(int rows, int Hpad) {
 }
 
 // Stage `nrows` query rows starting at global row `row0` (heads past H are
-// zero) and their weights (times the q scale for fp8) into LDS.
+// zero) and their weights (times the q scale for fp8) into LDS; MXFP8 rows
+// keep their block scales beside the codes (padded heads: 2^0).
 template <int DT, int D, int NT>
-__device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, const float* q_scale,
+__device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, const void* q_scale,
                               const float* w, int row0, int nrows, int H, int Hpad) {
   using G = IdxGeom<DT, D>;
   constexpr int CPH = D * G::ES / 16;  // 16-byte chunks per head
@@ -106,13 +121,20 @@ __device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, cons
     if (h < H) v = *reinterpret_cast<const uint4*>(qg + ((int64_t)(row0 + r) * H + h) * (D * G::ES) + part * 16);
     *reinterpret_cast<uint4*>(qs + (r * Hpad + h) * G::QSTRIDE + part * 16) = v;
   }
+  if constexpr (G::MX) {
+    for (int c = threadIdx.x; c < nrows * Hpad; c += NT) {
+      const int r = c / Hpad, h = c - r * Hpad;
+      const uint32_t e = h < H ? static_cast<const uint32_t*>(q_scale)[(int64_t)(row0 + r) * H + h] : 0x7f7f7f7fu;
+      *reinterpret_cast<uint32_t*>(qs + (r * Hpad + h) * G::QSTRIDE + D) = e;
+    }
+  }
   for (int c = threadIdx.x; c < nrows * Hpad; c += NT) {
     const int r = c / Hpad, h = c - r * Hpad;
     float wv = 0.f;
     if (h < H) {
       const int64_t o = (int64_t)(row0 + r) * H + h;
       wv = w[o];
-      if (DT == 2) wv *= q_scale[o];  // q scale > 0 folds through the ReLU
+      if (DT == 2) wv *= static_cast<const float*>(q_scale)[o];  // q scale > 0 folds through the ReLU
     }
     wsm[r * Hpad + h] = wv;
   }
@@ -121,16 +143,26 @@ __device__ void stage_queries(unsigned char* qs, float* wsm, const void* q, cons
 // Key fragments of NPT tiles of 16 positions of one page (slots slot0 ..
 // slot0 + 16 NPT - 1), in the B-operand layout: kf[pt][ks] holds 8 elements
 // of position slot0 + pt*16 + l16 at byte frag_byte(ks, g); kscale[pt] its
-// fp8 scale (1 otherwise).
+// fp8 scale (1 otherwise); kmx[pt] its MXFP8 block-g scale.
 template <int DT, int D, int NPT>
 struct KeyTiles {
   typename IdxGeom<DT, D>::frag_t kf[NPT][IdxGeom<DT, D>::KS];
   float kscale[NPT];
+  int kmx[NPT];
 };
+
+// The key scales of physical page `phys` (fp8: one fp32 per slot; MXFP8:
+// D/32 E8M0 bytes per slot), or null.
+template <int DT, int D>
+__device__ __forceinline__ const void* page_scales(const void* k_scale, int64_t phys) {
+  if constexpr (DT == 2) return static_cast<const float*>(k_scale) + phys * kPage;
+  if constexpr (DT == 3) return static_cast<const uint8_t*>(k_scale) + phys * kPage * (D / 32);
+  return nullptr;
+}
 
 template <int DT, int D, int NPT>
 __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const unsigned char* kpage,
-                                               const float* kscale_page, int slot0) {
+                                               const void* kscale_page, int slot0) {
   using G = IdxGeom<DT, D>;
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
@@ -138,7 +170,11 @@ __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const un
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) t.kf[pt][ks] = G::load_frag(kpage + (slot0 + pt * 16 + l16) * D * G::ES, ks, g);
 #pragma unroll
-  for (int pt = 0; pt < NPT; ++pt) t.kscale[pt] = (DT == 2) ? kscale_page[slot0 + pt * 16 + l16] : 1.f;
+  for (int pt = 0; pt < NPT; ++pt) {
+    const int slot = slot0 + pt * 16 + l16;
+    t.kscale[pt] = DT == 2 ? static_cast<const float*>(kscale_page)[slot] : 1.f;
+    t.kmx[pt] = DT == 3 ? static_cast<const uint8_t*>(kscale_page)[slot * (D / 32) + g] : 0;
+  }
 }
 
 // One wave scores NPT loaded key tiles for `nrows` staged rows.  emit(r,
@@ -163,8 +199,14 @@ __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const f
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const typename G::frag_t a = G::load_frag(qrow, ks, g);
+      if constexpr (G::MX) {
+        const int sa = qrow[D + g];
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_step(a, t.kf[pt][ks], acc[pt]);
+        for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_step_mx(a, t.kf[pt][ks], acc[pt], sa, t.kmx[pt]);
+      } else {
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) acc[pt] = mfma_step(a, t.kf[pt][ks], acc[pt]);
+      }
     }
     // acc[pt][i] = logit of head ht*16 + 4g + i at slot slot0 + pt*16 + l16
     const float* wr = wsm + r * hp + ht * 16 + 4 * g;

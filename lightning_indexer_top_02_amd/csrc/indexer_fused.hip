@@ -40,10 +40,10 @@ struct FusedParams {
   int batch, bt_stride;
   int H, Hpad, rcap;
   const void* q;
-  const float* q_scale;
+  const void* q_scale;
   const float* w;
   const void* k;
-  const float* k_scale;
+  const void* k_scale;
   int K;
   int32_t* out;
   int G;                // workgroups per request (each takes every G-th chunk)
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
     KeyTiles<DT, D, 1> ring[3];
     auto load_at = [&](KeyTiles<DT, D, 1>& t, int phys, int tpos) {
       load_key_tiles<DT, D, 1>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
-                               DT == 2 ? p.k_scale + (int64_t)phys * kPage : nullptr, tpos & 63);
+                               page_scales<DT, D>(p.k_scale, phys), tpos & 63);
     };
     if constexpr (MODE == 0) {
       // few chunks per workgroup (small batches): the first key tile is in
@@ -387,6 +387,7 @@ hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s) {
   switch (a.dtype) {
     case 0: return d64 ? launch_fused<0, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<0, 128>(p, a.batch, a.max_ctx_len, s);
     case 1: return d64 ? launch_fused<1, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<1, 128>(p, a.batch, a.max_ctx_len, s);
-    default: return d64 ? launch_fused<2, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<2, 128>(p, a.batch, a.max_ctx_len, s);
+    case 2: return d64 ? launch_fused<2, 64>(p, a.batch, a.max_ctx_len, s) : launch_fused<2, 128>(p, a.batch, a.max_ctx_len, s);
+    default: return launch_fused<3, 128>(p, a.batch, a.max_ctx_len, s);  // MXFP8: 128-dim only
   }
 }

@@ -48,10 +48,10 @@ struct PrefillParams {
   int batch, bt_stride;
   int H;
   const void* q;
-  const float* q_scale;
+  const void* q_scale;
   const float* w;
   const void* k;
-  const float* k_scale;
+  const void* k_scale;
   float* scores;
   int64_t score_stride;
   uint32_t* hist;  // [rows][kHistStride]: level-1 histogram at offset 0 (null: scores only)
@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   // two key tiles: tile t is read from buffer t % 2 while tile t + 1 is
   // written into the other
   unsigned char* const kbuf = smem;                                         // [2][kPfTile][KROW]
-  float* const kscb = reinterpret_cast<float*>(smem + 2 * kPfTile * KROW);  // [2][kPfTile] fp8 scales
+  // [2][kPfTile] key scales: fp8 one fp32, MXFP8 the four E8M0 bytes of the position
+  float* const kscb = reinterpret_cast<float*>(smem + 2 * kPfTile * KROW);
   uint32_t* lhist = reinterpret_cast<uint32_t*>(kscb + 2 * kPfTile);        // [kPfRows][kHistBins]
   const unsigned char* ktile = kbuf;                                        // the tile being read
   const float* ksc = kscb;
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   // this wave's query row as A fragments: qf[mt][ks] = step ks of q[row][mt*16 + l16] for lane group g
   frag_t qf[MT][KS];
   float wl[MT][4];  // weights of heads mt*16 + 4g + i (times the q scale for fp8)
+  int qsx[MT];      // MXFP8: the E8M0 scale of block g of head mt*16 + l16 (low byte)
   {
     const unsigned char* qg = static_cast<const unsigned char*>(p.q);
 #pragma unroll
@@ -113,13 +115,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
           v = Gm::load_frag(qg + ((int64_t)row * p.H + h) * (D * ES), ks, g);
         qf[mt][ks] = v;
       }
+      qsx[mt] = 0;
+      if (Gm::MX && row_ok && h < p.H)
+        qsx[mt] = static_cast<const uint8_t*>(p.q_scale)[((int64_t)row * p.H + h) * (D / 32) + g];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = mt * 16 + 4 * g + i;
         float wv = 0.f;
         if (row_ok && hh < p.H) {
           wv = p.w[(int64_t)row * p.H + hh];
-          if (DT == 2) wv *= p.q_scale[(int64_t)row * p.H + hh];
+          if (DT == 2) wv *= static_cast<const float*>(p.q_scale)[(int64_t)row * p.H + hh];
         }
         wl[mt][i] = wv;
       }
@@ -157,11 +162,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
         v = *reinterpret_cast<const uint4*>(kg + ((int64_t)phys * kPage + (pos & 63)) * (D * ES) + part * 16);
       pre[j] = v;
     }
-    if (DT == 2 && tid < kPfTile) {
+    if (DT >= 2 && tid < kPfTile) {
       int phys = ph[0];
 #pragma unroll
       for (int i = 1; i < PAGES; ++i) phys = (tid >> 6) == i ? ph[i] : phys;
-      pre_s = phys >= 0 ? p.k_scale[(int64_t)phys * kPage + (tid & 63)] : 0.f;
+      const int64_t slot = (int64_t)phys * kPage + (tid & 63);
+      if (phys < 0) pre_s = 0.f;
+      else if (DT == 2) pre_s = static_cast<const float*>(p.k_scale)[slot];
+      else pre_s = __uint_as_float(static_cast<const uint32_t*>(p.k_scale)[slot]);  // 4 E8M0 bytes
     }
   };
   auto stage = [&](int buf) {
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
       const int part = c - pos * PPR;
       *reinterpret_cast<uint4*>(kt + pos * KROW + part * 16) = pre[j];
     }
-    if (DT == 2 && tid < kPfTile) kscb[buf * kPfTile + tid] = pre_s;
+    if (DT >= 2 && tid < kPfTile) kscb[buf * kPfTile + tid] = pre_s;
   };
 
   // Two accumulator sets: the MFMAs of a sub-tile go to one while the
@@ -195,6 +203,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) a[mt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int kx[2] = {0, 0};  // MXFP8: block g scale of position sub*32 + pt*16 + l16 (low byte)
+    if constexpr (Gm::MX) {
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) kx[pt] = (int)(__float_as_uint(ksc[sub * kPfSub + pt * 16 + l16]) >> (8 * g));
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       frag_t cur[2] = {bf[0], bf[1]};
@@ -203,7 +216,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) a[mt][pt] = mfma_step(qf[mt][ks], cur[pt], a[mt][pt]);
+        for (int pt = 0; pt < 2; ++pt) {
+          if constexpr (Gm::MX) a[mt][pt] = mfma_step_mx(qf[mt][ks], cur[pt], a[mt][pt], qsx[mt], kx[pt]);
+          else a[mt][pt] = mfma_step(qf[mt][ks], cur[pt], a[mt][pt]);
+        }
     }
     // the scale of the position this lane ends up holding (lanes g < 2)
     if (DT == 2) kscale = ksc[sub * kPfSub + (g & 1) * 16 + l16];
@@ -324,7 +340,7 @@ bool dsa_indexer_rows_route(const DsaIndexerLaunch& a) {
   return a.max_q_per_req > 4 && a.num_rows >= 1024;
 }
 
-// Scores and level-1 histograms of every row (bf16 or fp8 keys, at most 64
+// Scores and level-1 histograms of every row (bf16, fp8 or MXFP8 keys, at most 64
 // heads; hipErrorInvalidValue otherwise).
 hipError_t dsa_launch_indexer_prefill_scores(const DsaIndexerLaunch& a, hipStream_t s) {
   if (a.dtype == 0 || a.n_heads > kPfHeads) return hipErrorInvalidValue;
@@ -346,5 +362,6 @@ hipError_t dsa_launch_indexer_prefill_scores(const DsaIndexerLaunch& a, hipStrea
   const dim3 grid((a.max_q_per_req + kPfRows - 1) / kPfRows, a.batch);
   const bool d64 = a.head_dim == 64;
   if (a.dtype == 1) return d64 ? launch_prefill<1, 64>(p, grid, s) : launch_prefill<1, 128>(p, grid, s);
+  if (a.dtype == 3) return launch_prefill<3, 128>(p, grid, s);  // MXFP8: 128-dim only
   return d64 ? launch_prefill<2, 64>(p, grid, s) : launch_prefill<2, 128>(p, grid, s);
 }

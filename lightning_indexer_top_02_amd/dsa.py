@@ -7,7 +7,8 @@ library is missing this module raises on import of the first call, so a
 missing build can never fall back to anything else.
 
 Storage dtypes: ``"f32"`` (torch.float32), ``"bf16"`` (torch.bfloat16 or its
-raw int16/uint16 bits), ``"fp8"`` (torch.float8_e4m3fn or raw uint8 codes).
+raw int16/uint16 bits), ``"fp8"`` (torch.float8_e4m3fn or raw uint8 codes),
+``"mxfp8"`` (e4m3 codes as for fp8, with uint8 E8M0 block scales).
 """
 from __future__ import annotations
 
@@ -24,11 +25,12 @@ DSA_OK = 0
 INDEXER_TWO_PASS = 1  # flag: scores through the workspace instead of the fused kernel
 INDEXER_SCORE_ROWS = 2  # flag: two-pass route, row-tiled MFMA scoring kernel
 INDEXER_SCORE_POSITIONS = 4  # flag: two-pass route, position-tiled scoring kernel
-DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3}
 _STORAGE = {
     "f32": (torch.float32,),
     "bf16": (torch.bfloat16, torch.int16, torch.uint16),
     "fp8": (torch.float8_e4m3fn, torch.uint8),
+    "mxfp8": (torch.float8_e4m3fn, torch.uint8),
 }
 
 
@@ -174,8 +176,9 @@ def make_indexer(q, weights, k_cache, topk, dtype, q_scale=None, k_scale=None, f
     _check_tensor(q, "q", _STORAGE[dtype])
     _check_tensor(k_cache, "k_cache", _STORAGE[dtype])
     _check_tensor(weights, "weights", (torch.float32,))
-    _check_tensor(q_scale, "q_scale", (torch.float32,))
-    _check_tensor(k_scale, "k_scale", (torch.float32,))
+    scale_dtypes = (torch.uint8,) if dtype == "mxfp8" else (torch.float32,)
+    _check_tensor(q_scale, "q_scale", scale_dtypes)
+    _check_tensor(k_scale, "k_scale", scale_dtypes)
     T, H, D = q.shape
     if k_cache.shape[-1] != D or weights.shape != (T, H):
         raise ValueError("indexer shapes disagree")

@@ -168,7 +168,8 @@ def compare_topk(gpu_idx, ora_idx, ora_scores, vis, exact: bool, rows=None):
 # in-bounds probe: one 448 x 1 product plus 31 products of 2^-6 gives 448.875
 # for 448.984375, and 448^2 + 31 x 1 loses 7 of the 31), so its dot products
 # carry errors of a few 1e-5 of their largest product.
-SCORE_REL_TOL = {"f32": 1e-5, "bf16": 1e-5, "fp8": 1e-4}
+# MXFP8 runs on the same 16x16x128 instruction (block-scaled form).
+SCORE_REL_TOL = {"f32": 1e-5, "bf16": 1e-5, "fp8": 1e-4, "mxfp8": 1e-4}
 
 
 def compare_scores(gpu_scores, ora_scores, vis, exact: bool, magnitude=None, dtype="bf16"):

@@ -89,7 +89,11 @@ BAD_INDEXER = [(dict(q=None), 1), (dict(weights=None), 1), (dict(k_cache=None), 
                (dict(n_heads=0), 1), (dict(dtype=7), 1), (dict(dtype=2), 1),  # fp8 without scales
                (dict(dtype=2, q_scale=FAKE), 1), (dict(n_heads=65), 2), (dict(topk=4097), 2),
                (dict(head_dim=96), 2), (dict(dtype=0, n_heads=64, head_dim=128), 2), (dict(flags=8), 1),
-               (dict(flags=6), 1), (dict(flags=7), 1), (dict(dtype=0, n_heads=4, head_dim=64, flags=2), 2)]
+               (dict(flags=6), 1), (dict(flags=7), 1), (dict(dtype=0, n_heads=4, head_dim=64, flags=2), 2),
+               (dict(dtype=3), 1), (dict(dtype=3, k_scale=FAKE), 1),  # MXFP8 without scales
+               (dict(dtype=3, q_scale=FAKE + 2, k_scale=FAKE), 1),  # scale words misaligned
+               (dict(dtype=3, q_scale=FAKE, k_scale=FAKE + 1), 1),
+               (dict(dtype=3, q_scale=FAKE, k_scale=FAKE, head_dim=64), 2)]
 
 
 @pytest.mark.parametrize("kw,status", BAD_INDEXER, ids=[str(k) for k, _ in BAD_INDEXER])

@@ -60,7 +60,7 @@ RAGGED = [1, 63, 64, 65, 300, 4097, 257]
 RAGGED_NQ = [1, 1, 2, 4, 3, 1, 4]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
 @pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
 def test_ragged_wide(dtype, exact):
     _run(inputs.make_case(name=f"ragged_wide_{dtype}", seed=77, ctx_lens=RAGGED, n_q=RAGGED_NQ,
@@ -114,7 +114,7 @@ PREFILL_NQ = [300, 17, 130, 5]
 
 
 @pytest.mark.parametrize("dtype,dim,heads", [("bf16", 128, 64), ("bf16", 64, 40), ("fp8", 128, 64),
-                                             ("fp8", 64, 23)])
+                                             ("fp8", 64, 23), ("mxfp8", 128, 64), ("mxfp8", 128, 23)])
 @pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
 def test_prefill_ragged_rows(dtype, dim, heads, exact):
     _run(inputs.make_case(name=f"prefill_ragged_{dtype}_{dim}x{heads}", seed=90, ctx_lens=PREFILL_LENS,
@@ -131,6 +131,9 @@ SCORE_CASES = {
     "ragged_fp8_d64": lambda exact: inputs.make_case(name="sc_fp8", seed=92, ctx_lens=PREFILL_LENS, n_q=PREFILL_NQ,
                                                      idx_dtype="fp8", n_heads_idx=19, head_dim_idx=64, topk=64,
                                                      sfa_dtype=None, exact=exact),
+    "ragged_mxfp8": lambda exact: inputs.make_case(name="sc_mxfp8", seed=93, ctx_lens=PREFILL_LENS, n_q=PREFILL_NQ,
+                                                   idx_dtype="mxfp8", n_heads_idx=37, head_dim_idx=128, topk=64,
+                                                   sfa_dtype=None, exact=exact),
 }
 
 
@@ -209,6 +212,14 @@ FUSED_BATCHED = {
     "b300_fp8_d64": lambda: inputs.make_case(name="fused_b300_fp8_d64", seed=92, ctx_lens=[20000] * 300, n_q=1,
                                              idx_dtype="fp8", n_heads_idx=64, head_dim_idx=64, topk=2048,
                                              sfa_dtype=None, device="cuda"),
+    # MXFP8 keys: 64 one-row requests (one-row 64-head mode) and the general mode
+    "b64_mxfp8": lambda: inputs.decode_32k(batch=64, device="cuda", sfa_dtype=None, idx_dtype="mxfp8",
+                                           name="fused_b64_mxfp8"),
+    "b24_mxfp8_48h": lambda: inputs.make_case(name="fused_b24_mxfp8_48h", seed=94,
+                                              ctx_lens=[5000 + 1117 * i for i in range(24)],
+                                              n_q=[1 + (i % 3 == 0) for i in range(24)], idx_dtype="mxfp8",
+                                              n_heads_idx=48, head_dim_idx=128, topk=2048, sfa_dtype=None,
+                                              device="cuda"),
 }
 
 
