@@ -69,6 +69,12 @@ WORKLOADS = {
         desc="DSA chunked-prefill step: 4096 query tokens appended to a 61440-token prefix (65536 "
              "positions, causal), MXFP8 indexer 64 heads x 128 (one E8M0 scale per 32 elements), Top-K "
              "2048 per row, sparse attention 128 heads x (512+64) bf16"),
+    "scratch_prefill": dict(
+        make=lambda dev, batch=1, sfa=True: inputs.chunked_prefill(
+            device=dev, prefix=0, new=16384, name="prefill_0+16384_bf16", **({} if sfa else {"sfa_dtype": None})),
+        desc="DSA prefill from scratch: one request of 16384 tokens, every one a causal query row (row i "
+             "sees i + 1 positions), indexer 64 heads x 128 bf16, Top-K 2048 per row, sparse attention "
+             "128 heads x (512+64) bf16"),
     "spec_verify": dict(
         make=lambda dev, batch=16: inputs.spec_verify(device=dev, batch=batch),
         desc="DSA speculative-verify step: {batch} requests x 4 causal query tokens at context "

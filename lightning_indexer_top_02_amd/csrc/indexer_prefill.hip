@@ -87,7 +87,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
 
   const int b = blockIdx.y;
   const int q0 = p.q_offsets[b], nb = p.q_offsets[b + 1] - q0;
-  const int r0 = blockIdx.x * kPfRows;
+  // Causal rows: a row block's work grows with its position in the request
+  // (row j sees L - n + j + 1 positions), up to twice the average in a
+  // prefill from scratch.  Blocks are dispatched heaviest first, so the light
+  // ones fill the compute units that the heavy ones leave free at the end
+  // instead of the heavy ones running alone in a tail.
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * kPfRows;
   if (r0 >= nb) return;
   const int nrows = min(kPfRows, nb - r0);
   const int first_pos = p.ctx_lens[b] - nb;

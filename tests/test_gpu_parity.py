@@ -122,6 +122,15 @@ def test_prefill_ragged_rows(dtype, dim, heads, exact):
                           sfa_dtype="bf16", n_heads_sfa=16, exact=exact), fused=False)
 
 
+# A prefill from scratch (every position a query row: the most uneven causal
+# work per row block) next to a short chunked request, every row checked.
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_scratch_prefill_rows(exact):
+    _run(inputs.make_case(name="scratch_prefill_1203", seed=95, ctx_lens=[1203, 500], n_q=[1203, 37],
+                          idx_dtype="bf16", n_heads_idx=64, head_dim_idx=128, topk=256, sfa_dtype="bf16",
+                          n_heads_sfa=16, exact=exact), fused=False)
+
+
 # --- scores alone (dsa_indexer_scores) against the oracle's scores -------------
 SCORE_CASES = {
     "tiny_f32": lambda exact: inputs.tiny_decode(exact=exact),
@@ -173,6 +182,12 @@ def test_chunked_prefill_full():
     """4096 query rows appended to a 61440-token prefix (65536 positions)."""
     case = inputs.chunked_prefill(device="cuda")
     _full(case, [0, 1, 1000, 2047, 3333, 4095])
+
+
+def test_scratch_prefill_full():
+    """A prefill from scratch: 16384 causal query rows, row i sees i + 1 positions."""
+    case = inputs.chunked_prefill(device="cuda", prefix=0, new=16384, name="prefill_0+16384_bf16")
+    _full(case, [0, 1, 7, 8, 2046, 2047, 2048, 9001, 16383])
 
 
 def test_spec_verify_full():
