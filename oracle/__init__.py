@@ -11,6 +11,9 @@ from .oracle import (  # noqa: F401
     decode_bf16,
     decode_e4m3,
     decode_e8m0,
+    encode_e4m3,
+    encode_bf16,
+    cache_append,
     visible,
     scores,
     select,

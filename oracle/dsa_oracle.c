@@ -388,3 +388,130 @@ int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
     }
     return 0;
 }
+
+/* ---- Cache append: the producer step that fills the indexer K pool --------
+ * ("Optimizing Inference for Hybrid Attention Architectures: From Operator
+ * Fusion to Sequence Sharding", section "Breaking Down the Computational Path
+ * of Hybrid Attention": the normalised key of each new token is written into
+ * the indexer's paged K cache, quantised where the indexer runs in low
+ * precision; section "Layered Quantization: Distinguishing Precision
+ * Sensitivity" for the MXFP8 grouping.)
+ *
+ * Placement: the n_b new keys of request b are its query tokens, so key j goes
+ * to position p = L_b - n_b + j (where the scoring looks for it): page
+ * block_table[b][p / page_size], slot p % page_size.
+ *
+ * Rounding: the codes are integer decisions taken from fp32 values, so the
+ * quotients are formed in fp32 and rounded from there to the storage grid,
+ * to nearest with ties to even.  round_to_grid is that rounding for a format
+ * with `mant` fraction bits whose exponent stops at `emin` (below 2^emin the
+ * spacing stays 2^(emin - mant): the subnormals). */
+static double round_to_grid(double a, int mant, int emin)
+{
+    if (a == 0.0)
+        return 0.0;
+    int e;
+    frexp(a, &e); /* a = f * 2^e with f in [0.5, 1), so floor(log2 a) = e - 1 */
+    int E = e - 1 < emin ? emin : e - 1;
+    double q = ldexp(1.0, E - mant);
+    return nearbyint(a / q) * q; /* the default rounding mode: ties to even */
+}
+
+/* e4m3 code of v: nearest even, saturating at +-448, sign kept on zero. */
+static uint8_t e4m3_of(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double r = round_to_grid(fabs(v), 3, -6);
+    if (r > 448.0)
+        r = 448.0;
+    if (r == 0.0)
+        return sign;
+    int e;
+    frexp(r, &e);
+    int E = e - 1;
+    if (E < -6) /* subnormal: a multiple of 2^-9 below 2^-6 */
+        return (uint8_t)(sign | (int)(r / ldexp(1.0, -9)));
+    return (uint8_t)(sign | ((E + 7) << 3) | (int)(r / ldexp(1.0, E - 3) - 8.0));
+}
+
+uint8_t dsa_oracle_encode_e4m3(float x)
+{
+    return e4m3_of((double)x);
+}
+
+uint16_t dsa_oracle_encode_bf16(float x)
+{
+    double r = round_to_grid(fabs((double)x), 7, -126);
+    float f = (float)(signbit(x) ? -r : r); /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+int dsa_oracle_cache_append(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
+                            const int32_t *block_table, int bt_stride, int page_size, int D,
+                            int src_dtype, const void *k_new, int dst_dtype,
+                            void *k_cache, void *k_scale)
+{
+    if (B < 1 || D < 1 || page_size < 1 || !q_offsets || !ctx_lens || !block_table || !k_new || !k_cache)
+        return -1;
+    if ((src_dtype != 0 && src_dtype != 1) || dst_dtype < 0 || dst_dtype > 3)
+        return -1;
+    if ((dst_dtype == 2 || dst_dtype == 3) && !k_scale)
+        return -1;
+    if (dst_dtype == 3 && D % 32 != 0)
+        return -1;
+    float *x = malloc(sizeof(float) * (size_t)D);
+    if (!x)
+        return -2;
+    for (int b = 0; b < B; ++b) {
+        int n = q_offsets[b + 1] - q_offsets[b], L = ctx_lens[b];
+        if (n < 0 || n > L) {
+            free(x);
+            return -1;
+        }
+        for (int j = 0; j < n; ++j) {
+            size_t i = (size_t)q_offsets[b] + j;
+            int p = L - n + j;
+            int page = block_table[(size_t)b * bt_stride + p / page_size];
+            size_t row = (size_t)page * page_size + p % page_size;
+            for (int d = 0; d < D; ++d)
+                x[d] = (float)load_elem(k_new, i * D + d, src_dtype); /* exact */
+            if (dst_dtype == 0) {
+                for (int d = 0; d < D; ++d)
+                    ((float *)k_cache)[row * D + d] = x[d];
+            } else if (dst_dtype == 1) {
+                for (int d = 0; d < D; ++d)
+                    ((uint16_t *)k_cache)[row * D + d] = dsa_oracle_encode_bf16(x[d]);
+            } else if (dst_dtype == 2) {
+                float amax = 0.0f;
+                for (int d = 0; d < D; ++d)
+                    amax = fabsf(x[d]) > amax ? fabsf(x[d]) : amax;
+                float s = amax > 0.0f ? amax / 448.0f : 1.0f; /* fp32 quotient */
+                ((float *)k_scale)[row] = s;
+                for (int d = 0; d < D; ++d) {
+                    float v = x[d] / s; /* fp32 quotient */
+                    ((uint8_t *)k_cache)[row * D + d] = e4m3_of(v);
+                }
+            } else {
+                for (int blk = 0; blk < D / 32; ++blk) {
+                    float amax = 0.0f;
+                    for (int d = 32 * blk; d < 32 * blk + 32; ++d)
+                        amax = fabsf(x[d]) > amax ? fabsf(x[d]) : amax;
+                    int e = 0;
+                    if (amax > 0.0f) {
+                        int ex;
+                        frexp(amax, &ex);
+                        e = ex - 1 - 8; /* floor(log2 amax) minus e4m3's largest exponent */
+                        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+                    }
+                    ((uint8_t *)k_scale)[row * (D / 32) + blk] = (uint8_t)(e + 127);
+                    for (int d = 32 * blk; d < 32 * blk + 32; ++d)
+                        ((uint8_t *)k_cache)[row * D + d] = e4m3_of(ldexp((double)x[d], -e)); /* exact scaling */
+                }
+            }
+        }
+    }
+    free(x);
+    return 0;
+}

@@ -93,6 +93,25 @@ int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
                            const int32_t *idx, int K,
                            double *out, double *lse, int nthreads);
 
+/* Encode one fp32 value: e4m3 (nearest even, saturating at +-448, the sign
+ * kept on zero) and bf16 (nearest even). */
+uint8_t dsa_oracle_encode_e4m3(float x);
+uint16_t dsa_oracle_encode_bf16(float x);
+
+/* Cache append: the n_b new keys of request b (k_new rows q_offsets[b] ..,
+ * [T][D] fp32 or bf16, src_dtype 0 or 1) are written to positions
+ * L_b - n_b + j of the paged K pool in dst_dtype: fp32 copied; bf16 rounded
+ * to nearest even; fp8 with a per-token fp32 scale amax / 448 (1 for a zero
+ * key) into k_scale [num_pages][page_size] and codes of the fp32 quotients;
+ * MXFP8 with one E8M0 byte per 32-element block (exponent floor(log2 amax)
+ * - 8, 0 for a zero block) into k_scale [num_pages][page_size][D/32] and codes
+ * of x * 2^-exponent.  Codes round to nearest even and saturate at +-448.
+ * Every other slot of the pools is left as it was. */
+int dsa_oracle_cache_append(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
+                            const int32_t *block_table, int bt_stride, int page_size, int D,
+                            int src_dtype, const void *k_new, int dst_dtype,
+                            void *k_cache, void *k_scale);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,11 @@ def _load():
         _lib.dsa_oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
         _lib.dsa_oracle_decode_e8m0.restype = ctypes.c_double
         _lib.dsa_oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+        _lib.dsa_oracle_encode_e4m3.restype = ctypes.c_uint8
+        _lib.dsa_oracle_encode_e4m3.argtypes = [ctypes.c_float]
+        _lib.dsa_oracle_encode_bf16.restype = ctypes.c_uint16
+        _lib.dsa_oracle_encode_bf16.argtypes = [ctypes.c_float]
+        _lib.dsa_oracle_cache_append.argtypes = [I, P, P, P, I, I, I, I, P, I, P, P]
         _lib.dsa_oracle_visible.argtypes = [I, P, P, P]
         _lib.dsa_oracle_scores.argtypes = [I, P, P, P, I, I, I, I, I, P, P, P, P, P, I, P, I]
         _lib.dsa_oracle_select.argtypes = [I, I, P, P, I, P, I]
@@ -113,6 +118,35 @@ def decode_e4m3(code: int) -> float:
 
 def decode_e8m0(code: int) -> float:
     return _load().dsa_oracle_decode_e8m0(int(code))
+
+
+def encode_e4m3(x: float) -> int:
+    return int(_load().dsa_oracle_encode_e4m3(float(x)))
+
+
+def encode_bf16(x: float) -> int:
+    return int(_load().dsa_oracle_encode_bf16(float(x)))
+
+
+def cache_append(q_offsets, ctx_lens, block_table, page_size, src_dtype, k_new, dst_dtype, k_cache,
+                 k_scale=None):
+    """The pools after appending k_new ([T][D] fp32, or bf16 bits as uint16)
+    at positions L_b - n_b + j: returns new (k_cache, k_scale) arrays; the
+    arguments are not modified."""
+    q_offsets, ctx_lens, bt = _i32(q_offsets), _i32(ctx_lens), _i32(block_table)
+    if bt.ndim != 2:
+        raise ValueError("block_table must be [B][max_pages]")
+    kn = _raw(k_new, src_dtype)
+    kc = _raw(k_cache, dst_dtype).copy()
+    ks = None if k_scale is None else _scales(k_scale, dst_dtype).copy()
+    D = kn.shape[-1]
+    if kc.shape[-1] != D:
+        raise ValueError("k_new and k_cache dims differ")
+    rc = _load().dsa_oracle_cache_append(len(ctx_lens), _ptr(q_offsets), _ptr(ctx_lens), _ptr(bt), bt.shape[1],
+                                         int(page_size), D, DTYPES[src_dtype], _ptr(kn), DTYPES[dst_dtype],
+                                         _ptr(kc), _ptr(ks))
+    _check(rc, "cache_append")
+    return kc, ks
 
 
 def _scales(a, dtype):

@@ -494,6 +494,150 @@ def check_sfa_uses_scale():
     assert not np.allclose(o1, o3, rtol=1e-6, atol=1e-9)
 
 
+# ---------------------------------------------------------------------------
+# encoding (the cache append's rounding) and the cache append itself
+# ---------------------------------------------------------------------------
+def _torch_e4m3(x32):
+    """torch's fp32 -> float8_e4m3fn cast (round to nearest even), raw bytes."""
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def check_encode_e4m3_against_torch():
+    """e4m3 encoding: every finite code round-trips; midpoints between
+    neighbouring codes, their fp32 neighbours and random values in [-448, 448]
+    round as torch's cast does (nearest, ties to even); beyond 448 saturates
+    to 0x7E / 0xFE (torch gives NaN there, so that part is the closed form)."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = _decoded(codes, "fp8")
+    finite = ~np.isnan(vals)
+    for c, v in zip(codes[finite], vals[finite]):
+        assert oracle.encode_e4m3(v) == c, f"code {c:#x} ({v}) does not round-trip"
+    pos = np.unique(vals[finite & (vals >= 0)])
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    probe = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                            -mids, np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 2.0 ** -9 * 1.5])])
+    rng = np.random.default_rng(41)
+    mag = np.exp2(rng.uniform(-12, np.log2(448), 4000)).astype(np.float32)
+    probe = np.concatenate([probe, mag * rng.choice(np.float32([-1, 1]), mag.size)]).astype(np.float32)
+    probe = probe[np.abs(probe) <= 448]
+    ref = _torch_e4m3(probe)
+    got = np.array([oracle.encode_e4m3(v) for v in probe], dtype=np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"e4m3 encoding differs from torch at {probe[bad[:5]]}: {got[bad[:5]]} vs {ref[bad[:5]]}"
+    for v in (448.5, 463.9, 464.0, 500.0, 1e6, 3e38):
+        assert oracle.encode_e4m3(v) == 0x7E and oracle.encode_e4m3(-v) == 0xFE, f"no saturation at {v}"
+
+
+def check_encode_bf16_against_torch():
+    """bf16 encoding equals torch's fp32 -> bfloat16 cast (nearest, ties to
+    even), on random values and on exact ties (low 16 bits 0x8000)."""
+    rng = np.random.default_rng(42)
+    bits = rng.integers(0, 2 ** 32, 3000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[((bits >> 23) & 0xFF) < 0xFE]  # finite, away from overflow
+    ties = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([bits, ties]).view(np.float32)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.encode_bf16(v) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, ref), "bf16 encoding differs from torch's cast"
+
+
+def _append_layout(seed, page_size=16):
+    """Three requests whose new keys cross page boundaries, a shuffled block
+    table and pools pre-filled with a sentinel (data movement only)."""
+    rng = np.random.default_rng(seed)
+    ctx = np.array([70, 5, 130], dtype=np.int32)
+    n_q = np.array([3, 5, 66], dtype=np.int32)
+    qo = np.concatenate([[0], np.cumsum(n_q)]).astype(np.int32)
+    npg = (ctx + page_size - 1) // page_size
+    perm = rng.permutation(int(npg.sum()) + 3)
+    bt = np.zeros((3, int(npg.max()) + 1), dtype=np.int32)
+    k = 0
+    for b in range(3):
+        bt[b, :npg[b]] = perm[k:k + npg[b]]
+        k += npg[b]
+    return qo, ctx, bt, len(perm), rng
+
+
+def _append_positions(qo, ctx, bt, page_size):
+    """(row of k_new, page, slot) of every new key: position L - n + j."""
+    out = []
+    for b in range(len(ctx)):
+        n = qo[b + 1] - qo[b]
+        for j in range(n):
+            p = ctx[b] - n + j
+            out.append((qo[b] + j, bt[b, p // page_size], p % page_size))
+    return out
+
+
+def check_cache_append():
+    """Cache append: key j of request b lands at position L_b - n_b + j through
+    the block table and nothing else changes; fp32 is copied, bf16 equals
+    torch's cast; fp8 scales are numpy's fp32 amax / 448 (1 for a zero key) and
+    codes torch's cast of the fp32 quotients; MXFP8 scale bytes are
+    127 + floor(log2 amax) - 8 from math.frexp (127 for a zero block) and codes
+    torch's cast of x * 2^-(that exponent), the same as the input generator's
+    MXFP8 quantizer; bf16 sources give what their fp32 values give."""
+    P, D = 16, 64
+    qo, ctx, bt, npages, rng = _append_layout(5, P)
+    T = int(qo[-1])
+    x = (rng.standard_normal((T, D)) * np.exp2(rng.integers(-6, 7, (T, 1)))).astype(np.float32)
+    x[2] = 0.0           # a zero key
+    x[7, 32:] = 0.0      # a zero MXFP8 block
+    x[9, 5] = 1e4        # one large element
+    # keys where x / scale formed in fp32 lands exactly on an e4m3 midpoint
+    # (ties to even) while the exact quotient lies just off it: found by a
+    # search over fp32 values, they tell an fp32 quotient from an fp64 one
+    for r, (am, v) in ((4, (64.0592041015625, 0.6077045202255249)), (6, (54.81887435913086, 3.303816080093384))):
+        x[r] = np.clip(x[r], -3, 3)
+        x[r, 0], x[r, 1] = am, v
+    where = _append_positions(qo, ctx, bt, P)
+    args = (qo, ctx, bt, P)
+
+    kc, _ = oracle.cache_append(*args, "f32", x, "f32", np.full((npages, P, D), -7.0, np.float32))
+    seen = np.zeros((npages, P), bool)
+    for i, pg, sl in where:
+        assert np.array_equal(kc[pg, sl], x[i]), f"key {i} not at its position"
+        seen[pg, sl] = True
+    assert np.all(kc[~seen] == -7.0), "an untouched slot changed"
+
+    kc, _ = oracle.cache_append(*args, "f32", x, "bf16", np.zeros((npages, P, D), np.uint16))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for i, pg, sl in where:
+        assert np.array_equal(kc[pg, sl], ref[i]), f"bf16 key {i}"
+
+    kc, ks = oracle.cache_append(*args, "f32", x, "fp8", np.zeros((npages, P, D), np.uint8),
+                                 np.full((npages, P), -1.0, np.float32))
+    amax = np.abs(x).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    for i, pg, sl in where:
+        assert ks[pg, sl] == scale[i], f"fp8 scale of key {i}: {ks[pg, sl]} vs {scale[i]}"
+        q32 = (torch.from_numpy(x[i]) / torch.tensor(scale[i])).clamp(-448, 448).numpy()
+        assert np.array_equal(kc[pg, sl], _torch_e4m3(q32)), f"fp8 codes of key {i}"
+    assert np.all(ks[~seen] == -1.0)
+
+    kc, ks = oracle.cache_append(*args, "f32", x, "mxfp8", np.zeros((npages, P, D), np.uint8),
+                                 np.full((npages, P, D // 32), 3, np.uint8))
+    gen_codes, gen_e = inputs.quantize_mxfp8(torch.from_numpy(x))
+    for i, pg, sl in where:
+        for blk in range(D // 32):
+            xb = x[i, 32 * blk:32 * blk + 32]
+            am = float(np.abs(xb).max())
+            e = math.frexp(am)[1] - 1 - 8 if am > 0 else 0
+            assert ks[pg, sl, blk] == 127 + e, f"E8M0 byte of key {i} block {blk}"
+            ref = _torch_e4m3(np.clip(np.ldexp(xb.astype(np.float64), -e), -448, 448).astype(np.float32))
+            assert np.array_equal(kc[pg, sl, 32 * blk:32 * blk + 32], ref), f"MXFP8 codes of key {i} block {blk}"
+        assert np.array_equal(kc[pg, sl], gen_codes[i].numpy()) and np.array_equal(ks[pg, sl], gen_e[i].numpy())
+    assert np.all(ks[~seen] == 3)
+
+    xb16 = torch.from_numpy(x).to(torch.bfloat16)
+    a1 = oracle.cache_append(*args, "bf16", xb16.view(torch.int16).numpy().view(np.uint16), "fp8",
+                             np.zeros((npages, P, D), np.uint8), np.zeros((npages, P), np.float32))
+    a2 = oracle.cache_append(*args, "f32", xb16.float().numpy(), "fp8",
+                             np.zeros((npages, P, D), np.uint8), np.zeros((npages, P), np.float32))
+    assert np.array_equal(a1[0], a2[0]) and np.array_equal(a1[1], a2[1])
+
+
 ALL_CHECKS = [
     check_decode_e4m3_all_codes,
     check_decode_e8m0_all_codes,
@@ -505,6 +649,9 @@ ALL_CHECKS = [
     check_one_hot_query_reads_key_element,
     check_fp8_scales,
     check_mxfp8_block_scales,
+    check_encode_e4m3_against_torch,
+    check_encode_bf16_against_torch,
+    check_cache_append,
     check_causal_visibility,
     check_selection_definition,
     check_selection_signed_zero_and_nesting,

@@ -61,6 +61,19 @@ MUTANTS = [
     ("sfa_lse_without_max", "lse[(size_t)i * H + h] = m + log(l);", "lse[(size_t)i * H + h] = log(l);"),
     ("sfa_padding_read", "if (t < 0)\n                    continue;\n                double p",
      "if (t < 0)\n                    t = 0;\n                double p"),
+    ("encode_ties_away", "return nearbyint(a / q) * q;", "return round(a / q) * q;"),
+    ("encode_truncates", "return nearbyint(a / q) * q;", "return floor(a / q) * q;"),
+    ("e4m3_no_saturation", "if (r > 448.0)\n        r = 448.0;", "if (r > 480.0)\n        r = 480.0;"),
+    ("e4m3_subnormal_step", "r / ldexp(1.0, -9)", "r / ldexp(1.0, -8)"),
+    ("bf16_six_bits", "round_to_grid(fabs((double)x), 7, -126)", "round_to_grid(fabs((double)x), 6, -126)"),
+    ("append_at_front", "int p = L - n + j;", "int p = j;"),
+    ("append_physical_page", "int page = block_table[(size_t)b * bt_stride + p / page_size];\n            size_t row",
+     "int page = p / page_size;\n            size_t row"),
+    ("fp8_scale_over_240", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 240.0f : 1.0f"),
+    ("fp8_zero_key_scale_0", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax / 448.0f"),
+    ("fp8_quotient_in_fp64", "float v = x[d] / s;", "double v = (double)x[d] / s;"),
+    ("mx_exponent_minus_7", "e = ex - 1 - 8;", "e = ex - 1 - 7;"),
+    ("mx_zero_block_byte_0", "int e = 0;\n                    if (amax > 0.0f)", "int e = -127;\n                    if (amax > 0.0f)"),
 ]
 
 
