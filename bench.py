@@ -296,6 +296,33 @@ def stage_breakdown(step: Step, steps, stream):
     return idx, sfa
 
 
+def cache_append_timing(case: inputs.Case, steps: int, stream):
+    """dsa_indexer_cache_append of the step's new keys (one per query token,
+    fp32 in) into a copy of the K pool in the workload's indexer dtype: the
+    producer step before the indexer, `steps` calls replayed as one HIP graph
+    and timed with HIP events on the replay stream.  Algorithmic bytes: the fp32 keys read, the stored keys and their
+    scales written, and the paging entries read."""
+    T, D = case.num_tokens, case.head_dim_idx
+    g = torch.Generator(device=case.q_idx.device)
+    g.manual_seed(7)
+    k_new = torch.randn((T, D), generator=g, device=case.q_idx.device)
+    kc = case.k_cache.clone()
+    ks = None if case.k_scale is None else case.k_scale.clone()
+    paged = dsa.make_paged(case.q_offsets, case.ctx_lens, case.block_table, case.num_pages,
+                           max_q_per_req=case.max_q_per_req, max_ctx_len=case.max_ctx, num_q_tokens=T)
+    ap = dsa.make_cache_append(k_new, "f32", kc, case.idx_dtype, k_scale=ks)
+    fn = lambda s, st: dsa.cache_append(paged, ap, stream=st)  # noqa: E731
+    ms = time_graph(fn, steps, 3)  # one graph replay: no host launch gaps
+    nbytes = T * D * 4 + T * (D * elem_bytes(case.idx_dtype) + scale_bytes(case.idx_dtype, D)) + T * 4 \
+        + case.batch * 12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"kernel": "li_cache_append", "keys": T, "dtype": f"f32->{case.idx_dtype}", "ms": ms,
+           "algorithmic_bytes": nbytes, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": gbs / HBM_PEAK_GBS}
+    del kc, ks, k_new
+    return out
+
+
 def prefill_scoring(steps: int, warmup: int, stream):
     """MFMA utilisation of the indexer's scoring kernel on the chunked-prefill
     shape (4096 rows x 64 heads x 128 bf16 against 65536 positions, causal):
@@ -450,6 +477,7 @@ def main():
         "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa, **kernels_ms},
         "roofline": roofline,
+        "cache_append": cache_append_timing(case, args.steps, stream),
         "kernel_source_hash": kernel_source_hash(),
     }
     if args.prefill_steps and args.workload != "chunked_prefill":

@@ -166,6 +166,43 @@ dsa_status_t dsa_indexer_topk(const dsa_paged_t *paged, const dsa_indexer_t *idx
 dsa_status_t dsa_indexer_scores(const dsa_paged_t *paged, const dsa_indexer_t *idx,
                                 float *scores, int64_t score_stride, void *stream);
 
+/* Indexer cache append: writes each new token's indexer key into the paged K
+ * pool, quantized for a low-precision indexer ("Optimizing Inference for
+ * Hybrid Attention Architectures: From Operator Fusion to Sequence
+ * Sharding", section "Breaking Down the Computational Path of Hybrid
+ * Attention", where the normalised key of a new token goes to the indexer's
+ * K cache; section "Layered Quantization: Distinguishing Precision
+ * Sensitivity" for the MXFP8 grouping).
+ * The n_b new keys of request b (rows q_offsets[b] .. q_offsets[b+1]-1 of
+ * k_new) are its query tokens: key j goes to position p = L_b - n_b + j, page
+ * block_table[b][p / 64], slot p % 64, where dsa_indexer_topk reads it.
+ * Per dst_dtype:
+ *   F32: copied.  BF16: rounded to nearest even.
+ *   FP8_E4M3: k_scale[page][slot] = amax / 448 in fp32 (1 for a zero key);
+ *     codes = e4m3 of the fp32 quotient x / scale.
+ *   MXFP8 (head_dim 128): per 32-element block, exponent e = floor(log2
+ *     amax) - 8 (0 for a zero block), k_scale byte e + 127; codes = e4m3 of
+ *     x * 2^-e.
+ *   e4m3 codes round to nearest even, saturate at +-448 and keep the sign
+ *   of zero.
+ * Other slots are not touched.  A key whose position or page falls outside
+ * [0, max_ctx_len) or [0, num_pages) is skipped.  Needs no workspace.  An
+ * append and an indexer call that reads the same pages must be ordered by
+ * the caller (one stream).  INVALID_ARG for NULL pointers or bad dtypes;
+ * UNSUPPORTED for head_dim other than 64 or 128 (MXFP8: 128). */
+typedef struct {
+    int32_t head_dim;          /* D_I */
+    int32_t src_dtype;         /* DSA_F32 or DSA_BF16 */
+    int32_t dst_dtype;         /* dsa_dtype_t of the cache */
+    const void *k_new;         /* [T][D_I] */
+    void *k_cache;             /* [num_pages][64][D_I] */
+    void *k_scale;             /* FP8_E4M3: fp32 [num_pages][64]; MXFP8: E8M0
+                                  bytes [num_pages][64][D_I/32]; else NULL */
+} dsa_cache_append_t;
+
+dsa_status_t dsa_indexer_cache_append(const dsa_paged_t *paged, const dsa_cache_append_t *append,
+                                      void *stream);
+
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_t *paged, const dsa_sfa_t *sfa,
                                       int32_t topk);
 

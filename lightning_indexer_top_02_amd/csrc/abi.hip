@@ -295,6 +295,35 @@ dsa_status_t dsa_indexer_scores(const dsa_paged_t* pg, const dsa_indexer_t* x, f
   return dsa_launch_indexer_scores(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
+dsa_status_t dsa_indexer_cache_append(const dsa_paged_t* pg, const dsa_cache_append_t* x, void* stream) {
+  if (!valid_paged(pg) || !x || !x->k_new || !x->k_cache) return DSA_ERR_INVALID_ARG;
+  if (x->src_dtype != DSA_F32 && x->src_dtype != DSA_BF16) return DSA_ERR_INVALID_ARG;
+  if (x->dst_dtype != DSA_F32 && x->dst_dtype != DSA_BF16 && x->dst_dtype != DSA_FP8_E4M3 &&
+      x->dst_dtype != DSA_MXFP8)
+    return DSA_ERR_INVALID_ARG;
+  if ((x->dst_dtype == DSA_FP8_E4M3 || x->dst_dtype == DSA_MXFP8) && !x->k_scale) return DSA_ERR_INVALID_ARG;
+  if (x->head_dim != 64 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (x->dst_dtype == DSA_MXFP8 && x->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  dsa_status_t st = check_device();
+  if (st != DSA_OK) return st;
+  DsaAppendLaunch a;
+  a.q_offsets = pg->q_offsets;
+  a.ctx_lens = pg->ctx_lens;
+  a.block_table = pg->block_table;
+  a.batch = pg->batch;
+  a.max_q_per_req = pg->max_q_per_req;
+  a.max_ctx_len = pg->max_ctx_len;
+  a.bt_stride = pg->max_pages_per_req;
+  a.num_pages = pg->num_pages;
+  a.head_dim = x->head_dim;
+  a.src_dtype = x->src_dtype;
+  a.dst_dtype = x->dst_dtype;
+  a.k_new = x->k_new;
+  a.k_cache = x->k_cache;
+  a.k_scale = x->k_scale;
+  return dsa_launch_cache_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) {
   if (check_sfa(pg, s, topk) != DSA_OK) return 0;
   return plan_sfa(pg, s, topk).total;

@@ -159,7 +159,19 @@ struct DsaSfaLaunch {
 // Let `kernel` use `bytes` of dynamic LDS on the current device (above the
 // default 64 KB).  The attribute is set once per (device, kernel, size) and
 // remembered, so launches do not pay for it every call.
+struct DsaAppendLaunch {
+  const int32_t* q_offsets;
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  int batch, max_q_per_req, max_ctx_len, bt_stride, num_pages;
+  int head_dim, src_dtype, dst_dtype;
+  const void* k_new;
+  void* k_cache;
+  void* k_scale;
+};
+
 hipError_t dsa_allow_lds(const void* kernel, size_t bytes);
+hipError_t dsa_launch_cache_append(const DsaAppendLaunch& a, hipStream_t s);
 
 hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s);

@@ -84,6 +84,17 @@ class Sfa(ctypes.Structure):
     ]
 
 
+class CacheAppend(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32),
+        ("src_dtype", ctypes.c_int32),
+        ("dst_dtype", ctypes.c_int32),
+        ("k_new", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -114,6 +125,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_fused_decode_workspace_size.argtypes = [PP, PI, PS]
         lib.dsa_fused_decode.restype = ctypes.c_int
         lib.dsa_fused_decode.argtypes = [PP, PI, PS, P, P, S, P]
+        lib.dsa_indexer_cache_append.restype = ctypes.c_int
+        lib.dsa_indexer_cache_append.argtypes = [PP, ctypes.POINTER(CacheAppend), P]
         lib.dsa_workspace_init.restype = ctypes.c_int
         lib.dsa_workspace_init.argtypes = [P, S, P]
         _lib = lib
@@ -248,6 +261,23 @@ def indexer_scores(paged: Paged, idx: Indexer, scores: torch.Tensor, stream=None
     if st != DSA_OK:
         raise DsaError(st, "dsa_indexer_scores")
     return scores
+
+
+def make_cache_append(k_new, src_dtype, k_cache, dst_dtype, k_scale=None) -> CacheAppend:
+    _check_tensor(k_new, "k_new", _STORAGE[src_dtype])
+    _check_tensor(k_cache, "k_cache", _STORAGE[dst_dtype])
+    _check_tensor(k_scale, "k_scale", (torch.uint8,) if dst_dtype == "mxfp8" else (torch.float32,))
+    D = k_new.shape[-1]
+    if k_cache.shape[-1] != D:
+        raise ValueError("k_new and k_cache dims differ")
+    return CacheAppend(D, DTYPE_CODE[src_dtype], DTYPE_CODE[dst_dtype], _ptr(k_new), _ptr(k_cache), _ptr(k_scale))
+
+
+def cache_append(paged: Paged, append: CacheAppend, stream=None):
+    """dsa_indexer_cache_append: each request's new keys into its K-pool slots."""
+    st = load().dsa_indexer_cache_append(ctypes.byref(paged), ctypes.byref(append), _stream(stream))
+    if st != DSA_OK:
+        raise DsaError(st, "dsa_indexer_cache_append")
 
 
 def sparse_attn_workspace_size(paged: Paged, sfa: Sfa, topk: int) -> int:

@@ -379,3 +379,75 @@ def permute_pages(case: Case, seed: int) -> Case:
     return dataclasses.replace(
         case, block_table=bt, decoy_pages=perm[case.decoy_pages],
         k_cache=move(case.k_cache), k_scale=move(case.k_scale), kv_cache=move(case.kv_cache))
+
+
+# ---------------------------------------------------------------------------
+# Cache-append inputs: new keys and the paging they go into
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class AppendCase:
+    name: str
+    seed: int
+    q_offsets: torch.Tensor   # int32 [B+1]
+    ctx_lens: torch.Tensor    # int32 [B]
+    block_table: torch.Tensor  # int32 [B][max_pages]
+    num_pages: int
+    max_q_per_req: int
+    max_ctx: int
+    k_new: torch.Tensor       # float32 [T][D]
+
+
+def e4m3_midpoints() -> torch.Tensor:
+    """Every midpoint between neighbouring positive finite e4m3 values, and
+    the fp32 values just below and above each (values on which rounding to
+    nearest even decides)."""
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    pos = torch.unique(vals[torch.isfinite(vals) & (vals >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    return torch.cat([mids, torch.nextafter(mids, torch.zeros_like(mids)),
+                      torch.nextafter(mids, torch.full_like(mids, 1e9))])
+
+
+def append_case(seed: int, ctx_lens, n_q, head_dim: int, name: str = "append", device="cpu",
+                page_size: int = PAGE_SIZE, n_decoy: int = 3) -> AppendCase:
+    """New keys for requests of lengths ``ctx_lens`` whose last ``n_q`` tokens
+    are new, with shuffled pages (plus decoy pages nothing maps to).  Rows are
+    N(0,1) times 2^k (k uniform in -6..6), except directed rows when there are
+    enough: a zero key, a key with a zero upper half, keys whose every 32-block
+    holds 448 (so the fp8 scale and the MXFP8 exponents are 1 and 0) and
+    otherwise e4m3 midpoints and their fp32 neighbours of both signs, and two
+    keys where x / (amax / 448) in fp32 falls exactly on a midpoint that the
+    exact quotient misses."""
+    g = torch.Generator()
+    g.manual_seed(int(seed))
+    lens = torch.tensor(list(ctx_lens), dtype=torch.int32)
+    nq = torch.tensor(list(n_q) if hasattr(n_q, "__len__") else [n_q] * len(lens), dtype=torch.int32)
+    B = len(lens)
+    qo = torch.zeros(B + 1, dtype=torch.int32)
+    qo[1:] = torch.cumsum(nq, 0)
+    T, D = int(qo[-1]), int(head_dim)
+    ppr = [(int(L) + page_size - 1) // page_size for L in lens]
+    num_pages = sum(ppr) + n_decoy
+    perm = torch.randperm(num_pages, generator=g).to(torch.int32)
+    bt = torch.full((B, max(ppr) + 1), int(perm[-1]), dtype=torch.int32)
+    cur = 0
+    for b in range(B):
+        bt[b, :ppr[b]] = perm[cur:cur + ppr[b]]
+        cur += ppr[b]
+    x = torch.randn((T, D), generator=g) * torch.exp2(torch.randint(-6, 7, (T, 1), generator=g).float())
+    mids = e4m3_midpoints()
+    if T >= 8:
+        x[0] = 0.0
+        x[1, D // 2:] = 0.0
+        for r in (2, 3):
+            pick = mids[torch.randint(0, mids.numel(), (D,), generator=g)]
+            sign = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
+            x[r] = pick * sign
+            x[r, ::32] = 448.0
+        for r, (am, v) in ((4, (64.0592041015625, 0.6077045202255249)), (5, (54.81887435913086, 3.303816080093384))):
+            x[r] = x[r].clamp(-3, 3)
+            x[r, 0], x[r, 1] = am, v
+    mx = int(nq.max())
+    return AppendCase(name=name, seed=int(seed), q_offsets=qo.to(device), ctx_lens=lens.to(device),
+                      block_table=bt.to(device), num_pages=num_pages, max_q_per_req=mx,
+                      max_ctx=int(lens.max()), k_new=x.contiguous().to(device))

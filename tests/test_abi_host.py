@@ -165,3 +165,18 @@ def test_indexer_scores_argument_checks():
     assert lib.dsa_indexer_scores(ctypes.byref(good_paged()), ctypes.byref(good_indexer()), sc, short, None) == 1
     assert lib.dsa_indexer_scores(ctypes.byref(good_paged()), ctypes.byref(good_indexer(n_heads=65)), sc,
                                   1 << 20, None) == 2
+
+
+def test_cache_append_argument_checks():
+    lib = dsa.load()
+
+    def call(paged=None, **kw):
+        a = dict(head_dim=128, src_dtype=0, dst_dtype=2, k_new=FAKE, k_cache=FAKE, k_scale=FAKE)
+        a.update(kw)
+        return lib.dsa_indexer_cache_append(ctypes.byref(paged or good_paged()), ctypes.byref(dsa.CacheAppend(**a)),
+                                            None)
+    assert call(k_new=None) == 1 and call(k_cache=None) == 1
+    assert call(k_scale=None) == 1 and call(dst_dtype=3, k_scale=None) == 1  # quantized without scales
+    assert call(src_dtype=2) == 1 and call(src_dtype=3) == 1 and call(dst_dtype=4) == 1
+    assert call(head_dim=96) == 2 and call(dst_dtype=3, head_dim=64) == 2
+    assert call(paged=good_paged(page_size=32)) == 1 and call(paged=good_paged(batch=0)) == 1

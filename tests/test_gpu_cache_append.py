@@ -1,0 +1,115 @@
+"""GPU parity of the indexer cache append (dsa_indexer_cache_append) with the
+CPU oracle: the whole pools after the append (new slots and untouched ones)
+must be bit-identical, since every stored value is an integer decision (a
+code, a scale, a rounded bf16) taken from the same fp32 values."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from lightning_indexer_top_02_amd import dsa, inputs
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = {"f32": (-7.0, None), "bf16": (0x1234, None), "fp8": (0x55, -1.0), "mxfp8": (0x55, 3)}
+STORE = {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8, "mxfp8": torch.uint8}
+
+
+def _pools(case, D, dst):
+    fill, sfill = SENTINEL[dst]
+    kc = torch.full((case.num_pages, 64, D), fill, dtype=STORE[dst])
+    ks = None
+    if dst == "fp8":
+        ks = torch.full((case.num_pages, 64), sfill, dtype=torch.float32)
+    elif dst == "mxfp8":
+        ks = torch.full((case.num_pages, 64, D // 32), sfill, dtype=torch.uint8)
+    return kc, ks
+
+
+def _src(case, src):
+    x = case.k_new.cpu()
+    return x.contiguous() if src == "f32" else x.to(torch.bfloat16).view(torch.int16).contiguous()
+
+
+def _gpu_append(case, src, dst, D):
+    kc, ks = _pools(case, D, dst)
+    kc, ks = kc.cuda(), None if ks is None else ks.cuda()
+    k_new = _src(case, src).cuda()
+    # the paging tensors stay referenced until the kernel has finished
+    qo, lens, bt = case.q_offsets.cuda(), case.ctx_lens.cuda(), case.block_table.cuda()
+    paged = dsa.make_paged(qo, lens, bt, case.num_pages, max_q_per_req=case.max_q_per_req, max_ctx_len=case.max_ctx)
+    dsa.cache_append(paged, dsa.make_cache_append(k_new, src, kc, dst, k_scale=ks))
+    torch.cuda.synchronize()
+    del qo, lens, bt
+    return kc.cpu(), None if ks is None else ks.cpu()
+
+
+def _oracle_append(case, src, dst, D):
+    kc, ks = _pools(case, D, dst)
+    raw = inputs.to_numpy_raw(_src(case, src))
+    return oracle.cache_append(case.q_offsets.numpy(), case.ctx_lens.numpy(), case.block_table.numpy(), 64,
+                               src, raw, dst, inputs.to_numpy_raw(kc), inputs.to_numpy_raw(ks))
+
+
+def _check(case, src, dst, D):
+    print(f"\n[case] append {case.name} src={src} dst={dst} D={D} T={case.k_new.shape[0]}", flush=True)
+    g_kc, g_ks = _gpu_append(case, src, dst, D)
+    o_kc, o_ks = _oracle_append(case, src, dst, D)
+    g = inputs.to_numpy_raw(g_kc)
+    bad = np.argwhere(g.view(np.uint8) != np.ascontiguousarray(o_kc).view(np.uint8))
+    assert bad.size == 0, f"cache differs from the oracle at {bad[:4].tolist()}"
+    if o_ks is not None:
+        gs = inputs.to_numpy_raw(g_ks)
+        assert np.array_equal(gs.view(np.uint8), np.ascontiguousarray(o_ks).view(np.uint8)), "scales differ"
+    print(f"[ok] append {case.name} {src}->{dst}", flush=True)
+
+
+# Ragged requests: a 1-token request, keys crossing page boundaries, a whole
+# page, 200 keys at the end of a 1000-token request, directed rows (zeros,
+# e4m3 midpoints, fp32-quotient midpoints).
+LENS, NQ = [1, 70, 64, 1000, 300], [1, 3, 64, 200, 17]
+COMBOS = [(s, d, D) for s in ("f32", "bf16") for d in ("f32", "bf16", "fp8", "mxfp8") for D in (64, 128)
+          if not (d == "mxfp8" and D == 64)]
+
+
+@pytest.mark.parametrize("src,dst,D", COMBOS, ids=[f"{s}-{d}-{D}" for s, d, D in COMBOS])
+def test_cache_append_matches_oracle(src, dst, D):
+    _check(inputs.append_case(31, LENS, NQ, D, name="ragged"), src, dst, D)
+
+
+@pytest.mark.parametrize("dst", ["fp8", "mxfp8"])
+def test_cache_append_full_prefill_and_decode(dst):
+    """The chunked-prefill append (4096 keys at 61440..65535) and a 64-request
+    decode append (one key each at lengths up to 131072), as the step appends
+    them, checked whole."""
+    _check(inputs.append_case(32, [65536], [4096], 128, name="prefill_61440+4096"), "f32", dst, 128)
+    lens = inputs.batched_fp8_lengths(seed=33)
+    _check(inputs.append_case(33, lens, 1, 128, name="decode_b64"), "bf16", dst, 128)
+
+
+@pytest.mark.parametrize("dst", ["fp8", "mxfp8"])
+def test_appended_cache_feeds_the_indexer(dst):
+    """The indexer reading a cache the GPU appended gives the same indices as
+    on the oracle-appended cache, and those match the oracle's indexer."""
+    base = inputs.make_case(name=f"append_then_score_{dst}", seed=34, ctx_lens=[3000, 700], n_q=[4, 64],
+                            idx_dtype=dst, n_heads_idx=64, head_dim_idx=128, topk=256, sfa_dtype=None)
+    ap = inputs.append_case(35, [3000, 700], [4, 64], 128, name="append_then_score")
+    # the new keys go into the case's own pages (its block table), over its data
+    kc = base.k_cache.clone().cuda()
+    ks = base.k_scale.clone().cuda()
+    dev = parity.to_device(base)  # referenced until the end: the paging pointers live in it
+    k_new = ap.k_new.cuda()
+    paged = parity.paged_of(dev)
+    dsa.cache_append(paged, dsa.make_cache_append(k_new, "f32", kc, dst, k_scale=ks))
+    o_kc, o_ks = oracle.cache_append(base.q_offsets.numpy(), base.ctx_lens.numpy(), base.block_table.numpy(), 64,
+                                     "f32", ap.k_new.numpy(), dst, base.k_cache.numpy(), base.k_scale.numpy())
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), o_kc) and np.array_equal(ks.cpu().numpy().view(np.uint8),
+                                                                     np.ascontiguousarray(o_ks).view(np.uint8))
+    case = dataclasses.replace(dev, k_cache=kc, k_scale=ks)
+    idx = parity.gpu_indexer_topk(case)
+    stats = parity.check_rows(case, idx, None, list(range(case.num_tokens)))
+    print(f"[ok] {base.name}: {stats}", flush=True)
