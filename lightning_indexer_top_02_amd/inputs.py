@@ -124,6 +124,24 @@ def quantize_mxfp8(x: torch.Tensor):
     return codes.view(torch.uint8).reshape(shp), (e.squeeze(-1) + 127).to(torch.uint8).contiguous()
 
 
+def pack_latent_fp8(x: torch.Tensor, v_dim: int = V_DIM, unit_scales: bool = False) -> torch.Tensor:
+    """Producer-side fp8 latent rows: the first v_dim elements as e4m3 codes
+    with one fp32 scale per 128-element tile (amax / 448, 1 for a zero tile,
+    or 1 throughout with ``unit_scales``; saturating nearest-even casts), then
+    the tile scales, then the remaining (rope) elements as bf16.  Returns uint8
+    rows of v_dim + 4 v_dim/128 + 2 (dim - v_dim) bytes."""
+    lead, dim = x.shape[:-1], x.shape[-1]
+    tiles = x[..., :v_dim].float().reshape(*lead, v_dim // 128, 128)
+    amax = tiles.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    if unit_scales:
+        scale = torch.ones_like(scale)
+    codes = (tiles / scale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8).reshape(*lead, v_dim)
+    sbytes = scale.squeeze(-1).contiguous().view(torch.uint8)
+    rope = _bf16_bits(x[..., v_dim:].float()).contiguous().view(torch.uint8)
+    return torch.cat([codes, sbytes, rope], dim=-1).contiguous()
+
+
 def _draw(gen, shape, device, dist: str, std: float = 1.0, exact: bool = False):
     if exact:
         return torch.randint(-3, 4, shape, generator=gen, device=device).float()
@@ -239,9 +257,10 @@ def make_case(
     # ---- sparse-attention inputs -------------------------------------------
     q_sfa = kv_cache = None
     if sfa_dtype is not None:
-        q_sfa = _storage(_draw(gen, (T, n_heads_sfa, qk_dim), device, "normal", sfa_std, exact), sfa_dtype)
-        kv_cache = _storage(_draw(gen, (num_pages, page_size, qk_dim), device, "normal", sfa_std, exact),
-                            sfa_dtype)
+        q_store = "bf16" if sfa_dtype == "fp8" else sfa_dtype  # the fp8 latent route takes bf16 queries
+        q_sfa = _storage(_draw(gen, (T, n_heads_sfa, qk_dim), device, "normal", sfa_std, exact), q_store)
+        lat = _draw(gen, (num_pages, page_size, qk_dim), device, "normal", sfa_std, exact)
+        kv_cache = pack_latent_fp8(lat, v_dim, unit_scales=exact) if sfa_dtype == "fp8" else _storage(lat, sfa_dtype)
 
     # ---- poison everything no correct read touches -------------------------
     poison_pages = decoys.to(device)

@@ -322,6 +322,31 @@ int dsa_oracle_indexer_topk(int B, const int32_t *q_offsets, const int32_t *ctx_
  *     m = max z,  l = sum_t exp(z_t - m)
  *     out[i][h][e] = sum_t exp(z_t - m) * c_t[e] / l,   lse = m + ln l.
  * ------------------------------------------------------------------------- */
+/* Element d of latent row `row` (pool row: page * page_size + slot).  fp32
+ * and bf16 rows hold Dqk elements.  The fp8 latent row (dtype 2; "Day0
+ * Inference Optimization for Next-Generation Hybrid-Architecture LLMs Based
+ * on CANN", section 3.1, and "Optimizing Inference for Hybrid Attention
+ * Architectures: From Operator Fusion to Sequence Sharding", section
+ * "Layered Quantization: Distinguishing Precision Sensitivity": an fp8 KV
+ * cache with one scale per token and 128-element tile) is Dv e4m3 codes, then
+ * Dv/128 fp32 scales (tile j covers codes 128j .. 128j + 127), then the
+ * Dqk - Dv rope elements in bf16: Dv + 4 Dv/128 + 2 (Dqk - Dv) bytes. */
+static double latent_elem(const void *kv, size_t row, int d, int Dqk, int Dv, int dtype)
+{
+    if (dtype != 2)
+        return load_elem(kv, row * Dqk + d, dtype);
+    size_t row_bytes = (size_t)Dv + 4 * (size_t)(Dv / 128) + 2 * (size_t)(Dqk - Dv);
+    const unsigned char *r = (const unsigned char *)kv + row * row_bytes;
+    if (d < Dv) {
+        float s;
+        memcpy(&s, r + Dv + 4 * (d / 128), sizeof s);
+        return dsa_oracle_decode_e4m3(r[d]) * (double)s;
+    }
+    uint16_t bits;
+    memcpy(&bits, r + Dv + 4 * (Dv / 128) + 2 * (d - Dv), sizeof bits);
+    return dsa_oracle_decode_bf16(bits);
+}
+
 int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
                            const int32_t *block_table, int bt_stride, int page_size,
                            int H, int Dqk, int Dv, int dtype, double scale,
@@ -332,8 +357,11 @@ int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
     if (B < 0 || !q_offsets || !block_table || H <= 0 || Dqk <= 0 || Dv <= 0 || Dv > Dqk ||
         page_size <= 0 || !q || !kv_cache || !idx || K <= 0 || !out)
         return -1;
-    if (dtype != 0 && dtype != 1)
+    if (dtype != 0 && dtype != 1 && dtype != 2)
         return -1;
+    if (dtype == 2 && Dv % 128 != 0)
+        return -1;
+    int q_dtype = dtype == 2 ? 1 : dtype; /* the fp8 latent route takes bf16 queries */
     int T = q_offsets[B];
     set_threads(nthreads);
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -344,17 +372,17 @@ int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
             double *z = (double *)malloc(sizeof(double) * (size_t)K);
             double *qd = (double *)malloc(sizeof(double) * (size_t)Dqk);
             for (int d = 0; d < Dqk; ++d)
-                qd[d] = load_elem(q, ((size_t)i * H + h) * Dqk + d, dtype);
+                qd[d] = load_elem(q, ((size_t)i * H + h) * Dqk + d, q_dtype);
             double m = -INFINITY;
             for (int r = 0; r < K; ++r) {
                 int t = sel[r];
                 if (t < 0)
                     continue;
                 int page = block_table[(size_t)b * bt_stride + t / page_size];
-                size_t base = ((size_t)page * page_size + t % page_size) * Dqk;
+                size_t prow = (size_t)page * page_size + t % page_size;
                 double dot = 0.0;
                 for (int d = 0; d < Dqk; ++d)
-                    dot += qd[d] * load_elem(kv_cache, base + d, dtype);
+                    dot += qd[d] * latent_elem(kv_cache, prow, d, Dqk, Dv, dtype);
                 z[r] = scale * dot;
                 if (z[r] > m)
                     m = z[r];
@@ -370,9 +398,9 @@ int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
                 double p = exp(z[r] - m);
                 l += p;
                 int page = block_table[(size_t)b * bt_stride + t / page_size];
-                size_t base = ((size_t)page * page_size + t % page_size) * Dqk;
+                size_t prow = (size_t)page * page_size + t % page_size;
                 for (int e = 0; e < Dv; ++e)
-                    o[e] += p * load_elem(kv_cache, base + e, dtype);
+                    o[e] += p * latent_elem(kv_cache, prow, e, Dqk, Dv, dtype);
             }
             if (l > 0.0) {
                 for (int e = 0; e < Dv; ++e)

@@ -440,6 +440,58 @@ def check_sfa_dense_reduction():
                 assert np.allclose(lse[i], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def _dequant_latent_fp8(rows, v_dim, dim):
+    """fp8 latent rows (uint8 [..., bytes]) to float64 with torch's e4m3 and
+    bf16 casts and numpy's view of the fp32 tile scales."""
+    codes = _decoded(np.ascontiguousarray(rows[..., :v_dim]), "fp8")
+    scales = np.ascontiguousarray(rows[..., v_dim:v_dim + 4 * (v_dim // 128)]).view(np.float32).astype(np.float64)
+    rope = np.ascontiguousarray(rows[..., v_dim + 4 * (v_dim // 128):]).view(np.uint16)
+    lat = codes * np.repeat(scales, 128, axis=-1)
+    return np.concatenate([lat, _decoded(rope, "bf16")], axis=-1)
+
+
+def check_sfa_fp8_latent():
+    """fp8 latent cache (e4m3 codes, one fp32 scale per token and 128-element
+    tile, bf16 rope): selecting every visible position equals torch's
+    scaled_dot_product_attention and logsumexp in float64 on rows dequantized
+    with torch's casts; raising one tile's scale changes only the outputs of
+    rows that see that token."""
+    c = _small_case(19, dtype="f32", sfa_dtype="fp8", ctx=(33, 90), n_q=(2, 3), H_q=3, qk_dim=288, v_dim=256)
+    a = _np_case(c)
+    vis = oracle.visible(a["q_offsets"], a["ctx_lens"])
+    K = int(vis.max())
+    idx = np.full((len(vis), K), -1, dtype=np.int32)
+    for i, n in enumerate(vis):
+        idx[i, :n] = np.arange(n)
+    qs, kvs = _raw(c.q_sfa), _raw(c.kv_cache)
+    assert kvs.shape[-1] == 256 + 8 + 64 and qs.dtype == np.uint16
+    out, lse = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "fp8", c.scale, qs, kvs, idx,
+                                  c.v_dim)
+    qd = torch.from_numpy(_decoded(qs, "bf16"))
+    kvd = _dequant_latent_fp8(kvs, c.v_dim, c.qk_dim)
+    for b in range(len(a["ctx_lens"])):
+        rows = torch.from_numpy(_logical_rows(kvd, a["block_table"][b], int(a["ctx_lens"][b]), c.page_size))
+        for i in range(a["q_offsets"][b], a["q_offsets"][b + 1]):
+            n = int(vis[i])
+            kk, vv = rows[:n], rows[:n, : c.v_dim]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qd[i][:, None, :], kk[None].expand(qd.shape[1], -1, -1),
+                vv[None].expand(qd.shape[1], -1, -1), scale=c.scale)[:, 0, :]
+            assert np.allclose(out[i], ref.numpy(), rtol=1e-11, atol=1e-12), i
+            ref_lse = torch.logsumexp(c.scale * (qd[i] @ kk.T), dim=-1)
+            assert np.allclose(lse[i], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+    # tile 1 of request 0's token 5 doubled: only request 0's rows change
+    kv2 = kvs.copy()
+    pg, sl = a["block_table"][0][5 // c.page_size], 5 % c.page_size
+    sc = kv2[pg, sl, 256:264].view(np.float32)
+    sc[1] *= 2
+    out2, _ = oracle.sparse_attn(a["q_offsets"], a["block_table"], c.page_size, "fp8", c.scale, qs, kv2, idx,
+                                 c.v_dim)
+    changed = np.nonzero(np.any(out2 != out, axis=(1, 2)))[0]
+    assert set(changed.tolist()) == set(range(a["q_offsets"][0], a["q_offsets"][1]))
+    assert np.array_equal(out2[:, :, :128][a["q_offsets"][1]:], out[:, :, :128][a["q_offsets"][1]:])
+
+
 def check_sfa_zero_query_is_mean():
     """q = 0 gives equal weights: the output is the mean of the selected values."""
     c = _small_case(19, sfa_dtype="f32", H_q=2, qk_dim=10, v_dim=6)
@@ -658,6 +710,7 @@ ALL_CHECKS = [
     check_indexer_topk_full_context,
     check_page_permutation_invariance,
     check_sfa_dense_reduction,
+    check_sfa_fp8_latent,
     check_sfa_zero_query_is_mean,
     check_sfa_dominant_row,
     check_sfa_uses_scale,

@@ -24,7 +24,10 @@ import oracle
 from lightning_indexer_top_02_amd import dsa, inputs
 
 TOPK_BAND_REL = 1e-3
-OUT_TOL = {"bf16": 2e-2, "f32": 2e-2}
+# fp8 latent: bf16 output like the bf16 route; the kernel dequantizes each
+# code times its tile scale to bf16 (a relative error of at most 2^-9 per
+# element, the size of the bf16 rounding of P it already carries).
+OUT_TOL = {"bf16": 2e-2, "f32": 2e-2, "fp8": 2e-2}
 OUT_TOL_FP8_ROUTE = 6e-2
 
 
@@ -100,7 +103,7 @@ def gpu_fused_decode(case: inputs.Case):
 
 def out_to_f64(out: torch.Tensor, dtype: str) -> np.ndarray:
     o = out.detach().cpu()
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp8"):  # the fp8 latent route writes bf16
         o = o.view(torch.bfloat16)
     return o.double().numpy()
 

@@ -53,8 +53,12 @@ MUTANTS = [
     ("e4m3_no_nan", "if (e == 15 && m == 7)\n        return NAN;", ""),
     ("bf16_low_half", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits;"),
     ("sfa_scale_dropped", "z[r] = scale * dot;", "z[r] = dot;"),
-    ("sfa_value_from_tail", "o[e] += p * load_elem(kv_cache, base + e, dtype);",
-     "o[e] += p * load_elem(kv_cache, base + (Dqk - Dv) + e, dtype);"),
+    ("sfa_value_from_tail", "o[e] += p * latent_elem(kv_cache, prow, e, Dqk, Dv, dtype);",
+     "o[e] += p * latent_elem(kv_cache, prow, (Dqk - Dv) + e, Dqk, Dv, dtype);"),
+    ("kv8_tile_of_64", "memcpy(&s, r + Dv + 4 * (d / 128), sizeof s);", "memcpy(&s, r + Dv + 4 * ((d / 64) % 4), sizeof s);"),
+    ("kv8_scale_ignored", "return dsa_oracle_decode_e4m3(r[d]) * (double)s;", "return dsa_oracle_decode_e4m3(r[d]);"),
+    ("kv8_rope_without_scale_gap", "memcpy(&bits, r + Dv + 4 * (Dv / 128) + 2 * (d - Dv), sizeof bits);",
+     "memcpy(&bits, r + Dv + 2 * (d - Dv), sizeof bits);"),
     ("sfa_key_without_rope", "for (int d = 0; d < Dqk; ++d)\n                    dot += qd[d]",
      "for (int d = 0; d < Dv; ++d)\n                    dot += qd[d]"),
     ("sfa_not_normalised", "o[e] /= l;", "o[e] /= 1.0;"),
