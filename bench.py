@@ -40,6 +40,13 @@ WORKLOADS = {
         desc="DSA decode step: batch {batch}, 1 query token, context 32768 in 512 shuffled 64-token "
              "pages; indexer 64 heads x 128 bf16, Top-K 2048; sparse attention 128 heads x "
              "(512+64) bf16 latent, bf16 out, fp32 accumulation"),
+    "decode_32k_kv8": dict(
+        make=lambda dev, batch=1: inputs.decode_32k(batch=batch, device=dev, sfa_dtype="fp8",
+                                                    name=f"decode_32k_kv8_b{batch}"),
+        desc="DSA decode step: batch {batch}, 1 query token, context 32768 in 512 shuffled 64-token "
+             "pages; indexer 64 heads x 128 bf16, Top-K 2048; sparse attention 128 heads over an fp8 "
+             "latent cache (512 e4m3 + 4 fp32 tile scales + 64 bf16 rope = 656 bytes a row), bf16 q "
+             "and out, fp32 accumulation"),
     "tiny_decode": dict(
         make=lambda dev, batch=1: inputs.tiny_decode(device=dev),
         desc="DSA decode step: batch 1, context 4096, fp32 indexer 4 x 64, Top-K 256, fp32 "
@@ -121,10 +128,14 @@ def algorithmic_bytes(case: inputs.Case):
     idx_bytes = (sum(lens) * key_row + T * H * case.head_dim_idx * eK + T * H * (4 + sb)
                  + sum((L + 63) // 64 for L in lens) * 4 + T * K * 4)
     eS = elem_bytes(case.sfa_dtype) if case.sfa_dtype != "none" else 0
+    # latent row bytes; the fp8 latent route has bf16 q and out
+    row_bytes = (case.v_dim + 4 * (case.v_dim // 128) + 2 * (case.qk_dim - case.v_dim) if case.sfa_dtype == "fp8"
+                 else case.qk_dim * eS)
+    eIO = 2 if case.sfa_dtype == "fp8" else eS
     vis = visible_per_row(case)
     sel = sum(min(v, K) for v in vis)
     rows_read = sum(min(sum(min(v, K) for v in vis[qo[b]:qo[b + 1]]), lens[b]) for b in range(len(lens)))
-    sfa_bytes = (T * K * 4 + rows_read * case.qk_dim * eS + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eS)
+    sfa_bytes = (T * K * 4 + rows_read * row_bytes + T * case.n_heads_sfa * (case.qk_dim + case.v_dim) * eIO)
     idx_flops = 2 * sum(vis) * H * case.head_dim_idx
     sfa_flops = 2 * sel * case.n_heads_sfa * (case.qk_dim + case.v_dim)
     return {"indexer": idx_bytes, "sparse_attn": sfa_bytes, "total": idx_bytes + sfa_bytes,
@@ -454,7 +465,7 @@ def main():
                                   compute_peak(case.idx_dtype))
     else:
         roofline = roofline_entry("sparse_attn", args.workload, ab["sparse_attn"], ab["sparse_attn_flops"], t_sfa,
-                                  compute_peak(case.sfa_dtype))
+                                  compute_peak("bf16" if case.sfa_dtype == "fp8" else case.sfa_dtype))  # fp8 latent: bf16 MFMAs
     result = {
         "metric": METRIC,
         "value": tokens_per_s,

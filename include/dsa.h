@@ -129,16 +129,25 @@ typedef struct {
 
 /* Sparse flash attention over a shared MLA latent cache: the key of a
  * position is its whole row (qk_dim = 576 = 512 latent + 64 rope), the value
- * its first v_dim = 512 entries.  Supported: dtype F32 or BF16,
- * qk_dim 576, v_dim 512, n_heads a multiple of 16 up to 128. */
+ * its first v_dim = 512 entries.  Supported: dtype F32, BF16 or FP8_E4M3,
+ * qk_dim 576, v_dim 512, n_heads a multiple of 16 up to 128.
+ * FP8_E4M3 is the fp8 latent cache ("Day0 Inference Optimization for
+ * Next-Generation Hybrid-Architecture LLMs Based on CANN", section 3.1: one
+ * scale per token and 128-element tile): each 656-byte row holds the 512
+ * latent dims as e4m3 codes, then four fp32 scales (scale j for dims
+ * 128j .. 128j + 127), then the 64 rope dims as bf16; q and out are bf16.
+ * The kernel rounds each code times its scale to bf16 before the products
+ * (relative error at most 2^-9 per element). */
 typedef struct {
     int32_t n_heads;           /* H_q */
     int32_t qk_dim;            /* 576 */
     int32_t v_dim;             /* 512 */
-    int32_t dtype;             /* DSA_F32 or DSA_BF16 (q, kv_cache and out) */
+    int32_t dtype;             /* DSA_F32 or DSA_BF16 (q, kv_cache and out),
+                                  or DSA_FP8_E4M3 (fp8 latent rows, bf16 q/out) */
     float scale;               /* softmax scale, e.g. 1/sqrt(576) */
     const void *q;             /* [T][H_q][qk_dim] */
-    const void *kv_cache;      /* [num_pages][64][qk_dim] */
+    const void *kv_cache;      /* [num_pages][64][qk_dim] (FP8_E4M3: [num_pages][64]
+                                  656-byte rows, 16-byte aligned) */
     void *out;                 /* [T][H_q][v_dim], same dtype */
     float *lse;                /* [T][H_q] natural-log sum-exp, or NULL */
 } dsa_sfa_t;

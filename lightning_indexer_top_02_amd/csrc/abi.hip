@@ -65,7 +65,7 @@ dsa_status_t check_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) 
   if (!s->q || !s->kv_cache || !s->out) return DSA_ERR_INVALID_ARG;
   if (topk < 1 || s->n_heads < 1 || s->qk_dim < 1 || s->v_dim < 1 || s->v_dim > s->qk_dim)
     return DSA_ERR_INVALID_ARG;
-  if (s->dtype != DSA_F32 && s->dtype != DSA_BF16) return DSA_ERR_INVALID_ARG;
+  if (s->dtype != DSA_F32 && s->dtype != DSA_BF16 && s->dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
   if (!std::isfinite(s->scale)) return DSA_ERR_INVALID_ARG;
   if (s->qk_dim != dsa::kQkDim || s->v_dim != dsa::kVDim) return DSA_ERR_UNSUPPORTED;
   if (s->n_heads % 16 != 0 || s->n_heads > kSfaMaxHeads || topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
@@ -117,7 +117,7 @@ struct SfaPlan {
 
 SfaPlan plan_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int topk) {
   SfaPlan p{1, topk, 1, 0, 0, 0};
-  if (s->dtype == DSA_BF16) {
+  if (s->dtype == DSA_BF16 || s->dtype == DSA_FP8_E4M3) {  // the fp8 latent route shares the bf16 kernel
     p.nw = sfa_waves(s->n_heads, pg->num_q_tokens);
     const int64_t blocks = (int64_t)pg->num_q_tokens * (s->n_heads / (16 * p.nw));
     // about one workgroup per compute unit: a bf16 SFA workgroup of four

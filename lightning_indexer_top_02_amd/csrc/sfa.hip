@@ -87,6 +87,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kKrowBytes = kSfaRows * kRowStride;
 constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chunk
 
+// fp8 latent rows in HBM ("Day0 Inference Optimization for Next-Generation
+// Hybrid-Architecture LLMs Based on CANN", section 3.1: an fp8 KV cache with
+// a scale per token and 128-element tile): the 512 latent dims as e4m3 codes,
+// their four fp32 tile scales, then the 64 rope dims in bf16, 656 bytes.  A
+// chunk is gathered as 40 pieces per row (32 of codes, each with its tile's
+// scale, and 8 of rope) and staged in the same bf16 LDS layout as the bf16
+// route: each code times its scale is rounded to bf16 (relative error at
+// most 2^-9), so everything after the staging is shared.
+constexpr int kF8RowBytes = kVDim + 4 * (kVDim / 128) + 2 * (kQkDim - kVDim);
+constexpr int kF8CodePieces = kVDim / 16;
+constexpr int kF8RowItems = kF8CodePieces + (kQkDim - kVDim) * 2 / 16;
+constexpr int kF8Items = kSfaRows * kF8RowItems;
+static_assert(kF8RowBytes % 16 == 0, "fp8 latent rows stay 16-byte aligned");
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -108,10 +122,10 @@ struct SfaXchg {
   float lsum[2][4][16];   // [half][head tile][head]
 };
 
-template <int NW>
+template <int NW, bool F8>
 __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   constexpr int NT = NW * 128;
-  constexpr int PPT = (kPieces + NT - 1) / NT;  // 16-byte pieces per thread per chunk
+  constexpr int PPT = ((F8 ? kF8Items : kPieces) + NT - 1) / NT;  // gathered pieces per thread per chunk
   constexpr int kHalfDims = kVDim / 2;
   extern __shared__ __align__(16) unsigned char smem[];
   SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + 2 * kKrowBytes);
@@ -161,23 +175,57 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   __syncthreads();
 
   // gather of one chunk into registers: PPT 16-byte pieces of its rows
+  // (fp8: code pieces with their tile scales, and rope pieces)
   uint4 va[PPT];
+  float vs[F8 ? PPT : 1];
+  const unsigned char* kv8 = static_cast<const unsigned char*>(p.kv);
   auto gather = [&](int c0) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int it = tid + j * NT;
-      const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
-      const int row = it < kPieces ? rowidx[c0 + r] : -1;
-      va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + part * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (F8) {
+        const int r = it / kF8RowItems, part = it - r * kF8RowItems;
+        const int row = it < kF8Items ? rowidx[c0 + r] : -1;
+        const unsigned char* rb = kv8 + (int64_t)max(row, 0) * kF8RowBytes;
+        const bool code = part < kF8CodePieces;
+        const int off = code ? part * 16 : kVDim + 4 * (kVDim / 128) + (part - kF8CodePieces) * 16;
+        va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + off) : make_uint4(0u, 0u, 0u, 0u);
+        vs[j] = row >= 0 && code ? *reinterpret_cast<const float*>(rb + kVDim + 4 * (part >> 3)) : 0.f;
+      } else {
+        const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
+        const int row = it < kPieces ? rowidx[c0 + r] : -1;
+        va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + part * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
   auto stage = [&](unsigned char* kb) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int it = tid + j * NT;
-      const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
-      if (it < kPieces) *reinterpret_cast<uint4*>(kb + r * kRowStride + part * 16) = va[j];
+      if constexpr (F8) {
+        const int r = it / kF8RowItems, part = it - r * kF8RowItems;
+        if (it >= kF8Items) continue;
+        if (part < kF8CodePieces) {  // 16 codes -> 16 bf16 values (32 bytes)
+          const uint32_t w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+          uint32_t o8[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+            o8[2 * k] = pack_bf16x2(lo[0] * vs[j], lo[1] * vs[j]);
+            o8[2 * k + 1] = pack_bf16x2(hi[0] * vs[j], hi[1] * vs[j]);
+          }
+          uint4* d = reinterpret_cast<uint4*>(kb + r * kRowStride + part * 32);
+          d[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+          d[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+        } else {  // rope: already bf16
+          *reinterpret_cast<uint4*>(kb + r * kRowStride + kVDim * 2 + (part - kF8CodePieces) * 16) = va[j];
+        }
+      } else {
+        const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
+        if (it < kPieces) *reinterpret_cast<uint4*>(kb + r * kRowStride + part * 16) = va[j];
+      }
     }
   };
 
@@ -451,14 +499,24 @@ __global__ __launch_bounds__(kF32Threads) void sfa_f32(SfaParams p) {
 
 using namespace dsa;
 
-template <int NW>
+template <int NW, bool F8>
 static hipError_t launch_sfa(dim3 grid, size_t lds, hipStream_t s, const SfaParams& p) {
   {
-    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(sfa_bf16<NW>), lds);
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(sfa_bf16<NW, F8>), lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(sfa_bf16<NW>, grid, dim3(NW * 128), lds, s, p);
+  hipLaunchKernelGGL((sfa_bf16<NW, F8>), grid, dim3(NW * 128), lds, s, p);
   return hipGetLastError();
+}
+
+template <bool F8>
+static hipError_t launch_sfa_nw(int nw, dim3 grid, size_t lds, hipStream_t s, const SfaParams& p) {
+  switch (nw) {
+    case 1: return launch_sfa<1, F8>(grid, lds, s, p);
+    case 2: return launch_sfa<2, F8>(grid, lds, s, p);
+    case 3: return launch_sfa<3, F8>(grid, lds, s, p);
+    default: return launch_sfa<4, F8>(grid, lds, s, p);
+  }
 }
 
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
@@ -496,12 +554,7 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   hipError_t e0;
   const size_t lds = (size_t)2 * kKrowBytes + sizeof(SfaXchg) +
                      (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
-  switch (nw) {
-    case 1: e0 = launch_sfa<1>(grid, lds, s, p); break;
-    case 2: e0 = launch_sfa<2>(grid, lds, s, p); break;
-    case 3: e0 = launch_sfa<3>(grid, lds, s, p); break;
-    default: e0 = launch_sfa<4>(grid, lds, s, p); break;
-  }
+  e0 = a.dtype == 2 ? launch_sfa_nw<true>(nw, grid, lds, s, p) : launch_sfa_nw<false>(nw, grid, lds, s, p);
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;

@@ -105,7 +105,8 @@ def test_indexer_null_output_rejected():
     assert call_indexer(good_paged(), good_indexer(), out=None) == 1
 
 
-BAD_SFA = [(dict(q=None), 1), (dict(kv_cache=None), 1), (dict(out=None), 1), (dict(dtype=2), 1),
+BAD_SFA = [(dict(q=None), 1), (dict(kv_cache=None), 1), (dict(out=None), 1), (dict(dtype=3), 1),
+           (dict(dtype=2, qk_dim=512), 2),
            (dict(v_dim=600), 1), (dict(scale=float("nan")), 1), (dict(qk_dim=512), 2),
            (dict(n_heads=24), 2), (dict(n_heads=144), 2)]
 

@@ -77,6 +77,20 @@ def test_ragged_narrow(dtype, exact):
                           n_heads_sfa=16, sfa_std=1.0))
 
 
+# fp8 latent cache for the sparse attention (bf16 indexer), every head-tile
+# width the kernel picks (16 heads: one tile; 128 heads at one row: one tile
+# per workgroup; several rows: four)
+@pytest.mark.parametrize("heads", [16, 64, 128])
+@pytest.mark.parametrize("exact", [True, False], ids=["exact", "float"])
+def test_sfa_fp8_latent(heads, exact):
+    _run(inputs.make_case(name=f"kv8_ragged_{heads}h", seed=96, ctx_lens=RAGGED, n_q=RAGGED_NQ, idx_dtype="bf16",
+                          n_heads_idx=64, head_dim_idx=128, topk=256, exact=exact, sfa_dtype="fp8",
+                          n_heads_sfa=heads))
+    _run(inputs.make_case(name=f"kv8_one_row_{heads}h", seed=97, ctx_lens=[5000], n_q=1, idx_dtype="bf16",
+                          n_heads_idx=64, head_dim_idx=128, topk=2048, exact=exact, sfa_dtype="fp8",
+                          n_heads_sfa=heads))
+
+
 @pytest.mark.parametrize("heads", [5, 17, 48])
 def test_odd_indexer_head_counts(heads):
     _run(inputs.make_case(name=f"heads{heads}", seed=79, ctx_lens=[5000, 777], n_q=[1, 2],
@@ -188,6 +202,13 @@ def test_scratch_prefill_full():
     """A prefill from scratch: 16384 causal query rows, row i sees i + 1 positions."""
     case = inputs.chunked_prefill(device="cuda", prefix=0, new=16384, name="prefill_0+16384_bf16")
     _full(case, [0, 1, 7, 8, 2046, 2047, 2048, 9001, 16383])
+
+
+@pytest.mark.parametrize("batch", [1, 64])
+def test_decode_32k_fp8_latent_full(batch):
+    """The 32K decode with the fp8 latent cache, one and 64 requests."""
+    case = inputs.decode_32k(batch=batch, device="cuda", sfa_dtype="fp8", name=f"decode_32k_kv8_b{batch}")
+    _full(case, [0] if batch == 1 else [0, 31, 63], routes=False)
 
 
 def test_spec_verify_full():
