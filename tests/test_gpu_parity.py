@@ -217,6 +217,20 @@ def test_spec_verify_full():
     _full(case, [0, 3, 17, 38, 60, 63], routes=False)
 
 
+def test_spec_verify_mxfp8_full():
+    """The speculative-verify shape with an MXFP8 indexer: 16 requests x 4
+    causal rows at 262144 positions (two-pass route, four rows per key read)."""
+    case = inputs.spec_verify(device="cuda", idx_dtype="mxfp8", name="spec_verify_mxfp8")
+    _full(case, [0, 3, 17, 38, 60, 63], routes=False)
+
+
+def test_prefill_mxfp8_full():
+    """The chunked prefill (4096 rows over 65536 positions) with an MXFP8
+    indexer: the row-tiled kernel at full size, every route."""
+    case = inputs.chunked_prefill(device="cuda", idx_dtype="mxfp8", name="prefill_61440+4096_mxfp8")
+    _full(case, [0, 1, 1000, 2047, 3333, 4095])
+
+
 @pytest.mark.parametrize("wide", [False, True], ids=["narrow", "wide"])
 def test_batched_fp8_full(wide):
     """64 single-row requests, lengths uniform in [4096, 131072], fp8 indexer."""
