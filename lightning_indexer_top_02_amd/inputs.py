@@ -126,20 +126,25 @@ def quantize_mxfp8(x: torch.Tensor):
 
 def pack_latent_fp8(x: torch.Tensor, v_dim: int = V_DIM, unit_scales: bool = False) -> torch.Tensor:
     """Producer-side fp8 latent rows: the first v_dim elements as e4m3 codes
-    with one fp32 scale per 128-element tile (amax / 448, 1 for a zero tile,
-    or 1 throughout with ``unit_scales``; saturating nearest-even casts), then
-    the tile scales, then the remaining (rope) elements as bf16.  Returns uint8
-    rows of v_dim + 4 v_dim/128 + 2 (dim - v_dim) bytes."""
+    with one power-of-two scale per 128-element tile, 2^e with e the smallest
+    integer such that amax / 2^e <= 448 (e = 0 for a zero tile, or throughout
+    with ``unit_scales``; clamped to [-126, 127]), codes = nearest-even casts
+    of x / 2^e (saturating); then a 16-byte block holding the tiles' E8M0
+    bytes e + 127; then the remaining (rope) elements as bf16.  Returns uint8
+    rows of v_dim + 16 + 2 (dim - v_dim) bytes."""
     lead, dim = x.shape[:-1], x.shape[-1]
     tiles = x[..., :v_dim].float().reshape(*lead, v_dim // 128, 128)
     amax = tiles.abs().amax(dim=-1, keepdim=True)
-    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax.clamp_min(1e-38) / FP8_MAX)), torch.zeros_like(amax))
     if unit_scales:
-        scale = torch.ones_like(scale)
-    codes = (tiles / scale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8).reshape(*lead, v_dim)
-    sbytes = scale.squeeze(-1).contiguous().view(torch.uint8)
+        e = torch.zeros_like(e)
+    e = e.clamp(-126, 127)
+    codes = (tiles / torch.exp2(e)).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = codes.reshape(*lead, v_dim)
+    eblock = torch.zeros((*lead, 16), dtype=torch.uint8, device=x.device)
+    eblock[..., : v_dim // 128] = (e.squeeze(-1) + 127).to(torch.uint8)
     rope = _bf16_bits(x[..., v_dim:].float()).contiguous().view(torch.uint8)
-    return torch.cat([codes, sbytes, rope], dim=-1).contiguous()
+    return torch.cat([codes, eblock, rope], dim=-1).contiguous()
 
 
 def _draw(gen, shape, device, dist: str, std: float = 1.0, exact: bool = False):

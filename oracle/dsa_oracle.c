@@ -329,21 +329,19 @@ int dsa_oracle_indexer_topk(int B, const int32_t *q_offsets, const int32_t *ctx_
  * Architectures: From Operator Fusion to Sequence Sharding", section
  * "Layered Quantization: Distinguishing Precision Sensitivity": an fp8 KV
  * cache with one scale per token and 128-element tile) is Dv e4m3 codes, then
- * Dv/128 fp32 scales (tile j covers codes 128j .. 128j + 127), then the
- * Dqk - Dv rope elements in bf16: Dv + 4 Dv/128 + 2 (Dqk - Dv) bytes. */
+ * a 16-byte block holding Dv/128 E8M0 scale bytes (tile j covers codes
+ * 128j .. 128j + 127; the rest of the block is unused), then the Dqk - Dv
+ * rope elements in bf16: Dv + 16 + 2 (Dqk - Dv) bytes. */
 static double latent_elem(const void *kv, size_t row, int d, int Dqk, int Dv, int dtype)
 {
     if (dtype != 2)
         return load_elem(kv, row * Dqk + d, dtype);
-    size_t row_bytes = (size_t)Dv + 4 * (size_t)(Dv / 128) + 2 * (size_t)(Dqk - Dv);
+    size_t row_bytes = (size_t)Dv + 16 + 2 * (size_t)(Dqk - Dv);
     const unsigned char *r = (const unsigned char *)kv + row * row_bytes;
-    if (d < Dv) {
-        float s;
-        memcpy(&s, r + Dv + 4 * (d / 128), sizeof s);
-        return dsa_oracle_decode_e4m3(r[d]) * (double)s;
-    }
+    if (d < Dv)
+        return dsa_oracle_decode_e4m3(r[d]) * dsa_oracle_decode_e8m0(r[Dv + d / 128]);
     uint16_t bits;
-    memcpy(&bits, r + Dv + 4 * (Dv / 128) + 2 * (d - Dv), sizeof bits);
+    memcpy(&bits, r + Dv + 16 + 2 * (d - Dv), sizeof bits);
     return dsa_oracle_decode_bf16(bits);
 }
 
@@ -359,7 +357,7 @@ int dsa_oracle_sparse_attn(int B, const int32_t *q_offsets,
         return -1;
     if (dtype != 0 && dtype != 1 && dtype != 2)
         return -1;
-    if (dtype == 2 && Dv % 128 != 0)
+    if (dtype == 2 && (Dv % 128 != 0 || Dv / 128 > 16))
         return -1;
     int q_dtype = dtype == 2 ? 1 : dtype; /* the fp8 latent route takes bf16 queries */
     int T = q_offsets[B];

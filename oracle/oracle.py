@@ -227,7 +227,8 @@ def sparse_attn(q_offsets, block_table, page_size, dtype, scale, q, kv_cache, id
                 nthreads=None):
     """Returns (out fp64 [T][H][v_dim], lse fp64 [T][H]).  dtype "fp8": bf16
     queries and fp8 latent rows as uint8 [pages][page_size][row bytes]
-    (v_dim e4m3 codes, v_dim/128 fp32 tile scales, the rope dims in bf16)."""
+    (v_dim e4m3 codes, a 16-byte block of v_dim/128 E8M0 tile scales, the rope
+    dims in bf16)."""
     q_offsets, block_table, idx = _i32(q_offsets), _i32(block_table), _i32(idx)
     B = len(q_offsets) - 1
     T, H, Dqk = q.shape
@@ -235,8 +236,8 @@ def sparse_attn(q_offsets, block_table, page_size, dtype, scale, q, kv_cache, id
     out = np.empty((T, H, v_dim), dtype=np.float64)
     lse = np.empty((T, H), dtype=np.float64)
     q, kv_cache = _raw(q, "bf16" if dtype == "fp8" else dtype), _raw(kv_cache, dtype)
-    if dtype == "fp8" and kv_cache.shape[-1] != v_dim + 4 * (v_dim // 128) + 2 * (Dqk - v_dim):
-        raise ValueError("fp8 latent rows must be v_dim codes + v_dim/128 fp32 scales + bf16 rope")
+    if dtype == "fp8" and kv_cache.shape[-1] != v_dim + 16 + 2 * (Dqk - v_dim):
+        raise ValueError("fp8 latent rows must be v_dim codes + a 16-byte E8M0 scale block + bf16 rope")
     rc = _load().dsa_oracle_sparse_attn(B, _ptr(q_offsets), _ptr(block_table), block_table.shape[1],
                                         page_size, H, Dqk, v_dim, DTYPES[dtype], float(scale),
                                         _ptr(q), _ptr(kv_cache), _ptr(idx), K, _ptr(out), _ptr(lse),

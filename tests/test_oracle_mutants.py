@@ -55,9 +55,10 @@ MUTANTS = [
     ("sfa_scale_dropped", "z[r] = scale * dot;", "z[r] = dot;"),
     ("sfa_value_from_tail", "o[e] += p * latent_elem(kv_cache, prow, e, Dqk, Dv, dtype);",
      "o[e] += p * latent_elem(kv_cache, prow, (Dqk - Dv) + e, Dqk, Dv, dtype);"),
-    ("kv8_tile_of_64", "memcpy(&s, r + Dv + 4 * (d / 128), sizeof s);", "memcpy(&s, r + Dv + 4 * ((d / 64) % 4), sizeof s);"),
-    ("kv8_scale_ignored", "return dsa_oracle_decode_e4m3(r[d]) * (double)s;", "return dsa_oracle_decode_e4m3(r[d]);"),
-    ("kv8_rope_without_scale_gap", "memcpy(&bits, r + Dv + 4 * (Dv / 128) + 2 * (d - Dv), sizeof bits);",
+    ("kv8_tile_of_64", "dsa_oracle_decode_e8m0(r[Dv + d / 128])", "dsa_oracle_decode_e8m0(r[Dv + (d / 64) % (Dv / 128)])"),
+    ("kv8_scale_ignored", "return dsa_oracle_decode_e4m3(r[d]) * dsa_oracle_decode_e8m0(r[Dv + d / 128]);",
+     "return dsa_oracle_decode_e4m3(r[d]);"),
+    ("kv8_rope_without_scale_gap", "memcpy(&bits, r + Dv + 16 + 2 * (d - Dv), sizeof bits);",
      "memcpy(&bits, r + Dv + 2 * (d - Dv), sizeof bits);"),
     ("sfa_key_without_rope", "for (int d = 0; d < Dqk; ++d)\n                    dot += qd[d]",
      "for (int d = 0; d < Dv; ++d)\n                    dot += qd[d]"),
