@@ -45,8 +45,14 @@ WORKLOADS = {
                                                     name=f"decode_32k_kv8_b{batch}"),
         desc="DSA decode step: batch {batch}, 1 query token, context 32768 in 512 shuffled 64-token "
              "pages; indexer 64 heads x 128 bf16, Top-K 2048; sparse attention 128 heads over an fp8 "
-             "latent cache (512 e4m3 + 4 fp32 tile scales + 64 bf16 rope = 656 bytes a row), bf16 q "
+             "latent cache (512 e4m3 + 16-byte block of E8M0 tile exponents + 64 bf16 rope = 656 bytes a "
+             "row), bf16 q "
              "and out, fp32 accumulation"),
+    "batched_fp8_narrow_kv8": dict(
+        make=lambda dev, batch=64: inputs.batched_decode_fp8(device=dev, batch=batch, sfa_dtype="fp8",
+                                                             name="batched_fp8_narrow_kv8"),
+        desc="DSA decode step: batch {batch}, contexts U[4096,131072], fp8 indexer 4 x 64, Top-K 2048, "
+             "sparse attention 16 heads over an fp8 latent cache (656-byte rows), bf16 q and out"),
     "tiny_decode": dict(
         make=lambda dev, batch=1: inputs.tiny_decode(device=dev),
         desc="DSA decode step: batch 1, context 4096, fp32 indexer 4 x 64, Top-K 256, fp32 "
@@ -129,7 +135,7 @@ def algorithmic_bytes(case: inputs.Case):
                  + sum((L + 63) // 64 for L in lens) * 4 + T * K * 4)
     eS = elem_bytes(case.sfa_dtype) if case.sfa_dtype != "none" else 0
     # latent row bytes; the fp8 latent route has bf16 q and out
-    row_bytes = (case.v_dim + 4 * (case.v_dim // 128) + 2 * (case.qk_dim - case.v_dim) if case.sfa_dtype == "fp8"
+    row_bytes = (case.v_dim + 16 + 2 * (case.qk_dim - case.v_dim) if case.sfa_dtype == "fp8"
                  else case.qk_dim * eS)
     eIO = 2 if case.sfa_dtype == "fp8" else eS
     vis = visible_per_row(case)

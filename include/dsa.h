@@ -134,10 +134,10 @@ typedef struct {
  * FP8_E4M3 is the fp8 latent cache ("Day0 Inference Optimization for
  * Next-Generation Hybrid-Architecture LLMs Based on CANN", section 3.1: one
  * scale per token and 128-element tile): each 656-byte row holds the 512
- * latent dims as e4m3 codes, then four fp32 scales (scale j for dims
- * 128j .. 128j + 127), then the 64 rope dims as bf16; q and out are bf16.
- * The kernel rounds each code times its scale to bf16 before the products
- * (relative error at most 2^-9 per element). */
+ * latent dims as e4m3 codes, then a 16-byte block whose byte j is the E8M0
+ * exponent E_j of dims 128j .. 128j + 127 (value = code * 2^(E_j - 127);
+ * E_j in 1 .. 254; the other 12 bytes are unused), then the 64 rope dims as
+ * bf16; q and out are bf16.  code * 2^(E - 127) is exact in bf16. */
 typedef struct {
     int32_t n_heads;           /* H_q */
     int32_t qk_dim;            /* 576 */

@@ -90,12 +90,15 @@ constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chu
 // fp8 latent rows in HBM ("Day0 Inference Optimization for Next-Generation
 // Hybrid-Architecture LLMs Based on CANN", section 3.1: an fp8 KV cache with
 // a scale per token and 128-element tile): the 512 latent dims as e4m3 codes,
-// their four fp32 tile scales, then the 64 rope dims in bf16, 656 bytes.  A
-// chunk is gathered as 40 pieces per row (32 of codes, each with its tile's
-// scale, and 8 of rope) and staged in the same bf16 LDS layout as the bf16
-// route: each code times its scale is rounded to bf16 (relative error at
-// most 2^-9), so everything after the staging is shared.
-constexpr int kF8RowBytes = kVDim + 4 * (kVDim / 128) + 2 * (kQkDim - kVDim);
+// a 16-byte block whose first four bytes are the tiles' E8M0 exponents
+// (power-of-two scales), then the 64 rope dims in bf16, 656 bytes.  A chunk
+// is gathered as 40 pieces per row (32 of codes, each with its tile's
+// exponent, and 8 of rope) and staged in the same bf16 LDS layout as the bf16
+// route, so everything after the staging is shared.  code * 2^e is exact in
+// bf16, and gfx950's scaled conversion (v_cvt_scalef32_pk_bf16_fp8, which
+// applies the exponent of its fp32 scale operand) makes two values per
+// instruction.
+constexpr int kF8RowBytes = kVDim + 16 + 2 * (kQkDim - kVDim);
 constexpr int kF8CodePieces = kVDim / 16;
 constexpr int kF8RowItems = kF8CodePieces + (kQkDim - kVDim) * 2 / 16;
 constexpr int kF8Items = kSfaRows * kF8RowItems;
@@ -188,9 +191,11 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
         const int row = it < kF8Items ? rowidx[c0 + r] : -1;
         const unsigned char* rb = kv8 + (int64_t)max(row, 0) * kF8RowBytes;
         const bool code = part < kF8CodePieces;
-        const int off = code ? part * 16 : kVDim + 4 * (kVDim / 128) + (part - kF8CodePieces) * 16;
+        const int off = code ? part * 16 : kVDim + 16 + (part - kF8CodePieces) * 16;
         va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + off) : make_uint4(0u, 0u, 0u, 0u);
-        vs[j] = row >= 0 && code ? *reinterpret_cast<const float*>(rb + kVDim + 4 * (part >> 3)) : 0.f;
+        // the tile's scale 2^(E - 127) as an fp32 (exponent field E, E in 1 .. 254)
+        const uint32_t ew = row >= 0 && code ? *reinterpret_cast<const uint32_t*>(rb + kVDim) : 0u;
+        vs[j] = __uint_as_float(((ew >> (8 * (part >> 3))) & 0xFFu) << 23);
       } else {
         const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
         const int row = it < kPieces ? rowidx[c0 + r] : -1;
@@ -210,11 +215,9 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
           const uint32_t w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
           uint32_t o8[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-            o8[2 * k] = pack_bf16x2(lo[0] * vs[j], lo[1] * vs[j]);
-            o8[2 * k + 1] = pack_bf16x2(hi[0] * vs[j], hi[1] * vs[j]);
+          for (int k = 0; k < 4; ++k) {  // codes 4k, 4k + 1 (low half), 4k + 2, 4k + 3 (high half)
+            o8[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], vs[j], false));
+            o8[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], vs[j], true));
           }
           uint4* d = reinterpret_cast<uint4*>(kb + r * kRowStride + part * 32);
           d[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);

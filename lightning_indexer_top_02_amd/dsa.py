@@ -201,14 +201,15 @@ def make_indexer(q, weights, k_cache, topk, dtype, q_scale=None, k_scale=None, f
 
 def make_sfa(q, kv_cache, out, scale, dtype, lse=None, v_dim=512) -> Sfa:
     """dtype "fp8": bf16 q and out, kv_cache uint8 [pages][64][656] fp8
-    latent rows (512 e4m3 codes, 4 fp32 tile scales, 64 bf16 rope dims)."""
+    latent rows (512 e4m3 codes, a 16-byte block of 4 E8M0 tile exponents,
+    64 bf16 rope dims)."""
     io = "bf16" if dtype == "fp8" else dtype
     _check_tensor(q, "q", _STORAGE[io])
     _check_tensor(kv_cache, "kv_cache", (torch.uint8,) if dtype == "fp8" else _STORAGE[dtype])
     _check_tensor(out, "out", _STORAGE[io])
     _check_tensor(lse, "lse", (torch.float32,))
     T, H, Dqk = q.shape
-    row = v_dim + 4 * (v_dim // 128) + 2 * (Dqk - v_dim) if dtype == "fp8" else Dqk
+    row = v_dim + 16 + 2 * (Dqk - v_dim) if dtype == "fp8" else Dqk
     if out.shape != (T, H, v_dim) or kv_cache.shape[-1] != row:
         raise ValueError("sparse-attention shapes disagree")
     return Sfa(H, Dqk, v_dim, DTYPE_CODE[dtype], float(scale), _ptr(q), _ptr(kv_cache), _ptr(out),
