@@ -19,7 +19,7 @@
  *   s_t = sum_h w_h * max(q_h . k_t, 0)
  * the tie rule (equal scores: the lower position wins), the causal visibility
  * rule and the output order (ascending positions, then -1) are the readings
- * adopted for this build.  Every floating-point step runs in fp64.
+ * this oracle takes from that prose.  Every floating-point step runs in fp64.
  *
  * Storage conventions (identical to the GPU library's, restated here so the
  * oracle stands alone):
