@@ -113,3 +113,33 @@ def test_appended_cache_feeds_the_indexer(dst):
     idx = parity.gpu_indexer_topk(case)
     stats = parity.check_rows(case, idx, None, list(range(case.num_tokens)))
     print(f"[ok] {base.name}: {stats}", flush=True)
+
+
+def test_cache_append_graph_replays_match_eager():
+    """The append captured in a HIP graph: three replays, each after the pools
+    are reset eagerly, every one equal to the eager append."""
+    case = inputs.append_case(36, LENS, NQ, 128, name="graph")
+    qo, lens, bt = case.q_offsets.cuda(), case.ctx_lens.cuda(), case.block_table.cuda()
+    paged = dsa.make_paged(qo, lens, bt, case.num_pages, max_q_per_req=case.max_q_per_req, max_ctx_len=case.max_ctx)
+    k_new = case.k_new.cuda()
+    kc0, ks0 = (t.cuda() for t in _pools(case, 128, "mxfp8"))
+    kc, ks = kc0.clone(), ks0.clone()
+    ap = dsa.make_cache_append(k_new, "f32", kc, "mxfp8", k_scale=ks)
+    dsa.cache_append(paged, ap)
+    torch.cuda.synchronize()
+    ref_c, ref_s = kc.clone(), ks.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dsa.cache_append(paged, ap, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        kc.copy_(kc0)
+        ks.copy_(ks0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(kc, ref_c) and torch.equal(ks, ref_s), f"replay {rep} differs from the eager append"
+    del g
+    print("[ok] append graph replays", flush=True)
