@@ -506,6 +506,11 @@ def main():
         if step is None:
             step = Step(case, 1)
         result["cpu_baseline"] = cpu_baseline(case, step, args.cpu_budget)
+        if result["cpu_baseline"]["parity_vs_gpu"] != "ok":
+            # a result that fails the correctness gate yields no throughput figure
+            result["value"] = None
+            print(json.dumps(result), flush=True)
+            sys.exit(1)
     print(json.dumps(result), flush=True)
 
 

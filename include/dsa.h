@@ -91,9 +91,10 @@ typedef struct {
     const int32_t *block_table;/* device [B][max_pages_per_req] */
 } dsa_paged_t;
 
-/* Lightning indexer.  Supported: dtype F32 with head_dim % 4 == 0 and
- * n_heads*head_dim <= 4096; BF16 or FP8_E4M3 with head_dim in {64, 128};
- * MXFP8 with head_dim 128; 1 <= n_heads <= 64; 1 <= topk <= 4096. */
+/* Lightning indexer.  Supported: head_dim in {64, 128} for F32, BF16 and
+ * FP8_E4M3 (F32 also needs n_heads*head_dim <= 4096); MXFP8 with head_dim
+ * 128; 1 <= n_heads <= 64; 1 <= topk <= 4096.  Anything else returns
+ * DSA_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t n_heads;           /* H_I */
     int32_t head_dim;          /* D_I */
@@ -132,7 +133,7 @@ typedef struct {
  * its first v_dim = 512 entries.  Supported: dtype F32, BF16 or FP8_E4M3,
  * qk_dim 576, v_dim 512, n_heads a multiple of 16 up to 128.
  * FP8_E4M3 is the fp8 latent cache ("Day0 Inference Optimization for
- * Next-Generation Hybrid-Architecture LLMs Based on CANN", section 3.1: one
+ * Next-Generation Hybrid-Architecture LLMs Based on CANN", section 3.2: one
  * scale per token and 128-element tile): each 656-byte row holds the 512
  * latent dims as e4m3 codes, then a 16-byte block whose byte j is the E8M0
  * exponent E_j of dims 128j .. 128j + 127 (value = code * 2^(E_j - 127);

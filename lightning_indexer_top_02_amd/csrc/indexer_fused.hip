@@ -63,6 +63,8 @@ constexpr int kFusedMaxRows = 4;               // query rows per request
 constexpr int kKeysPerThread = kFusedMaxRow / kFusedThreads;
 constexpr int kFusedMaxPages = kFusedMaxRow / kFusedChunk * (kFusedChunk / kPage);  // pages one workgroup scores
 constexpr int kFusedKeyBuf = 16384;  // keys a workgroup may stage in LDS (64 KB)
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;  // gfx950
+constexpr size_t kFusedStaticLds = 256;           // wsum, res and s_last, rounded up
 
 // Slot of position p in a row's key array.  The selecting workgroup holds
 // positions 32 t .. 32 t + 31 in thread t and loads them 4 at a time; keys
@@ -343,11 +345,19 @@ hipError_t launch_fused(FusedParams p, int batch, int max_ctx, hipStream_t s) {
   // the loads) decides
   const int max_ch = (chunks + p.G - 1) / p.G;
   const int mode = max_ch < 3 ? 0 : (DT != 0 && p.rcap == 1 && p.Hpad == 64 ? 2 : 1);
-  // batched modes stage a workgroup's keys in LDS when they fit
-  p.kbuf_stride = mode != 0 && p.rcap * max_ch * kFusedChunk <= kFusedKeyBuf ? max_ch * kFusedChunk : 0;
-  const size_t lds = std::max(query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4 +
-                                  (size_t)kFusedMaxPages * 4 + (size_t)p.rcap * p.kbuf_stride * 4,
-                              (size_t)kHistBins * 4);
+  // batched modes stage a workgroup's keys in LDS when they fit, both the
+  // staging cap and the device's LDS beside the queries, histograms and
+  // page table (4-row requests of 64 bf16 heads would otherwise ask for
+  // 167 KB); else keys are stored as they are made
+  const size_t base = query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4 +
+                      (size_t)kFusedMaxPages * 4;
+  const size_t kbuf_bytes = (size_t)p.rcap * max_ch * kFusedChunk * 4;
+  p.kbuf_stride = mode != 0 && p.rcap * max_ch * kFusedChunk <= kFusedKeyBuf &&
+                          base + kbuf_bytes + kFusedStaticLds <= kLdsPerWorkgroup
+                      ? max_ch * kFusedChunk
+                      : 0;
+  const size_t lds = std::max(base + (size_t)p.rcap * p.kbuf_stride * 4, (size_t)kHistBins * 4);
+  if (lds + kFusedStaticLds > kLdsPerWorkgroup) return hipErrorInvalidValue;
   if (mode == 0) return launch_fused_as<DT, D, 0>(p, batch, lds, s);
   if (mode == 1) return launch_fused_as<DT, D, 1>(p, batch, lds, s);
   return launch_fused_as<DT, D, 2>(p, batch, lds, s);

@@ -88,7 +88,7 @@ constexpr int kKrowBytes = kSfaRows * kRowStride;
 constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chunk
 
 // fp8 latent rows in HBM ("Day0 Inference Optimization for Next-Generation
-// Hybrid-Architecture LLMs Based on CANN", section 3.1: an fp8 KV cache with
+// Hybrid-Architecture LLMs Based on CANN", section 3.2: an fp8 KV cache with
 // a scale per token and 128-element tile): the 512 latent dims as e4m3 codes,
 // a 16-byte block whose first four bytes are the tiles' E8M0 exponents
 // (power-of-two scales), then the 64 rope dims in bf16, 656 bytes.  A chunk

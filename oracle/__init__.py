@@ -14,6 +14,7 @@ from .oracle import (  # noqa: F401
     encode_e4m3,
     encode_bf16,
     cache_append,
+    latent_append,
     visible,
     scores,
     select,

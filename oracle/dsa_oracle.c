@@ -325,7 +325,7 @@ int dsa_oracle_indexer_topk(int B, const int32_t *q_offsets, const int32_t *ctx_
 /* Element d of latent row `row` (pool row: page * page_size + slot).  fp32
  * and bf16 rows hold Dqk elements.  The fp8 latent row (dtype 2; "Day0
  * Inference Optimization for Next-Generation Hybrid-Architecture LLMs Based
- * on CANN", section 3.1, and "Optimizing Inference for Hybrid Attention
+ * on CANN", section 3.2, and "Optimizing Inference for Hybrid Attention
  * Architectures: From Operator Fusion to Sequence Sharding", section
  * "Layered Quantization: Distinguishing Precision Sensitivity": an fp8 KV
  * cache with one scale per token and 128-element tile) is Dv e4m3 codes, then
@@ -534,6 +534,92 @@ int dsa_oracle_cache_append(int B, const int32_t *q_offsets, const int32_t *ctx_
                     ((uint8_t *)k_scale)[row * (D / 32) + blk] = (uint8_t)(e + 127);
                     for (int d = 32 * blk; d < 32 * blk + 32; ++d)
                         ((uint8_t *)k_cache)[row * D + d] = e4m3_of(ldexp((double)x[d], -e)); /* exact scaling */
+                }
+            }
+        }
+    }
+    free(x);
+    return 0;
+}
+
+/* ---- Latent cache append: the new token's row of the main attention cache --
+ * Besides the indexer key, each new token leaves one latent row (Dv latent
+ * dims, then the rope dims) in the paged cache that sparse attention reads
+ * ("Optimizing Inference for Hybrid Attention Architectures: From Operator
+ * Fusion to Sequence Sharding", section "Breaking Down the Computational Path
+ * of Hybrid Attention", item 2: the main attention cache).  Placement is the
+ * indexer append's: row j of request b's new rows goes to position
+ * L_b - n_b + j.  dst_dtype 0 copies fp32 rows, 1 rounds to bf16 (nearest
+ * even).  dst_dtype 2 writes the fp8 latent row read by sparse attention
+ * ("Day0 Inference Optimization for Next-Generation Hybrid-Architecture LLMs
+ * Based on CANN", section 3.2: FP8 per token and per 128-element tile):
+ * for tile t (latent dims 128t .. 128t + 127) the exponent e is the smallest
+ * integer with amax <= 448 * 2^e (e = 0 for a zero tile), clamped to
+ * [-126, 127]; byte t of the 16-byte scale block is e + 127 (the other bytes
+ * are 0); the codes are the e4m3 codes of x * 2^-e (exact); the rope dims
+ * follow as bf16 (nearest even). */
+static int tile_exponent(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int e = ilogb(amax) - 8; /* a start near the answer; the loops fix it exactly */
+    while (amax > ldexp(448.0, e))
+        ++e;
+    while (amax <= ldexp(448.0, e - 1))
+        --e;
+    return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
+int dsa_oracle_latent_append(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
+                             const int32_t *block_table, int bt_stride, int page_size, int Dqk, int Dv,
+                             int src_dtype, const void *x_new, int dst_dtype, void *kv_cache)
+{
+    if (B < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || page_size < 1 || !q_offsets || !ctx_lens || !block_table ||
+        !x_new || !kv_cache)
+        return -1;
+    if ((src_dtype != 0 && src_dtype != 1) || dst_dtype < 0 || dst_dtype > 2)
+        return -1;
+    if (dst_dtype == 2 && (Dv % 128 != 0 || Dv / 128 > 16))
+        return -1;
+    size_t row_bytes = dst_dtype == 2 ? (size_t)Dv + 16 + 2 * (size_t)(Dqk - Dv)
+                                      : (size_t)Dqk * (dst_dtype == 0 ? 4 : 2);
+    float *x = malloc(sizeof(float) * (size_t)Dqk);
+    if (!x)
+        return -2;
+    for (int b = 0; b < B; ++b) {
+        int n = q_offsets[b + 1] - q_offsets[b], L = ctx_lens[b];
+        if (n < 0 || n > L) {
+            free(x);
+            return -1;
+        }
+        for (int j = 0; j < n; ++j) {
+            size_t i = (size_t)q_offsets[b] + j;
+            int p = L - n + j;
+            int page = block_table[(size_t)b * bt_stride + p / page_size];
+            unsigned char *r = (unsigned char *)kv_cache + ((size_t)page * page_size + p % page_size) * row_bytes;
+            for (int d = 0; d < Dqk; ++d)
+                x[d] = (float)load_elem(x_new, i * Dqk + d, src_dtype); /* exact */
+            if (dst_dtype == 0) {
+                memcpy(r, x, sizeof(float) * (size_t)Dqk);
+            } else if (dst_dtype == 1) {
+                for (int d = 0; d < Dqk; ++d) {
+                    uint16_t h = dsa_oracle_encode_bf16(x[d]);
+                    memcpy(r + 2 * (size_t)d, &h, sizeof h);
+                }
+            } else {
+                memset(r + Dv, 0, 16);
+                for (int t = 0; t < Dv / 128; ++t) {
+                    double amax = 0.0;
+                    for (int d = 128 * t; d < 128 * t + 128; ++d)
+                        amax = fabs((double)x[d]) > amax ? fabs((double)x[d]) : amax;
+                    int e = tile_exponent(amax);
+                    r[Dv + t] = (uint8_t)(e + 127);
+                    for (int d = 128 * t; d < 128 * t + 128; ++d)
+                        r[d] = e4m3_of(ldexp((double)x[d], -e));
+                }
+                for (int d = Dv; d < Dqk; ++d) {
+                    uint16_t h = dsa_oracle_encode_bf16(x[d]);
+                    memcpy(r + Dv + 16 + 2 * (size_t)(d - Dv), &h, sizeof h);
                 }
             }
         }

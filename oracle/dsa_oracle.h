@@ -112,6 +112,19 @@ int dsa_oracle_cache_append(int B, const int32_t *q_offsets, const int32_t *ctx_
                             int src_dtype, const void *k_new, int dst_dtype,
                             void *k_cache, void *k_scale);
 
+/* Latent cache append: the n_b new rows of request b (x_new rows
+ * q_offsets[b] .., [T][Dqk] fp32 or bf16, src_dtype 0 or 1) are written to
+ * positions L_b - n_b + j of the latent pool in dst_dtype: 0 fp32 rows of Dqk
+ * elements, copied; 1 bf16 rows, rounded to nearest even; 2 fp8 latent rows
+ * of Dv + 16 + 2 (Dqk - Dv) bytes: Dv e4m3 codes of x * 2^-e_t, where e_t is
+ * the smallest integer with amax of 128-element tile t <= 448 * 2^e_t (0 for
+ * a zero tile, clamped to [-126, 127]), then a 16-byte block whose byte t is
+ * e_t + 127 (the rest 0), then the Dqk - Dv rope dims in bf16.  Every other
+ * row of the pool is left as it was. */
+int dsa_oracle_latent_append(int B, const int32_t *q_offsets, const int32_t *ctx_lens,
+                             const int32_t *block_table, int bt_stride, int page_size, int Dqk, int Dv,
+                             int src_dtype, const void *x_new, int dst_dtype, void *kv_cache);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,7 @@ def _load():
         _lib.dsa_oracle_encode_bf16.restype = ctypes.c_uint16
         _lib.dsa_oracle_encode_bf16.argtypes = [ctypes.c_float]
         _lib.dsa_oracle_cache_append.argtypes = [I, P, P, P, I, I, I, I, P, I, P, P]
+        _lib.dsa_oracle_latent_append.argtypes = [I, P, P, P, I, I, I, I, I, P, I, P]
         _lib.dsa_oracle_visible.argtypes = [I, P, P, P]
         _lib.dsa_oracle_scores.argtypes = [I, P, P, P, I, I, I, I, I, P, P, P, P, P, I, P, I]
         _lib.dsa_oracle_select.argtypes = [I, I, P, P, I, P, I]
@@ -147,6 +148,28 @@ def cache_append(q_offsets, ctx_lens, block_table, page_size, src_dtype, k_new, 
                                          _ptr(kc), _ptr(ks))
     _check(rc, "cache_append")
     return kc, ks
+
+
+def latent_append(q_offsets, ctx_lens, block_table, page_size, src_dtype, x_new, dst_dtype, kv_cache,
+                  v_dim=512):
+    """The latent pool after appending x_new ([T][qk_dim] fp32, or bf16 bits
+    as uint16) at positions L_b - n_b + j: returns a new pool array (fp32
+    [..][qk_dim], bf16 bits uint16 [..][qk_dim], or fp8 latent rows uint8
+    [..][v_dim + 16 + 2 (qk_dim - v_dim)]); the arguments are not modified."""
+    q_offsets, ctx_lens, bt = _i32(q_offsets), _i32(ctx_lens), _i32(block_table)
+    if bt.ndim != 2:
+        raise ValueError("block_table must be [B][max_pages]")
+    xn = _raw(x_new, src_dtype)
+    kv = _raw(kv_cache, dst_dtype).copy()
+    Dqk = xn.shape[-1]
+    want = v_dim + 16 + 2 * (Dqk - v_dim) if dst_dtype == "fp8" else Dqk
+    if kv.shape[-1] != want:
+        raise ValueError("x_new and kv_cache rows disagree")
+    rc = _load().dsa_oracle_latent_append(len(ctx_lens), _ptr(q_offsets), _ptr(ctx_lens), _ptr(bt), bt.shape[1],
+                                          int(page_size), Dqk, int(v_dim), DTYPES[src_dtype], _ptr(xn),
+                                          DTYPES[dst_dtype], _ptr(kv))
+    _check(rc, "latent_append")
+    return kv
 
 
 def _scales(a, dtype):

@@ -689,6 +689,78 @@ def check_cache_append():
     assert np.array_equal(a1[0], a2[0]) and np.array_equal(a1[1], a2[1])
 
 
+def _min_tile_exponent(amax):
+    """Brute force over the definition: the smallest integer e with
+    amax <= 448 * 2^e (Python floats: 448 * 2.0**k is exact here)."""
+    if amax == 0.0:
+        return 0
+    return min(k for k in range(-200, 200) if amax <= 448.0 * 2.0 ** k)
+
+
+def check_latent_append():
+    """Latent cache append: row j of request b lands at position L_b - n_b + j
+    through the block table and nothing else changes; fp32 rows are copied,
+    bf16 rows equal torch's cast; an fp8 latent row holds, per 128-element
+    tile, the byte 127 + e with e the smallest integer such that amax <= 448
+    * 2^e (brute force over e, clamped to [-126, 127], 0 for a zero tile),
+    the codes of torch's e4m3 cast of x * 2^-e, zeros in the rest of the
+    16-byte block and the rope dims as torch's bf16 cast; random rows equal
+    the input generator's fp8 latent packing; bf16 sources give what their
+    fp32 values give."""
+    P, Dqk, Dv = 16, 576, 512
+    qo, ctx, bt, npages, rng = _append_layout(6, P)
+    T = int(qo[-1])
+    x = (rng.standard_normal((T, Dqk)) * np.exp2(rng.integers(-6, 7, (T, 1)))).astype(np.float32)
+    x[0] = 0.0                                      # every tile zero
+    x[1, :128] = 0.0                                # one zero tile
+    x[2, 5] = 448.0 * 8                             # tile 0 amax exactly 448 * 2^3
+    x[3, 130] = np.nextafter(np.float32(448.0 * 8), np.float32(1e9))  # just above: e = 4
+    x[4, 256:384] = 1e-38                           # e clamped to -126
+    x[5, 384:512] = inputs.e4m3_midpoints()[:128].numpy() * 4  # e4m3 midpoints at scale 2^2
+    x[5, 384] = 448.0 * 4
+    where = _append_positions(qo, ctx, bt, P)
+    args = (qo, ctx, bt, P)
+    row8 = Dv + 16 + 2 * (Dqk - Dv)
+
+    kv = oracle.latent_append(*args, "f32", x, "f32", np.full((npages, P, Dqk), -7.0, np.float32), v_dim=Dv)
+    seen = np.zeros((npages, P), bool)
+    for i, pg, sl in where:
+        assert np.array_equal(kv[pg, sl], x[i]), f"latent row {i} not at its position"
+        seen[pg, sl] = True
+    assert np.all(kv[~seen] == -7.0), "an untouched latent row changed"
+
+    kv = oracle.latent_append(*args, "f32", x, "bf16", np.zeros((npages, P, Dqk), np.uint16), v_dim=Dv)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for i, pg, sl in where:
+        assert np.array_equal(kv[pg, sl], ref[i]), f"bf16 latent row {i}"
+
+    kv = oracle.latent_append(*args, "f32", x, "fp8", np.full((npages, P, row8), 0xA5, np.uint8), v_dim=Dv)
+    rope = torch.from_numpy(x[:, Dv:].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8)
+    for i, pg, sl in where:
+        r = kv[pg, sl]
+        for t in range(Dv // 128):
+            xt = x[i, 128 * t:128 * t + 128]
+            e = min(127, max(-126, _min_tile_exponent(float(np.abs(xt).max()))))
+            assert r[Dv + t] == 127 + e, f"tile {t} exponent byte of row {i}: {r[Dv + t]} vs {127 + e}"
+            q32 = np.clip(np.ldexp(xt.astype(np.float64), -e), -448, 448).astype(np.float32)
+            assert np.array_equal(r[128 * t:128 * t + 128], _torch_e4m3(q32)), f"fp8 codes of row {i} tile {t}"
+        assert np.all(r[Dv + Dv // 128:Dv + 16] == 0), f"unused scale bytes of row {i}"
+        assert np.array_equal(r[Dv + 16:], rope[i].reshape(-1)), f"rope of row {i}"
+    assert np.all(kv[~seen] == 0xA5)
+    assert kv[where[2][1], where[2][2], Dv] == 127 + 3 and kv[where[3][1], where[3][2], Dv + 1] == 127 + 4
+    assert kv[where[4][1], where[4][2], Dv + 2] == 1 and kv[where[0][1], where[0][2], Dv] == 127
+    gen = inputs.pack_latent_fp8(torch.from_numpy(x[6:]), Dv).numpy()
+    for k, (i, pg, sl) in enumerate(where[6:]):
+        assert np.array_equal(kv[pg, sl], gen[k]), f"row {i} differs from the generator's fp8 packing"
+
+    xb16 = torch.from_numpy(x).to(torch.bfloat16)
+    a1 = oracle.latent_append(*args, "bf16", xb16.view(torch.int16).numpy().view(np.uint16), "fp8",
+                              np.zeros((npages, P, row8), np.uint8), v_dim=Dv)
+    a2 = oracle.latent_append(*args, "f32", xb16.float().numpy(), "fp8", np.zeros((npages, P, row8), np.uint8),
+                              v_dim=Dv)
+    assert np.array_equal(a1, a2)
+
+
 ALL_CHECKS = [
     check_decode_e4m3_all_codes,
     check_decode_e8m0_all_codes,
@@ -703,6 +775,7 @@ ALL_CHECKS = [
     check_encode_e4m3_against_torch,
     check_encode_bf16_against_torch,
     check_cache_append,
+    check_latent_append,
     check_causal_visibility,
     check_selection_definition,
     check_selection_signed_zero_and_nesting,

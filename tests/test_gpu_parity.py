@@ -265,6 +265,15 @@ FUSED_BATCHED = {
     # MXFP8 keys: 64 one-row requests (one-row 64-head mode) and the general mode
     "b64_mxfp8": lambda: inputs.decode_32k(batch=64, device="cuda", sfa_dtype=None, idx_dtype="mxfp8",
                                            name="fused_b64_mxfp8"),
+    # 4-row requests (speculative-verify shape) in the batched modes: the key
+    # staging must fit the device's LDS beside 4 rows of staged queries
+    "b32x4_bf16": lambda: inputs.decode_32k(batch=32, n_q=4, device="cuda", sfa_dtype=None,
+                                            name="fused_b32x4_bf16"),
+    "b64x4_bf16_16k": lambda: inputs.decode_32k(batch=64, n_q=4, ctx_lens=[16384] * 64, device="cuda",
+                                                sfa_dtype=None, name="fused_b64x4_bf16_16k"),
+    "b32x4_f32_64x64": lambda: inputs.make_case(name="fused_b32x4_f32_64x64", seed=98, ctx_lens=[32768] * 32,
+                                                n_q=4, idx_dtype="f32", n_heads_idx=64, head_dim_idx=64,
+                                                topk=2048, sfa_dtype=None, device="cuda"),
     "b24_mxfp8_48h": lambda: inputs.make_case(name="fused_b24_mxfp8_48h", seed=94,
                                               ctx_lens=[5000 + 1117 * i for i in range(24)],
                                               n_q=[1 + (i % 3 == 0) for i in range(24)], idx_dtype="mxfp8",

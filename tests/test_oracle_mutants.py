@@ -78,6 +78,24 @@ MUTANTS = [
     ("fp8_zero_key_scale_0", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax / 448.0f"),
     ("fp8_quotient_in_fp64", "float v = x[d] / s;", "double v = (double)x[d] / s;"),
     ("mx_exponent_minus_7", "e = ex - 1 - 8;", "e = ex - 1 - 7;"),
+    ("latent_tile_of_64", "for (int d = 128 * t; d < 128 * t + 128; ++d)\n                        amax",
+     "for (int d = 128 * t; d < 128 * t + 64; ++d)\n                        amax"),
+    ("latent_exponent_for_256", "while (amax > ldexp(448.0, e))\n        ++e;\n    while (amax <= ldexp(448.0, e - 1))",
+     "while (amax > ldexp(256.0, e))\n        ++e;\n    while (amax <= ldexp(256.0, e - 1))"),
+    ("latent_exponent_strict", "while (amax > ldexp(448.0, e))\n        ++e;\n    while (amax <= ldexp(448.0, e - 1))",
+     "while (amax >= ldexp(448.0, e))\n        ++e;\n    while (amax < ldexp(448.0, e - 1))"),
+    ("latent_no_clamp", "return e < -126 ? -126 : (e > 127 ? 127 : e);", "return e;"),
+    ("latent_zero_tile_byte_0", "if (amax == 0.0)\n        return 0;\n    int e = ilogb",
+     "if (amax == 0.0)\n        return -127;\n    int e = ilogb"),
+    ("latent_scale_bytes_reversed", "r[Dv + t] = (uint8_t)(e + 127);", "r[Dv + 15 - t] = (uint8_t)(e + 127);"),
+    ("latent_rope_truncated", "uint16_t h = dsa_oracle_encode_bf16(x[d]);\n                    memcpy(r + Dv + 16",
+     "uint32_t u_; memcpy(&u_, &x[d], 4); uint16_t h = (uint16_t)(u_ >> 16);\n                    memcpy(r + Dv + 16"),
+    ("latent_rope_without_gap", "memcpy(r + Dv + 16 + 2 * (size_t)(d - Dv), &h, sizeof h);",
+     "memcpy(r + Dv + 2 * (size_t)(d - Dv), &h, sizeof h);"),
+    ("latent_at_front", "int p = L - n + j;\n            int page = block_table[(size_t)b * bt_stride + p / page_size];\n            unsigned char",
+     "int p = j;\n            int page = block_table[(size_t)b * bt_stride + p / page_size];\n            unsigned char"),
+    ("latent_bf16_truncated", "uint16_t h = dsa_oracle_encode_bf16(x[d]);\n                    memcpy(r + 2 * (size_t)d",
+     "uint32_t u_; memcpy(&u_, &x[d], 4); uint16_t h = (uint16_t)(u_ >> 16);\n                    memcpy(r + 2 * (size_t)d"),
     ("mx_zero_block_byte_0", "int e = 0;\n                    if (amax > 0.0f)", "int e = -127;\n                    if (amax > 0.0f)"),
 ]
 
