@@ -213,6 +213,43 @@ typedef struct {
 dsa_status_t dsa_indexer_cache_append(const dsa_paged_t *paged, const dsa_cache_append_t *append,
                                       void *stream);
 
+/* Latent cache append: writes each new token's latent row (qk_dim = 576: the
+ * 512 latent dims, then the 64 rope dims) into the paged latent pool that
+ * dsa_sparse_attn gathers from ("Optimizing Inference for Hybrid Attention
+ * Architectures: From Operator Fusion to Sequence Sharding", section
+ * "Breaking Down the Computational Path of Hybrid Attention", item 2: the
+ * main attention cache; "Day0 Inference Optimization for Next-Generation
+ * Hybrid-Architecture LLMs Based on CANN", section 3.2 for the fp8 rows).
+ * Placement is dsa_indexer_cache_append's: row j of request b (rows
+ * q_offsets[b] .. q_offsets[b+1]-1 of x_new) goes to position
+ * p = L_b - n_b + j, page block_table[b][p / 64], slot p % 64.
+ * Per dst_dtype:
+ *   F32: copied.  BF16: rounded to nearest even.
+ *   FP8_E4M3: the 656-byte fp8 latent row of dsa_sfa_t: for each tile t of
+ *     128 latent dims, e_t = the smallest integer with amax <= 448 * 2^e_t
+ *     (0 for a zero tile, at least -126); the codes are the e4m3 codes of
+ *     x * 2^-e_t (nearest even, exact scaling); byte t of the 16-byte block
+ *     after the codes is e_t + 127 and its other 12 bytes are 0; the 64 rope
+ *     dims follow in bf16 (nearest even).
+ * Other rows are not touched.  A row whose position or page falls outside
+ * [0, max_ctx_len) or [0, num_pages) is skipped.  Needs no workspace.  The
+ * indexer append and this one touch different pools and may run on two
+ * streams at once; either must be ordered before the calls that read it.
+ * INVALID_ARG for NULL pointers or bad dtypes; UNSUPPORTED for qk_dim other
+ * than 576 or v_dim other than 512. */
+typedef struct {
+    int32_t qk_dim;            /* 576 */
+    int32_t v_dim;             /* 512 */
+    int32_t src_dtype;         /* DSA_F32 or DSA_BF16 */
+    int32_t dst_dtype;         /* DSA_F32, DSA_BF16 or DSA_FP8_E4M3 (the pool's dtype) */
+    const void *x_new;         /* [T][qk_dim] */
+    void *kv_cache;            /* [num_pages][64][qk_dim] (FP8_E4M3: [num_pages][64]
+                                  656-byte rows, 16-byte aligned) */
+} dsa_latent_append_t;
+
+dsa_status_t dsa_latent_cache_append(const dsa_paged_t *paged, const dsa_latent_append_t *append,
+                                     void *stream);
+
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_t *paged, const dsa_sfa_t *sfa,
                                       int32_t topk);
 

@@ -324,6 +324,31 @@ dsa_status_t dsa_indexer_cache_append(const dsa_paged_t* pg, const dsa_cache_app
   return dsa_launch_cache_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
+dsa_status_t dsa_latent_cache_append(const dsa_paged_t* pg, const dsa_latent_append_t* x, void* stream) {
+  if (!valid_paged(pg) || !x || !x->x_new || !x->kv_cache) return DSA_ERR_INVALID_ARG;
+  if (x->src_dtype != DSA_F32 && x->src_dtype != DSA_BF16) return DSA_ERR_INVALID_ARG;
+  if (x->dst_dtype != DSA_F32 && x->dst_dtype != DSA_BF16 && x->dst_dtype != DSA_FP8_E4M3)
+    return DSA_ERR_INVALID_ARG;
+  if (x->qk_dim != dsa::kQkDim || x->v_dim != dsa::kVDim) return DSA_ERR_UNSUPPORTED;
+  if (x->dst_dtype == DSA_FP8_E4M3 && (reinterpret_cast<uintptr_t>(x->kv_cache) & 15)) return DSA_ERR_INVALID_ARG;
+  dsa_status_t st = check_device();
+  if (st != DSA_OK) return st;
+  DsaLatentAppendLaunch a;
+  a.q_offsets = pg->q_offsets;
+  a.ctx_lens = pg->ctx_lens;
+  a.block_table = pg->block_table;
+  a.batch = pg->batch;
+  a.max_q_per_req = pg->max_q_per_req;
+  a.max_ctx_len = pg->max_ctx_len;
+  a.bt_stride = pg->max_pages_per_req;
+  a.num_pages = pg->num_pages;
+  a.src_dtype = x->src_dtype;
+  a.dst_dtype = x->dst_dtype == DSA_FP8_E4M3 ? 2 : x->dst_dtype;
+  a.x_new = x->x_new;
+  a.kv_cache = x->kv_cache;
+  return dsa_launch_latent_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) {
   if (check_sfa(pg, s, topk) != DSA_OK) return 0;
   return plan_sfa(pg, s, topk).total;

@@ -170,8 +170,19 @@ struct DsaAppendLaunch {
   void* k_scale;
 };
 
+struct DsaLatentAppendLaunch {
+  const int32_t* q_offsets;
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  int batch, max_q_per_req, max_ctx_len, bt_stride, num_pages;
+  int src_dtype, dst_dtype;  // src 0 fp32 / 1 bf16; dst 0 fp32, 1 bf16, 2 fp8 latent rows
+  const void* x_new;
+  void* kv_cache;
+};
+
 hipError_t dsa_allow_lds(const void* kernel, size_t bytes);
 hipError_t dsa_launch_cache_append(const DsaAppendLaunch& a, hipStream_t s);
+hipError_t dsa_launch_latent_append(const DsaLatentAppendLaunch& a, hipStream_t s);
 
 hipError_t dsa_launch_indexer_topk(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_indexer_two_pass(const DsaIndexerLaunch& a, hipStream_t s);

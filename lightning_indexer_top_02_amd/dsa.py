@@ -95,6 +95,17 @@ class CacheAppend(ctypes.Structure):
     ]
 
 
+class LatentAppend(ctypes.Structure):
+    _fields_ = [
+        ("qk_dim", ctypes.c_int32),
+        ("v_dim", ctypes.c_int32),
+        ("src_dtype", ctypes.c_int32),
+        ("dst_dtype", ctypes.c_int32),
+        ("x_new", ctypes.c_void_p),
+        ("kv_cache", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -127,6 +138,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_fused_decode.argtypes = [PP, PI, PS, P, P, S, P]
         lib.dsa_indexer_cache_append.restype = ctypes.c_int
         lib.dsa_indexer_cache_append.argtypes = [PP, ctypes.POINTER(CacheAppend), P]
+        lib.dsa_latent_cache_append.restype = ctypes.c_int
+        lib.dsa_latent_cache_append.argtypes = [PP, ctypes.POINTER(LatentAppend), P]
         lib.dsa_workspace_init.restype = ctypes.c_int
         lib.dsa_workspace_init.argtypes = [P, S, P]
         _lib = lib
@@ -283,6 +296,25 @@ def cache_append(paged: Paged, append: CacheAppend, stream=None):
     st = load().dsa_indexer_cache_append(ctypes.byref(paged), ctypes.byref(append), _stream(stream))
     if st != DSA_OK:
         raise DsaError(st, "dsa_indexer_cache_append")
+
+
+def make_latent_append(x_new, src_dtype, kv_cache, dst_dtype, v_dim=512) -> LatentAppend:
+    """x_new [T][576] (fp32, or bf16); kv_cache the latent pool in dst_dtype
+    ("f32", "bf16", or "fp8": uint8 [pages][64][656] fp8 latent rows)."""
+    _check_tensor(x_new, "x_new", _STORAGE[src_dtype])
+    _check_tensor(kv_cache, "kv_cache", (torch.uint8,) if dst_dtype == "fp8" else _STORAGE[dst_dtype])
+    Dqk = x_new.shape[-1]
+    row = v_dim + 16 + 2 * (Dqk - v_dim) if dst_dtype == "fp8" else Dqk
+    if kv_cache.shape[-1] != row:
+        raise ValueError("x_new and kv_cache rows disagree")
+    return LatentAppend(Dqk, v_dim, DTYPE_CODE[src_dtype], DTYPE_CODE[dst_dtype], _ptr(x_new), _ptr(kv_cache))
+
+
+def latent_append(paged: Paged, append: LatentAppend, stream=None):
+    """dsa_latent_cache_append: each request's new latent rows into their pool slots."""
+    st = load().dsa_latent_cache_append(ctypes.byref(paged), ctypes.byref(append), _stream(stream))
+    if st != DSA_OK:
+        raise DsaError(st, "dsa_latent_cache_append")
 
 
 def sparse_attn_workspace_size(paged: Paged, sfa: Sfa, topk: int) -> int:

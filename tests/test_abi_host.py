@@ -181,3 +181,18 @@ def test_cache_append_argument_checks():
     assert call(src_dtype=2) == 1 and call(src_dtype=3) == 1 and call(dst_dtype=4) == 1
     assert call(head_dim=96) == 2 and call(dst_dtype=3, head_dim=64) == 2
     assert call(paged=good_paged(page_size=32)) == 1 and call(paged=good_paged(batch=0)) == 1
+
+
+def test_latent_append_argument_checks():
+    lib = dsa.load()
+
+    def call(paged=None, **kw):
+        a = dict(qk_dim=576, v_dim=512, src_dtype=0, dst_dtype=2, x_new=FAKE, kv_cache=FAKE)
+        a.update(kw)
+        return lib.dsa_latent_cache_append(ctypes.byref(paged or good_paged()),
+                                           ctypes.byref(dsa.LatentAppend(**a)), None)
+    assert call(x_new=None) == 1 and call(kv_cache=None) == 1
+    assert call(src_dtype=2) == 1 and call(dst_dtype=3) == 1 and call(dst_dtype=7) == 1
+    assert call(kv_cache=FAKE + 8) == 1  # fp8 rows must be 16-byte aligned
+    assert call(qk_dim=512) == 2 and call(v_dim=448) == 2
+    assert call(paged=good_paged(page_size=32)) == 1 and call(paged=good_paged(batch=0)) == 1

@@ -143,3 +143,103 @@ def test_cache_append_graph_replays_match_eager():
         assert torch.equal(kc, ref_c) and torch.equal(ks, ref_s), f"replay {rep} differs from the eager append"
     del g
     print("[ok] append graph replays", flush=True)
+
+
+# --- latent rows (dsa_latent_cache_append) --------------------------------------
+LATENT_SENTINEL = {"f32": -7.0, "bf16": 0x1234, "fp8": 0x55}
+LATENT_ROW = {"f32": 576, "bf16": 576, "fp8": 656}
+
+
+def _latent_case(seed=37, lens=LENS, nq=NQ, name="latent_ragged"):
+    """Ragged new latent rows, with directed rows at the fp8 tile-exponent
+    boundaries: a tile whose amax is exactly 448 * 2^3 (exponent 3) and one
+    just above it (exponent 4), a tile of 1e-38 (exponent clamped to -126),
+    a zero row, e4m3 midpoints with 448 in every 32-block (exponent 0)."""
+    c = inputs.append_case(seed, lens, nq, 576, name=name)
+    x = c.k_new.clone()
+    if x.shape[0] >= 12:
+        x[6:10] = x[6:10].clamp(-3, 3)
+        x[6, 5] = 448.0 * 8
+        x[7, 130] = float(np.nextafter(np.float32(448.0 * 8), np.float32(1e9)))
+        x[8, 256:384] = 1e-38
+        x[9] = 0.0
+    return dataclasses.replace(c, k_new=x.contiguous())
+
+
+def _latent_pool(case, dst):
+    dt = torch.float32 if dst == "f32" else (torch.int16 if dst == "bf16" else torch.uint8)
+    return torch.full((case.num_pages, 64, LATENT_ROW[dst]), LATENT_SENTINEL[dst], dtype=dt)
+
+
+def _check_latent(case, src, dst):
+    print(f"\n[case] latent append {case.name} src={src} dst={dst} T={case.k_new.shape[0]}", flush=True)
+    kv = _latent_pool(case, dst).cuda()
+    x_new = _src(case, src).cuda()
+    qo, lens, bt = case.q_offsets.cuda(), case.ctx_lens.cuda(), case.block_table.cuda()
+    paged = dsa.make_paged(qo, lens, bt, case.num_pages, max_q_per_req=case.max_q_per_req, max_ctx_len=case.max_ctx)
+    dsa.latent_append(paged, dsa.make_latent_append(x_new, src, kv, dst))
+    torch.cuda.synchronize()
+    del qo, lens, bt
+    o = oracle.latent_append(case.q_offsets.numpy(), case.ctx_lens.numpy(), case.block_table.numpy(), 64, src,
+                             inputs.to_numpy_raw(_src(case, src)), dst, inputs.to_numpy_raw(_latent_pool(case, dst)))
+    g = inputs.to_numpy_raw(kv.cpu())
+    bad = np.argwhere(g.view(np.uint8) != np.ascontiguousarray(o).view(np.uint8))
+    assert bad.size == 0, f"latent pool differs from the oracle at {bad[:4].tolist()}"
+    print(f"[ok] latent append {case.name} {src}->{dst}", flush=True)
+
+
+LATENT_COMBOS = [(s, d) for s in ("f32", "bf16") for d in ("f32", "bf16", "fp8")]
+
+
+@pytest.mark.parametrize("src,dst", LATENT_COMBOS, ids=[f"{s}-{d}" for s, d in LATENT_COMBOS])
+def test_latent_append_matches_oracle(src, dst):
+    _check_latent(_latent_case(), src, dst)
+
+
+def test_latent_append_decode_batch_fp8():
+    """A 64-request decode append (one row each, lengths up to 131072) into
+    fp8 latent rows, checked whole."""
+    lens = inputs.batched_fp8_lengths(seed=38)
+    _check_latent(_latent_case(38, lens, 1, name="latent_decode_b64"), "bf16", "fp8")
+
+
+@pytest.mark.parametrize("sfa_dtype", ["bf16", "fp8"])
+def test_two_stream_appends_then_decode(sfa_dtype):
+    """The step's producers on two streams at once: the indexer-key append on
+    one, the latent-row append on the other, joined by events before the
+    fused decode on the caller's stream.  The pools equal the oracle's
+    appends bit for bit, and the decode over them matches the oracle."""
+    base = inputs.make_case(name=f"two_stream_{sfa_dtype}", seed=39, ctx_lens=[3000, 700, 4500], n_q=[1, 4, 2],
+                            idx_dtype="bf16", n_heads_idx=64, head_dim_idx=128, topk=512, sfa_dtype=sfa_dtype,
+                            n_heads_sfa=128)
+    g = torch.Generator()
+    g.manual_seed(40)
+    T = base.num_tokens
+    k_new = torch.randn((T, 128), generator=g)
+    x_new = torch.randn((T, 576), generator=g) * 0.5
+    dev = parity.to_device(base)  # referenced until the end: the paging pointers live in it
+    kc, kv = dev.k_cache.clone(), dev.kv_cache.clone()
+    paged = parity.paged_of(dev)
+    kn, xn = k_new.cuda(), x_new.cuda()
+    ak = dsa.make_cache_append(kn, "f32", kc, "bf16")
+    al = dsa.make_latent_append(xn, "f32", kv, sfa_dtype)
+    cur = torch.cuda.current_stream()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(cur)
+    s2.wait_stream(cur)
+    dsa.cache_append(paged, ak, stream=s1)
+    dsa.latent_append(paged, al, stream=s2)
+    cur.wait_stream(s1)
+    cur.wait_stream(s2)
+    case = dataclasses.replace(dev, k_cache=kc, kv_cache=kv)
+    f_idx, f_out, f_lse = parity.gpu_fused_decode(case)
+    torch.cuda.synchronize()
+    args = (base.q_offsets.numpy(), base.ctx_lens.numpy(), base.block_table.numpy(), 64, "f32")
+    o_kc, _ = oracle.cache_append(*args, k_new.numpy(), "bf16", inputs.to_numpy_raw(base.k_cache))
+    o_kv = oracle.latent_append(*args, x_new.numpy(), sfa_dtype, inputs.to_numpy_raw(base.kv_cache))
+    assert np.array_equal(inputs.to_numpy_raw(kc.cpu()), o_kc), "indexer pool differs from the oracle's append"
+    assert np.array_equal(inputs.to_numpy_raw(kv.cpu()), o_kv), "latent pool differs from the oracle's append"
+    stats = parity.check_case(case)
+    print(f"[ok] {base.name}: {stats}", flush=True)
+    s_idx, s_out, _ = parity.gpu_fused_decode(case)
+    assert torch.equal(f_idx, s_idx) and torch.equal(f_out, s_out)
