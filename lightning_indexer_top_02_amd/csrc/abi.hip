@@ -6,9 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <map>
 #include <mutex>
-#include <utility>
 
 #include "../../include/dsa.h"
 #include "dsa_device.h"
@@ -223,17 +221,31 @@ __global__ void zero_words(uint32_t* x, size_t n) {
 
 hipError_t dsa_allow_lds(const void* kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
+  // (device, kernel) -> bytes allowed, in a fixed table: a launch path never
+  // allocates, not even host memory
+  struct Allowed {
+    int dev;
+    const void* kernel;
+    size_t bytes;
+  };
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, size_t> done;  // (device, kernel) -> bytes allowed
+  static Allowed done[256];
+  static int n_done = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = done.find({dev, kernel});
-  if (it != done.end() && it->second >= bytes) return hipSuccess;
+  int at = -1;
+  for (int k = 0; k < n_done; ++k)
+    if (done[k].dev == dev && done[k].kernel == kernel) {
+      if (done[k].bytes >= bytes) return hipSuccess;
+      at = k;
+    }
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done[{dev, kernel}] = bytes;
-  return e;
+  if (e != hipSuccess) return e;
+  if (at < 0 && n_done < 256) at = n_done++;
+  if (at >= 0) done[at] = Allowed{dev, kernel, bytes};
+  return hipSuccess;
 }
 
 extern "C" {
