@@ -66,7 +66,9 @@ typedef enum {
     DSA_ERR_UNSUPPORTED = 2,       /* valid but not implemented (dims, dtype) */
     DSA_ERR_WORKSPACE_TOO_SMALL = 3,
     DSA_ERR_LAUNCH = 4,            /* the HIP runtime refused a launch */
-    DSA_ERR_DEVICE = 5             /* no usable gfx950 device current */
+    DSA_ERR_DEVICE = 5,            /* no usable gfx950 device current */
+    DSA_ERR_SCRATCH_LIMIT = 6      /* dsa_fused_decode_static: more scratch needed than
+                                      DSA_STATIC_SCRATCH_BYTES */
 } dsa_status_t;
 
 /* DSA_MXFP8: e4m3 codes with one E8M0 scale byte (value 2^(E - 127)) per 32
@@ -269,6 +271,23 @@ size_t dsa_fused_decode_workspace_size(const dsa_paged_t *paged, const dsa_index
 dsa_status_t dsa_fused_decode(const dsa_paged_t *paged, const dsa_indexer_t *idx,
                               const dsa_sfa_t *sfa, int32_t *topk_idx,
                               void *ws, size_t ws_bytes, void *stream);
+
+/* dsa_fused_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that forbid allocation, harnesses
+ * that ban hipMalloc.  It takes no workspace: its scratch is one static
+ * device array of DSA_STATIC_SCRATCH_BYTES per GPU, which the library holds
+ * from its first use on that GPU until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine) and clears
+ * the scratch words that must start at zero with a fill kernel on `stream`
+ * before its kernels run.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap in time on one GPU race: the caller orders them (one
+ * stream, or events).  Results, arguments and errors are dsa_fused_decode's,
+ * plus DSA_ERR_SCRATCH_LIMIT (returned before any device work) when
+ * dsa_fused_decode_workspace_size of the same arguments exceeds
+ * DSA_STATIC_SCRATCH_BYTES. */
+#define DSA_STATIC_SCRATCH_BYTES (64u << 20)
+dsa_status_t dsa_fused_decode_static(const dsa_paged_t *paged, const dsa_indexer_t *idx,
+                                     const dsa_sfa_t *sfa, int32_t *topk_idx, void *stream);
 
 /* Zero-fill a workspace (enqueued on `stream`).  ws_bytes % 4 == 0. */
 dsa_status_t dsa_workspace_init(void *ws, size_t ws_bytes, void *stream);

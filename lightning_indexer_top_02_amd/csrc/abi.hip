@@ -219,6 +219,64 @@ __global__ void zero_words(uint32_t* x, size_t n) {
 
 }  // namespace
 
+namespace {
+
+// Workspace of the fused call: the indexer's, then the indices (when the
+// caller passes no topk_idx), then the sparse attention's.
+struct FusedPlan {
+  IndexerPlan ip;
+  SfaPlan sp;
+  size_t idx_off, sfa_off, total;
+};
+
+FusedPlan plan_fused(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s) {
+  FusedPlan f;
+  f.ip = plan_indexer(pg);
+  f.sp = plan_sfa(pg, s, x->topk);
+  f.idx_off = align_up(f.ip.total);
+  f.sfa_off = f.idx_off + align_up((size_t)pg->num_q_tokens * x->topk * 4);
+  f.total = f.sfa_off + f.sp.total;
+  return f;
+}
+
+dsa_status_t launch_fused_decode(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s,
+                                 int32_t* topk_idx, unsigned char* w, const FusedPlan& fp, hipStream_t hs) {
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + fp.idx_off);
+  if (dsa_launch_indexer_topk(indexer_args(pg, x, idx, w, fp.ip), hs) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa_launch_sparse_attn(sfa_args(pg, s, idx, x->topk, w + fp.sfa_off, fp.sp), hs) != hipSuccess)
+    return DSA_ERR_LAUNCH;
+  return DSA_OK;
+}
+
+// Scratch of dsa_fused_decode_static: one array per device, held until the
+// process ends.  Host code never uses the array's name as an address (it is a
+// host-side stand-in); the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+constexpr size_t kStaticScratchBytes = (size_t)DSA_STATIC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[64];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+dsa_status_t static_scratch(unsigned char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DSA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSA_ERR_DEVICE;
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
 hipError_t dsa_allow_lds(const void* kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
   // (device, kernel) -> bytes allowed, in a fixed table: a launch path never
@@ -272,6 +330,7 @@ const char* dsa_status_string(dsa_status_t s) {
     case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small or misaligned";
     case DSA_ERR_LAUNCH: return "kernel launch failed";
     case DSA_ERR_DEVICE: return "no gfx950 device is current";
+    case DSA_ERR_SCRATCH_LIMIT: return "needs more scratch than the library's static array holds";
   }
   return "unknown status";
 }
@@ -380,8 +439,7 @@ dsa_status_t dsa_sparse_attn(const dsa_paged_t* pg, const dsa_sfa_t* s, const in
 
 size_t dsa_fused_decode_workspace_size(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s) {
   if (check_indexer(pg, x) != DSA_OK || !x || check_sfa(pg, s, x->topk) != DSA_OK) return 0;
-  return align_up(plan_indexer(pg).total) + align_up((size_t)pg->num_q_tokens * x->topk * 4) +
-         plan_sfa(pg, s, x->topk).total;
+  return plan_fused(pg, x, s).total;
 }
 
 dsa_status_t dsa_fused_decode(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s,
@@ -389,19 +447,32 @@ dsa_status_t dsa_fused_decode(const dsa_paged_t* pg, const dsa_indexer_t* x, con
   dsa_status_t st = check_indexer(pg, x);
   if (st != DSA_OK) return st;
   if ((st = check_sfa(pg, s, x->topk)) != DSA_OK) return st;
-  const IndexerPlan ip = plan_indexer(pg);
-  const SfaPlan sp = plan_sfa(pg, s, x->topk);
-  const size_t idx_off = align_up(ip.total);
-  const size_t sfa_off = idx_off + align_up((size_t)pg->num_q_tokens * x->topk * 4);
-  if (!ws_ok(ws, ws_bytes, sfa_off + sp.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  const FusedPlan fp = plan_fused(pg, x, s);
+  if (!ws_ok(ws, ws_bytes, fp.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
   if ((st = check_device()) != DSA_OK) return st;
-  unsigned char* w = static_cast<unsigned char*>(ws);
-  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + idx_off);
+  return launch_fused_decode(pg, x, s, topk_idx, static_cast<unsigned char*>(ws), fp, static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_fused_decode_static(const dsa_paged_t* pg, const dsa_indexer_t* x, const dsa_sfa_t* s,
+                                     int32_t* topk_idx, void* stream) {
+  dsa_status_t st = check_indexer(pg, x);
+  if (st != DSA_OK) return st;
+  if ((st = check_sfa(pg, s, x->topk)) != DSA_OK) return st;
+  const FusedPlan fp = plan_fused(pg, x, s);
+  if (fp.total > kStaticScratchBytes) return DSA_ERR_SCRATCH_LIMIT;
+  if ((st = check_device()) != DSA_OK) return st;
+  unsigned char* w = nullptr;
+  if ((st = static_scratch(&w)) != DSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (dsa_launch_indexer_topk(indexer_args(pg, x, idx, w, ip), hs) != hipSuccess) return DSA_ERR_LAUNCH;
-  if (dsa_launch_sparse_attn(sfa_args(pg, s, idx, x->topk, w + sfa_off, sp), hs) != hipSuccess)
-    return DSA_ERR_LAUNCH;
-  return DSA_OK;
+  // The array keeps the previous call's contents, and a call of another
+  // shape may have left scores or indices where this call's arrival
+  // counters and histograms lie: clear those words (a fill kernel, so the
+  // call can be captured in a graph), the rest is written before it is read.
+  const size_t ctrl_words = fp.ip.scores_off / 4;
+  hipLaunchKernelGGL(zero_words, dim3((unsigned)std::min<size_t>((ctrl_words + 255) / 256, 2048)), dim3(256), 0, hs,
+                     reinterpret_cast<uint32_t*>(w), ctrl_words);
+  if (hipGetLastError() != hipSuccess) return DSA_ERR_LAUNCH;
+  return launch_fused_decode(pg, x, s, topk_idx, w, fp, hs);
 }
 
 }  // extern "C"

@@ -140,6 +140,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_indexer_cache_append.argtypes = [PP, ctypes.POINTER(CacheAppend), P]
         lib.dsa_latent_cache_append.restype = ctypes.c_int
         lib.dsa_latent_cache_append.argtypes = [PP, ctypes.POINTER(LatentAppend), P]
+        lib.dsa_fused_decode_static.restype = ctypes.c_int
+        lib.dsa_fused_decode_static.argtypes = [PP, PI, PS, P, P]
         lib.dsa_workspace_init.restype = ctypes.c_int
         lib.dsa_workspace_init.argtypes = [P, S, P]
         _lib = lib
@@ -352,3 +354,14 @@ def fused_decode(paged: Paged, idx: Indexer, sfa: Sfa, topk_idx: Optional[torch.
                               _stream(stream))
     if st != DSA_OK:
         raise DsaError(st, "dsa_fused_decode")
+
+
+def fused_decode_static(paged: Paged, idx: Indexer, sfa: Sfa, topk_idx: Optional[torch.Tensor] = None,
+                        stream=None):
+    """dsa_fused_decode_static: steps 1-3 with the library's static scratch
+    (no workspace, no allocation); calls on one GPU must not overlap."""
+    _check_tensor(topk_idx, "topk_idx", (torch.int32,))
+    st = load().dsa_fused_decode_static(ctypes.byref(paged), ctypes.byref(idx), ctypes.byref(sfa), _ptr(topk_idx),
+                                        _stream(stream))
+    if st != DSA_OK:
+        raise DsaError(st, "dsa_fused_decode_static")

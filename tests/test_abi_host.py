@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert dsa.abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert dsa.status_string(s) and dsa.status_string(s) != "unknown status"
     assert dsa.status_string(99) == "unknown status"
 
@@ -196,3 +196,21 @@ def test_latent_append_argument_checks():
     assert call(kv_cache=FAKE + 8) == 1  # fp8 rows must be 16-byte aligned
     assert call(qk_dim=512) == 2 and call(v_dim=448) == 2
     assert call(paged=good_paged(page_size=32)) == 1 and call(paged=good_paged(batch=0)) == 1
+
+
+def test_static_fused_decode_checks_before_device_work():
+    """The no-allocation fused decode validates like dsa_fused_decode and
+    refuses shapes whose scratch exceeds its static array, on the host."""
+    lib = dsa.load()
+
+    def call(paged, idx, sfa, out=None):
+        return lib.dsa_fused_decode_static(ctypes.byref(paged), ctypes.byref(idx), ctypes.byref(sfa), out, None)
+    assert call(good_paged(batch=0), good_indexer(), good_sfa()) == 1
+    assert call(good_paged(), good_indexer(q=None), good_sfa()) == 1
+    assert call(good_paged(), good_indexer(), good_sfa(n_heads=24)) == 2
+    # 64 rows of 262144 positions: 64 MiB of scores alone
+    big = good_paged(batch=64, num_q_tokens=64, max_q_per_req=1, max_ctx_len=262144, max_pages_per_req=4096)
+    need = lib.dsa_fused_decode_workspace_size(ctypes.byref(big), ctypes.byref(good_indexer()), ctypes.byref(good_sfa()))
+    assert need > (64 << 20)
+    assert call(big, good_indexer(), good_sfa()) == 6
+    assert "static" in dsa.status_string(6)
