@@ -270,10 +270,10 @@ def time_steps(fn, steps, stream):
     return start.elapsed_time(end) / steps
 
 
-def time_graph(fn, steps, warmup):
+def time_graph(fn, steps, warmup, repeats=5):
     """Capture `steps` calls of fn into one HIP graph (on a side stream) and
-    time one replay with events on the replay stream; the host then issues a
-    single launch for the whole timed region."""
+    time `repeats` replays with events on the replay stream; the host issues a
+    single launch per replay.  Returns the median replay's ms per step."""
     cs = torch.cuda.Stream()
     cs.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cs):
@@ -288,13 +288,16 @@ def time_graph(fn, steps, warmup):
     g.replay()  # untimed first replay
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    g.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / steps)
     del g
-    return start.elapsed_time(end) / steps
+    return sorted(times)[len(times) // 2]
 
 
 def stage_breakdown(step: Step, steps, stream):
@@ -403,6 +406,163 @@ def cpu_baseline(case: inputs.Case, step: Step, budget_s: float):
             "parity_vs_gpu": status}
 
 
+def replicas_for(case: inputs.Case) -> int:
+    """Cache replicas so that the rotated state is at least three times the
+    256 MB Infinity Cache (at most 32): each step then reads its caches from
+    HBM, as each layer of a model reads its own caches."""
+    state = sum(x.numel() * x.element_size() for x in (case.k_cache, case.kv_cache, case.k_scale) if x is not None)
+    return max(1, min(32, math.ceil(768e6 / state)))
+
+
+def measure(name: str, case: inputs.Case, steps: int, warmup: int, eager: bool = False, R: int = 0):
+    """One workload's step (dsa_fused_decode) and its two stages, timed as
+    the median of 5 graph replays of `steps` steps (or eagerly), with the
+    dominant stage's roofline."""
+    R = R or replicas_for(case)
+    step = Step(case, R)
+    ab = algorithmic_bytes(case)
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        step.fused(s, stream)
+    torch.cuda.synchronize()
+    ms_eager = time_steps(step.fused, steps, stream)
+    if eager:
+        ms = ms_eager
+        t_idx, t_sfa = stage_breakdown(step, steps, stream)
+    else:
+        # the whole timed region as one HIP graph: no host launch gaps between steps
+        ms = time_graph(step.fused, steps, warmup)
+        t_idx = time_graph(step.indexer, steps, 1)
+        t_sfa = time_graph(step.sparse_attn, steps, 1)
+    T = case.num_tokens
+    dom = "indexer" if t_idx >= t_sfa else "sparse_attn"
+    rows_route = case.max_q_per_req > 4 and T >= 1024 and case.idx_dtype in MFMA_PEAK_TFLOPS
+    kernels_ms = {}
+    if rows_route:
+        # the indexer call is two launches: the scoring GEMM, then per-row selection
+        kernels_ms["indexer_scores"] = time_steps(step.scores_only, steps, stream)
+    if dom == "indexer" and rows_route:
+        roofline = roofline_entry("indexer_scores", name, ab["indexer"], ab["indexer_flops"],
+                                  kernels_ms["indexer_scores"], compute_peak(case.idx_dtype))
+    elif dom == "indexer":
+        roofline = roofline_entry("indexer_topk", name, ab["indexer"], ab["indexer_flops"], t_idx,
+                                  compute_peak(case.idx_dtype))
+    else:
+        roofline = roofline_entry("sparse_attn", name, ab["sparse_attn"], ab["sparse_attn_flops"], t_sfa,
+                                  compute_peak("bf16" if case.sfa_dtype == "fp8" else case.sfa_dtype))  # fp8 latent: bf16 MFMAs
+    out = {"ms_per_step": ms, "ms_per_step_eager": ms_eager, "tokens_per_s": T / (ms * 1e-3),
+           "algorithmic_bytes": ab["total"], "hbm_gbs_step": ab["total"] / (ms * 1e-3) / 1e9,
+           "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa, **kernels_ms},
+           "roofline": roofline, "cache_replicas": R, "steps": steps,
+           "timing": "eager launches" if eager else f"median of 5 HIP-graph replays of {steps} steps"}
+    return step, out
+
+
+# The grid of workloads measured beside the headline (the batch x sequence-length
+# baselines of the decode and prefill routes): name -> (maker, steps).
+GRID = {
+    "decode_32k_b8": (lambda dev: inputs.decode_32k(batch=8, device=dev), 50),
+    "decode_32k_b32": (lambda dev: inputs.decode_32k(batch=32, device=dev), 20),
+    "decode_32k_b64": (lambda dev: inputs.decode_32k(batch=64, device=dev), 20),
+    "decode_32k_b128": (lambda dev: inputs.decode_32k(batch=128, device=dev), 10),
+    "batched_fp8_narrow": (lambda dev: inputs.batched_decode_fp8(device=dev), 20),
+    "batched_fp8_wide": (lambda dev: inputs.batched_decode_fp8(device=dev, wide=True), 20),
+    "spec_verify": (lambda dev: inputs.spec_verify(device=dev), 10),
+    "chunked_prefill": (lambda dev: inputs.chunked_prefill(device=dev), 5),
+}
+
+
+def grid(dev):
+    """Every grid workload: step time, tokens/s, algorithmic GB/s and its
+    fraction of 8 TB/s, stage times and the dominant stage's roofline."""
+    res = {}
+    for name, (make, steps) in GRID.items():
+        case = make(dev)
+        step, m = measure(name, case, steps, 3)
+        m["workload"] = {"name": case.name, "batch": case.batch, "query_tokens": case.num_tokens,
+                         "max_context": case.max_ctx, "sum_context": int(case.ctx_lens.sum().item()),
+                         "indexer": f"{case.n_heads_idx}x{case.head_dim_idx} {case.idx_dtype}",
+                         "sparse_attn": f"{case.n_heads_sfa} heads {case.sfa_dtype}", "topk": case.topk}
+        res[name] = m
+        print(f"# grid {name}: {m['ms_per_step'] * 1e3:.1f} us/step, {m['tokens_per_s']:.0f} tokens/s", file=sys.stderr,
+              flush=True)
+        del step, case
+        torch.cuda.empty_cache()
+    return res
+
+
+def prolog_overlap(dev, steps: int = 20):
+    """The step's two producers before the indexer: the indexer-key append and
+    the latent-row append (independent: different pools), either on one
+    stream one after the other, or on two same-priority streams at once,
+    joined by events before the fused decode.  Two sizes: a 64-request 32K
+    decode batch (one new token each) and the chunked prefill (4096 new
+    tokens).  Each variant is timed eagerly and as one captured HIP graph
+    (the two streams become two graph branches), median of 5 runs of `steps`
+    steps."""
+    res = {}
+    for label, case in (("decode_32k_b64", inputs.decode_32k(batch=64, device=dev)),
+                        ("chunked_prefill", inputs.chunked_prefill(device=dev))):
+        T = case.num_tokens
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        k_new = torch.randn((T, case.head_dim_idx), generator=g, device=dev)
+        x_new = torch.randn((T, 576), generator=g, device=dev) * 0.5
+        step = Step(case, 1)
+        ak = dsa.make_cache_append(k_new, "f32", step.k[0], case.idx_dtype, k_scale=step.ks[0])
+        al = dsa.make_latent_append(x_new, "f32", step.kv[0], case.sfa_dtype)
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+        def appends(main, two):
+            if not two:
+                dsa.cache_append(step.paged, ak, stream=main)
+                dsa.latent_append(step.paged, al, stream=main)
+                return
+            s1.wait_stream(main)
+            s2.wait_stream(main)
+            dsa.cache_append(step.paged, ak, stream=s1)
+            dsa.latent_append(step.paged, al, stream=s2)
+            main.wait_stream(s1)
+            main.wait_stream(s2)
+
+        def run(main, two, with_step):
+            appends(main, two)
+            if with_step:
+                step.fused(0, main)
+
+        def eager(two, with_step):
+            main = torch.cuda.current_stream()
+            for _ in range(3):
+                run(main, two, with_step)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(main)
+                for _ in range(steps):
+                    run(main, two, with_step)
+                e1.record(main)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) / steps)
+            return sorted(ts)[2]
+
+        def graph(two, with_step):
+            return time_graph(lambda s_, cs: run(cs, two, with_step), steps, 2)
+
+        r = {"new_tokens": T}
+        for with_step in (False, True):
+            key = "appends_then_step" if with_step else "appends"
+            r[key] = {"one_stream_eager_ms": eager(False, with_step), "two_streams_eager_ms": eager(True, with_step),
+                      "one_stream_graph_ms": graph(False, with_step), "two_streams_graph_ms": graph(True, with_step)}
+        res[label] = r
+        del step, case, k_new, x_new
+        torch.cuda.empty_cache()
+    res["note"] = ("appends: dsa_indexer_cache_append (fp32 keys -> bf16 pool) and dsa_latent_cache_append "
+                   "(fp32 rows -> bf16 latent pool); step: dsa_fused_decode after them")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,15 +570,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=None)
-    ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to exceed 512 MB)")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="cache replicas (0 = enough to exceed three times the 256 MB Infinity Cache)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-grid", action="store_true", help="skip the grid of other workloads")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of replaying a captured HIP graph")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="steps of the chunked-prefill scoring measurement (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain MB-sized device copy (counter calibration)")
+    ap.add_argument("--prolog-only", action="store_true",
+                    help="only measure the two cache appends on one stream against two streams")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -431,55 +595,24 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, 10)
         return
+    if args.prolog_only:
+        print(json.dumps({"prolog_overlap": prolog_overlap(dev, args.steps)}), flush=True)
+        return
 
     w = WORKLOADS[args.workload]
     kw = {} if args.batch is None else {"batch": args.batch}
     case = w["make"](dev, **kw)
-    state_bytes = sum(x.numel() * x.element_size() for x in (case.k_cache, case.kv_cache, case.k_scale)
-                      if x is not None)
-    R = args.replicas or max(1, min(32, math.ceil(512e6 / state_bytes)))
-    step = Step(case, R)
-    ab = algorithmic_bytes(case)
     stream = torch.cuda.current_stream()
-
-    for s in range(args.warmup):
-        step.fused(s, stream)
-    torch.cuda.synchronize()
-    ms_eager = time_steps(step.fused, args.steps, stream)
-    if args.eager:
-        ms = ms_eager
-        t_idx, t_sfa = stage_breakdown(step, args.steps, stream)
-    else:
-        # the whole timed region as one HIP graph: no host launch gaps between steps
-        ms = time_graph(step.fused, args.steps, args.warmup)
-        t_idx = time_graph(step.indexer, args.steps, 1)
-        t_sfa = time_graph(step.sparse_attn, args.steps, 1)
-
+    step, m = measure(args.workload, case, args.steps, args.warmup, args.eager, args.replicas)
     T = case.num_tokens
-    tokens_per_s = T / (ms * 1e-3)
-    dom = "indexer" if t_idx >= t_sfa else "sparse_attn"
-    rows_route = case.max_q_per_req > 4 and T >= 1024 and case.idx_dtype in MFMA_PEAK_TFLOPS
-    kernels_ms = {}
-    if rows_route:
-        # the indexer call is two launches: the scoring GEMM, then per-row selection
-        kernels_ms["indexer_scores"] = time_steps(step.scores_only, args.steps, stream)
-    if dom == "indexer" and rows_route:
-        roofline = roofline_entry("indexer_scores", args.workload, ab["indexer"], ab["indexer_flops"],
-                                  kernels_ms["indexer_scores"], compute_peak(case.idx_dtype))
-    elif dom == "indexer":
-        roofline = roofline_entry("indexer_topk", args.workload, ab["indexer"], ab["indexer_flops"], t_idx,
-                                  compute_peak(case.idx_dtype))
-    else:
-        roofline = roofline_entry("sparse_attn", args.workload, ab["sparse_attn"], ab["sparse_attn_flops"], t_sfa,
-                                  compute_peak("bf16" if case.sfa_dtype == "fp8" else case.sfa_dtype))  # fp8 latent: bf16 MFMAs
     result = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -487,30 +620,31 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["desc"].format(batch=case.batch), "name": case.name, "batch": case.batch,
                    "query_tokens": T, "max_context": case.max_ctx, "topk": case.topk,
-                   "cache_replicas": R, "parallelism": "single GPU",
-                   "launch": "eager" if args.eager else "hip_graph"},
-        "ms_per_step_eager": ms_eager,
-        "hbm_gbs_step": ab["total"] / (ms * 1e-3) / 1e9,
-        "hbm_frac_step": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stages_ms": {"indexer_topk": t_idx, "sparse_attn": t_sfa, **kernels_ms},
-        "roofline": roofline,
+                   "cache_replicas": m["cache_replicas"], "parallelism": "single GPU",
+                   "launch": "eager" if args.eager else "hip_graph", "timing": m["timing"]},
+        "ms_per_step_eager": m["ms_per_step_eager"],
+        "hbm_gbs_step": m["hbm_gbs_step"],
+        "hbm_frac_step": m["hbm_frac_step"],
+        "stages_ms": m["stages_ms"],
+        "roofline": m["roofline"],
         "cache_append": cache_append_timing(case, args.steps, stream),
         "kernel_source_hash": kernel_source_hash(),
     }
-    if args.prefill_steps and args.workload != "chunked_prefill":
-        del step
-        torch.cuda.empty_cache()
-        result["prefill_indexer_mfma"] = prefill_scoring(args.prefill_steps, max(2, args.prefill_steps // 10), stream)
-        step = None
     if not args.no_cpu:
-        if step is None:
-            step = Step(case, 1)
+        # the correctness gate first, on the headline workload's own result
         result["cpu_baseline"] = cpu_baseline(case, step, args.cpu_budget)
         if result["cpu_baseline"]["parity_vs_gpu"] != "ok":
             # a result that fails the correctness gate yields no throughput figure
             result["value"] = None
             print(json.dumps(result), flush=True)
             sys.exit(1)
+    del step, case
+    torch.cuda.empty_cache()
+    if args.prefill_steps and args.workload != "chunked_prefill":
+        result["prefill_indexer_mfma"] = prefill_scoring(args.prefill_steps, max(2, args.prefill_steps // 10), stream)
+    if not args.no_grid and args.workload == "decode_32k" and args.batch is None:
+        result["prolog_overlap"] = prolog_overlap(dev)
+        result["grid"] = grid(dev)
     print(json.dumps(result), flush=True)
 
 

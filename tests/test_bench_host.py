@@ -32,3 +32,23 @@ def test_algorithmic_bytes_quantized_routes():
         100 * 132 + 4 * 128 + 4 * (4 + 4) + 8 + 64
     # fp8 latent rows: 656 bytes each; q and out stay bf16
     assert bench.algorithmic_bytes(_case("bf16", "fp8"))["sparse_attn"] == 64 + 16 * 656 + 16 * (576 + 512) * 2
+
+
+def test_replicas_cover_three_infinity_caches():
+    """The 32K decode state (indexer keys and latent rows, ~46 MB) is rotated
+    over at least 16 replicas, so the rotated state exceeds the 256 MB
+    Infinity Cache three times over; a state above 768 MB needs no replica."""
+    c = inputs.decode_32k(sfa_dtype="bf16")
+    state = sum(x.numel() * x.element_size() for x in (c.k_cache, c.kv_cache) if x is not None)
+    R = bench.replicas_for(c)
+    assert R >= 16 and R * state >= 768e6
+    big = inputs.make_case(name="big", seed=2, ctx_lens=[262144] * 3, n_q=1, idx_dtype="bf16", n_heads_idx=4,
+                           head_dim_idx=64, topk=16, sfa_dtype="bf16", n_heads_sfa=16)
+    assert bench.replicas_for(big) == 1
+
+
+def test_grid_names_every_scope_workload():
+    """The grid carries the 32K batch sweep and the batched fp8 (both widths),
+    speculative-verify and chunked-prefill workloads."""
+    assert {"decode_32k_b8", "decode_32k_b32", "decode_32k_b64", "decode_32k_b128", "batched_fp8_narrow",
+            "batched_fp8_wide", "spec_verify", "chunked_prefill"} <= set(bench.GRID)
