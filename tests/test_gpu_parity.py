@@ -192,10 +192,34 @@ def _full(case, rows, routes=True):
     print(f"[ok] {case.name}: {stats}", flush=True)
 
 
+def _seeded_rows(n_rows, count, seed, must=()):
+    """`count` distinct seeded rows of n_rows, plus the `must` rows, sorted."""
+    rng = np.random.default_rng(seed)
+    rows = set(int(r) for r in must)
+    rows |= set(int(r) for r in rng.choice(n_rows, size=min(count, n_rows), replace=False))
+    return sorted(rows)
+
+
+def _request_rows(case, requests):
+    """Every query row of the given requests."""
+    qo = case.q_offsets.cpu().tolist()
+    return [i for b in requests for i in range(qo[b], qo[b + 1])]
+
+
 def test_chunked_prefill_full():
-    """4096 query rows appended to a 61440-token prefix (65536 positions)."""
+    """4096 query rows appended to a 61440-token prefix (65536 positions):
+    256 seeded rows, rows 0 and 4095 among them."""
     case = inputs.chunked_prefill(device="cuda")
-    _full(case, [0, 1, 1000, 2047, 3333, 4095])
+    _full(case, _seeded_rows(4096, 254, 7, must=(0, 4095)))
+
+
+def test_chunked_prefill_full_exact():
+    """The chunked prefill in exact mode (integer inputs, every score an
+    exact integer, many equal): index sets bit-exact on 64 seeded rows; each
+    row's selection runs over 8 segments of 8192 positions with integer
+    ties."""
+    case = inputs.chunked_prefill(device="cuda", exact=True)
+    _full(case, _seeded_rows(4096, 62, 8, must=(0, 4095)))
 
 
 def test_scratch_prefill_full():
@@ -212,9 +236,20 @@ def test_decode_32k_fp8_latent_full(batch):
 
 
 def test_spec_verify_full():
-    """16 requests x 4 causal query rows at 262144 positions, fp8 indexer."""
+    """16 requests x 4 causal query rows at 262144 positions, fp8 indexer:
+    every row of 4 requests and a seeded sample of the rest."""
     case = inputs.spec_verify(device="cuda")
-    _full(case, [0, 3, 17, 38, 60, 63], routes=False)
+    rows = sorted(set(_request_rows(case, [0, 5, 10, 15])) | set(_seeded_rows(64, 6, 9)))
+    _full(case, rows, routes=False)
+
+
+def test_spec_verify_full_exact():
+    """The speculative-verify shape in exact mode: index sets bit-exact on
+    every row of 4 requests and a seeded sample (32 segments of 8192
+    positions per row, integer ties)."""
+    case = inputs.spec_verify(device="cuda", exact=True)
+    rows = sorted(set(_request_rows(case, [1, 6, 11, 14])) | set(_seeded_rows(64, 4, 10)))
+    _full(case, rows, routes=False)
 
 
 def test_spec_verify_mxfp8_full():
@@ -233,11 +268,20 @@ def test_prefill_mxfp8_full():
 
 @pytest.mark.parametrize("wide", [False, True], ids=["narrow", "wide"])
 def test_batched_fp8_full(wide):
-    """64 single-row requests, lengths uniform in [4096, 131072], fp8 indexer."""
+    """64 single-row requests, lengths uniform in [4096, 131072], fp8 indexer:
+    the longest and shortest requests, 4 fixed ones and a seeded sample."""
     case = inputs.batched_decode_fp8(wide=wide, device="cuda")
     lens = case.ctx_lens.cpu()
-    rows = sorted({0, 63, int(lens.argmax()), int(lens.argmin()), 21, 42})
+    rows = sorted({0, 63, int(lens.argmax()), int(lens.argmin()), 21, 42} | set(_seeded_rows(64, 6, 11)))
     _full(case, rows)
+
+
+def test_batched_fp8_wide_full_exact():
+    """The wide batched fp8 decode in exact mode: bit-exact index sets on a
+    seeded sample of rows, the longest (two-pass selection) among them."""
+    case = inputs.batched_decode_fp8(wide=True, device="cuda", exact=True)
+    lens = case.ctx_lens.cpu()
+    _full(case, sorted({int(lens.argmax()), int(lens.argmin())} | set(_seeded_rows(64, 6, 12))), routes=False)
 
 
 # --- batched decode through the single-kernel indexer ---------------------------
