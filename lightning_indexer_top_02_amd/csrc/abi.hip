@@ -77,7 +77,7 @@ dsa_status_t check_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int32_t topk) 
 struct IndexerPlan {
   int64_t score_stride;
   int cand_cap;
-  size_t ctrl_off, hist_off, scores_off, cand_key_off, cand_pos_off, total;
+  size_t ctrl_off, hist_off, scores_off, cand_key_off, cand_pos_off, keep_off, total;
 };
 
 IndexerPlan plan_indexer(const dsa_paged_t* pg) {
@@ -90,7 +90,8 @@ IndexerPlan plan_indexer(const dsa_paged_t* pg) {
   p.cand_cap = dsa_seg_cand_cap(pg->max_ctx_len);
   p.cand_key_off = p.scores_off + align_up(T * p.score_stride * 4);
   p.cand_pos_off = p.cand_key_off + align_up(T * (size_t)p.cand_cap * 4);
-  p.total = p.cand_pos_off + align_up(T * (size_t)p.cand_cap * 4);
+  p.keep_off = p.cand_pos_off + align_up(T * (size_t)p.cand_cap * 4);
+  p.total = p.keep_off + align_up(T * (size_t)(p.score_stride / 32) * 4);
   return p;
 }
 
@@ -176,6 +177,7 @@ DsaIndexerLaunch indexer_args(const dsa_paged_t* pg, const dsa_indexer_t* x, int
   a.score_stride = plan.score_stride;
   a.cand_key = reinterpret_cast<uint32_t*>(ws + plan.cand_key_off);
   a.cand_pos = reinterpret_cast<int32_t*>(ws + plan.cand_pos_off);
+  a.keep_bits = reinterpret_cast<uint32_t*>(ws + plan.keep_off);
   a.cand_cap = plan.cand_cap;
   a.force_two_pass = (x->flags & (DSA_INDEXER_TWO_PASS | DSA_INDEXER_SCORE_ROWS | DSA_INDEXER_SCORE_POSITIONS)) != 0;
   a.score_route = (x->flags & DSA_INDEXER_SCORE_ROWS) ? 1 : (x->flags & DSA_INDEXER_SCORE_POSITIONS) ? 2 : 0;

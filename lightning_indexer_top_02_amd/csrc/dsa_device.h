@@ -132,6 +132,7 @@ struct DsaIndexerLaunch {
   uint32_t* cand_key;  // [rows][cand_cap] selection candidates (two-pass)
   int32_t* cand_pos;
   int cand_cap;
+  uint32_t* keep_bits;  // [rows][score_stride / 32] kept-position bitmaps (two-pass)
   bool force_two_pass; // skip the fused kernel
   int score_route;     // two-pass scoring: 0 chosen by shape, 1 row-tiled, 2 position-tiled
 };

@@ -22,7 +22,10 @@
 //                  positions gives the last kept position; per-segment kept
 //                  counts become output offsets;
 //   li_seg_write   (a workgroup per segment): writes the kept positions of
-//                  its segment at its offset, in order.
+//                  its segment at its offset, in order, from a bitmap of
+//                  the row's kept positions (li_seg_gather sets the bits of
+//                  the keys above the boundary bin, li_seg_resolve those of
+//                  the kept candidates), so the scores are read only once.
 // A row whose boundary bin holds more keys than the candidate list can take
 // (heavy ties) is flagged and selected whole by li_seg_resolve's workgroup
 // (select_whole_row), and li_seg_write leaves it alone.  The per-row state
@@ -59,6 +62,7 @@ struct SegParams {
   uint32_t* cand_key;  // [rows][cand_cap] low 21 key bits
   int32_t* cand_pos;   // [rows][cand_cap] positions
   int cand_cap;
+  uint32_t* keep;      // [rows][score_stride / 32] bitmap of the kept positions
 };
 
 __device__ __forceinline__ int visible_of(const SegParams& p, int i) {
@@ -141,12 +145,19 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   const int pos0 = s0 + tid * kSegPer;
   seg_keys_from_lds(buf, pos0, vis, key);
   int ngt = 0, neq = 0;
+  uint32_t gtm = 0u;  // bit c: position pos0 + c lies above the boundary bin
 #pragma unroll
-  for (int c = 0; c < kSegPer; ++c) {
+  for (int c = kSegPer - 1; c >= 0; --c) {
     const uint32_t d = key[c] >> kLevelShift[0];
-    ngt += pos0 + c < vis && d > bin1;
+    const bool gt = pos0 + c < vis && d > bin1;
+    ngt += gt;
     neq += pos0 + c < vis && d == bin1;
+    gtm = (gtm << 1) | (gt ? 1u : 0u);
   }
+  // this thread's 32 positions are one word of the row's kept-position
+  // bitmap (rows hold score_stride / 32 words, so the last segment's words
+  // past the row are not there); li_seg_resolve adds the kept candidates
+  if (gather && pos0 < vis) p.keep[(int64_t)i * (p.score_stride / 32) + pos0 / 32] = gtm;
   // keys above the boundary bin: a count per segment
   const int gt_total = block_sum<kSegThreads>(ngt, wsum);
   if (tid == 0) hrow[kSegBase + seg] = (uint32_t)gt_total;
@@ -443,10 +454,14 @@ __global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
   const int nseg = (vis + kSegLen - 1) / kSegLen;
   for (int s = tid; s < nseg; s += kResolveThreads) sh.segc[s] = hrow[kSegBase + s];
   __syncthreads();
+  uint32_t* keep = p.keep + (int64_t)i * (p.score_stride / 32);
   for (int c = tid; c < ncand; c += kResolveThreads) {
     const uint32_t k = ck[c];
     const int pos = cp[c];
-    if (k > low || (k == low && pos <= limit)) atomicAdd(&sh.segc[pos / kSegLen], 1u);
+    if (k > low || (k == low && pos <= limit)) {
+      atomicAdd(&sh.segc[pos / kSegLen], 1u);
+      atomicOr(&keep[pos >> 5], 1u << (pos & 31));
+    }
   }
   __syncthreads();
   constexpr int kPerT = (kMaxSegs + kResolveThreads - 1) / kResolveThreads;
@@ -476,7 +491,6 @@ __global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
 
 __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   __shared__ __align__(16) int wsum[kSegThreads / 64];
-  __shared__ __align__(16) float buf[kSegBufFloats];
   const int i = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int vis = visible_of(p, i);
   const int K = p.K;
@@ -488,31 +502,20 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   const uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
   const int s0 = seg * kSegLen;
   if (s0 >= vis) return;
-  // the segment's scores are in flight while the row's state is read
-  fetch_seg_scores(p.scores + (int64_t)i * p.score_stride, s0, vis, buf);
-  if (hrow[kStateFlags] & 1u) return;  // (uniform) the row was selected whole by li_seg_resolve
-  const uint32_t kth = hrow[kStateKth];
-  const int limit = (int)hrow[kStateLimit];
-  const int off = (int)hrow[kSegBase + seg];
-  __syncthreads();
-  uint32_t key[kSegPer];
+  // the kept positions are the set bits of the row's bitmap (the keys
+  // above the boundary bin, from li_seg_gather, and the kept candidates,
+  // from li_seg_resolve); thread t owns positions s0 + 32 t .. + 31
   const int pos0 = s0 + tid * kSegPer;
-  seg_keys_from_lds(buf, pos0, vis, key);
-  int n = 0;
-#pragma unroll
-  for (int c = 0; c < kSegPer; ++c) {
-    const bool valid = pos0 + c < vis;
-    n += valid && (key[c] > kth || (key[c] == kth && pos0 + c <= limit));
-  }
+  uint32_t sel = pos0 < vis ? p.keep[(int64_t)i * (p.score_stride / 32) + pos0 / 32] : 0u;
+  if (hrow[kStateFlags] & 1u) return;  // (uniform) the row was selected whole by li_seg_resolve
+  const int off = (int)hrow[kSegBase + seg];
   int total;
-  int o = off + block_excl_scan<kSegThreads>(n, total, wsum);
-#pragma unroll
-  for (int c = 0; c < kSegPer; ++c) {
-    const bool valid = pos0 + c < vis;
-    if (valid && (key[c] > kth || (key[c] == kth && pos0 + c <= limit))) {
-      if (o < K) out[o] = pos0 + c;
-      ++o;
-    }
+  int o = off + block_excl_scan<kSegThreads>(__popc(sel), total, wsum);
+  while (sel != 0u) {
+    const int c = __builtin_ctz(sel);
+    if (o < K) out[o] = pos0 + c;
+    ++o;
+    sel &= sel - 1u;
   }
 }
 
@@ -537,6 +540,7 @@ hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s) {
   p.cand_key = a.cand_key;
   p.cand_pos = a.cand_pos;
   p.cand_cap = a.cand_cap;
+  p.keep = a.keep_bits;
   const int nseg = (a.max_ctx_len + kSegLen - 1) / kSegLen;
   const dim3 grid(nseg, a.num_rows);
   hipLaunchKernelGGL(li_seg_gather, grid, dim3(kSegThreads), 0, s, p);
