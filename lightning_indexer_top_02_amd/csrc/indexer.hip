@@ -18,6 +18,7 @@
 //
 // Selection runs over segments of each row (topk_seg.hip).
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_device.h"
 #include "indexer_common.h"
@@ -50,6 +51,8 @@ constexpr int kChunk = 256;         // positions per workgroup and step
 // start-up (chunk search, query staging, histogram flush) once over a long
 // range (speculative verify, 16 x 256K: 300 us with 2048, 270 us with 512).
 constexpr int kScoreTargetWGs = 512;
+// Chunks whose block-table entries a workgroup stages in LDS at a time.
+constexpr int kWinChunks = 256;
 
 // Chunks of 256 positions row group y (rows 4y .. 4y + 3) of request b
 // covers: every position its last row sees, 0 when the request has no such
@@ -61,15 +64,28 @@ __device__ __forceinline__ int chunks_of(const LiParams& p, int b, int r0) {
   return pos_max / kChunk + 1;
 }
 
+template <int DT, int D>
+__host__ __device__ constexpr size_t score_lds_bytes(int rcap, int Hpad) {
+  return query_lds_bytes<DT, D>(rcap, Hpad) + (size_t)rcap * kHistBins * 4 + (DT == 0 ? 0 : kWinChunks * 4 * 4);
+}
+
 // The chunks of all requests (for one row group) form one list, split evenly
 // over the workgroups of the grid's x dimension, so requests of different
 // lengths cost their share and no workgroup waits on a long one.  A
-// workgroup walks its range in order: it stages the request's query rows
-// (and starts its histogram) when it enters a request, flushes the histogram
-// when it leaves, and each wave loads its page of the next chunk while it
-// scores the current one.
+// workgroup walks its range request by request: it stages the request's
+// query rows (and starts its histogram), scores its chunks of the request,
+// and flushes the histogram.  For bf16 and fp8 keys the block-table entries
+// of up to 256 chunks go to LDS first, then each wave scores its page of
+// every chunk with its next page's tiles in flight (1-byte keys: the next
+// two pages', three tile sets rotating).  Every chunk issues the same vector
+// memory operations: past the range a valid page is loaded and not used,
+// pages past the rows' last position are scored and not stored, and the
+// score stores are buffer stores whose masked lanes carry an offset the
+// hardware drops.  The wait for a tile set therefore leaves the later sets'
+// loads in flight (a conditional store or load among them would make it wait
+// for everything).
 template <int DT, int D>
-__global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
+__global__ __launch_bounds__(kScoreThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void li_score(LiParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) int wsum[kScoreThreads / 64];
   __shared__ int s_b0, s_base0;
@@ -77,7 +93,9 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
   unsigned char* qs = smem;
   float* wsm = reinterpret_cast<float*>(smem + (size_t)p.rcap * p.Hpad * Gm::QSTRIDE);
   uint32_t* hl = reinterpret_cast<uint32_t*>(wsm + p.rcap * p.Hpad);
+  int* pages = reinterpret_cast<int*>(hl + p.rcap * kHistBins);  // [kWinChunks][4] (bf16 / fp8)
   const int tid = threadIdx.x, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int r0 = blockIdx.y * kRowsPerBlock;
 
   // total chunks and the request holding this workgroup's first one
@@ -98,16 +116,19 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
   }
   __syncthreads();
 
-  // the request being scored
-  int b = s_b0, base = s_base0, q0 = 0, nb = 0, nrows = 0, first_pos = 0, pos_max = -1, nchunks = 0;
-  auto enter = [&](int nbq) {
-    b = nbq;
+  // the request being scored (uniform over the workgroup)
+  int b = __builtin_amdgcn_readfirstlane(s_b0), base = __builtin_amdgcn_readfirstlane(s_base0);
+  int q0 = 0, nrows = 0, first_pos = 0, pos_max = -1, nchunks = 0;
+  __amdgpu_buffer_rsrc_t srs;  // this request's row group of the score rows
+  auto enter = [&]() {
     q0 = p.q_offsets[b];
-    nb = p.q_offsets[b + 1] - q0;
+    const int nb = p.q_offsets[b + 1] - q0;
     nrows = min(kRowsPerBlock, nb - r0);
     first_pos = p.ctx_lens[b] - nb;
     pos_max = first_pos + r0 + nrows - 1;
     nchunks = pos_max / kChunk + 1;
+    srs = __builtin_amdgcn_make_buffer_rsrc(p.scores + (int64_t)(q0 + r0) * p.score_stride, 0,
+                                            (int)((int64_t)nrows * p.score_stride * 4), 0x00020000);
     stage_queries<DT, D, kScoreThreads>(qs, wsm, p.q, p.q_scale, p.w, q0 + r0, nrows, p.H, p.Hpad);
     for (int c = tid; c < nrows * kHistBins; c += kScoreThreads) hl[c] = 0u;
     __syncthreads();
@@ -123,98 +144,105 @@ __global__ __launch_bounds__(kScoreThreads) void li_score(LiParams p) {
       }
     }
   };
+  // Every lane issues the store; a position row r does not see gets an
+  // offset past the buffer, which the hardware drops.
   auto emit = [&](int r, int pos, float sc) {
-    if (pos <= first_pos + r0 + r) {
-      p.scores[(int64_t)(q0 + r0 + r) * p.score_stride + pos] = sc;
-      atomicAdd(&hl[r * kHistBins + (score_key(sc) >> kLevelShift[0])], 1u);
-    }
+    const bool ok = pos <= first_pos + r0 + r;
+    const uint32_t off = ok ? (uint32_t)(r * p.score_stride + pos) * 4u : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srs, (int)off, 0, 0);
+    if (ok) atomicAdd(&hl[r * kHistBins + (score_key(sc) >> kLevelShift[0])], 1u);
   };
-  enter(b);
 
-  if (DT == 0) {
-    for (int f = f0; f < f1; ++f) {
-      if (f - base >= nchunks) {
-        leave();
-        base += nchunks;
-        int nbq = b + 1;
-        while (chunks_of(p, nbq, r0) == 0) ++nbq;
-        enter(nbq);
-      }
-      const int pos = (f - base) * kChunk + tid;
-      if (pos <= pos_max) {
-        const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
-        const float* krow = static_cast<const float*>(p.k) + ((int64_t)btrow[pos >> 6] * kPage + (pos & 63)) * D;
-        score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, nrows, krow,
-                         [&](int r, float sc) { emit(r, pos, sc); });
-      }
-    }
-  } else {
-    const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
-    // look-ahead cursor: the request, its first flat chunk and page limit of chunk fn
-    int nb_req = b, nb_base = base, nb_chunks = nchunks, nb_posmax = pos_max;
-    auto advance_to = [&](int fn) {
-      while (fn - nb_base >= nb_chunks) {
-        nb_base += nb_chunks;
-        ++nb_req;
-        nb_chunks = chunks_of(p, nb_req, r0);
-        if (nb_chunks) {
-          const int nbb = p.q_offsets[nb_req + 1] - p.q_offsets[nb_req];
-          nb_posmax = p.ctx_lens[nb_req] - nbb + r0 + min(kRowsPerBlock, nbb - r0) - 1;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.k);
+  int f = f0;
+  while (true) {
+    enter();
+    const int c_begin = f - base, c_end = min(f1 - base, nchunks);  // chunks of this request here
+    if constexpr (DT == 0) {
+      const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
+      for (int c = c_begin; c < c_end; ++c) {
+        const int pos = c * kChunk + tid;
+        if (pos <= pos_max) {
+          const float* krow = static_cast<const float*>(p.k) + ((int64_t)btrow[pos >> 6] * kPage + (pos & 63)) * D;
+          score_pos_f32<D>(reinterpret_cast<const float*>(qs), wsm, p.H, nrows, krow,
+                           [&](int r, float sc) { emit(r, pos, sc); });
         }
       }
-    };
-    auto load = [&](KeyTiles<DT, D, 4>& t, int phys) {
-      load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
-                               page_scales<DT, D>(p.k_scale, phys), 0);
-    };
-    // block-table entry of this wave's page of chunk fn (-1: none); read one
-    // chunk ahead of the tile load that needs it, so the tile loads never wait
-    // on a block-table read
-    auto page_of = [&](int fn) {
-      if (fn >= f1) return -1;
-      advance_to(fn);
-      const int pgn = (fn - nb_base) * (kChunk / kPage) + wave;
-      return pgn * kPage <= nb_posmax ? p.bt[(int64_t)nb_req * p.bt_stride + pgn] : -1;
-    };
-    KeyTiles<DT, D, 4> cur, nxt;
-    bool have = false;
-    {
-      const int pg = (f0 - base) * (kChunk / kPage) + wave;
-      if (pg * kPage <= pos_max) {
-        load(nxt, p.bt[(int64_t)b * p.bt_stride + pg]);
-        have = true;
-      }
-    }
-    int ph1 = page_of(f0 + 1);
-    for (int f = f0; f < f1; ++f) {
-      if (f - base >= nchunks) {
-        leave();
-        base += nchunks;
-        int nbq = b + 1;
-        while (chunks_of(p, nbq, r0) == 0) ++nbq;
-        enter(nbq);
-      }
-      cur = nxt;
-      const bool have_cur = have;
-      have = ph1 >= 0;
-      if (have) load(nxt, ph1);  // next chunk's page for this wave
-      ph1 = page_of(f + 2);
-      if (have_cur) {
-        const int pg = (f - base) * (kChunk / kPage) + wave;
-        // one or four rows of 64 heads (decode, speculative verify) with
-        // the row and head-tile loops unrolled, anything else through the
-        // general loops; the sums are formed in the same order either way
-        auto em = [&](int r, int slot, float sc) { emit(r, pg * kPage + slot, sc); };
+    } else {
+      const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
+      for (int w0 = c_begin; w0 < c_end; w0 += kWinChunks) {
+        const int n = min(kWinChunks, c_end - w0);
+        // block-table entries of the window: entry 4j + i is page i of chunk
+        // w0 + j, or the window's first page past the rows' last position
+        __syncthreads();
+        for (int i = tid; i < 4 * n; i += kScoreThreads) {
+          const int pg = w0 * 4 + i;
+          pages[i] = btrow[pg * kPage <= pos_max ? pg : w0 * 4];
+        }
+        __syncthreads();
+        auto load = [&](KeyTiles<DT, D, 4>& t, int j) __attribute__((always_inline)) {
+          const int phys = pages[4 * min(j, n - 1) + wave_u];  // this wave's page of chunk w0 + j (clamped)
+          load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
+                                   page_scales<DT, D>(p.k_scale, phys), 0);
+          // issued here, not sunk below the scoring that follows (the
+          // scheduler would otherwise reuse the scored tile's registers)
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        // The ring for one scoring shape: one or four rows of 64 heads
+        // (decode, speculative verify) with the row and head-tile loops
+        // unrolled, anything else through the general loops (the sums are
+        // formed in the same order either way).  Everything is inlined so the
+        // tile sets stay in registers.
+        auto ring_loop = [&](auto nr_c, auto mt_c) __attribute__((always_inline)) {
+          constexpr int NR = decltype(nr_c)::value, MT = decltype(mt_c)::value;
+          auto score = [&](const KeyTiles<DT, D, 4>& t, int j) __attribute__((always_inline)) {
+            const int pg0 = ((w0 + j) * 4 + wave_u) * kPage;
+            score_key_tiles<DT, D, 4, NR, MT>(qs, wsm, MT > 0 ? 16 * MT : p.Hpad, nrows, t, 0,
+                                              [&](int r, int slot, float sc) { emit(r, pg0 + slot, sc); });
+          };
+          if constexpr (Gm::ES == 1 && NR > 0) {  // 1-byte keys, unrolled shapes: two tile sets ahead
+            KeyTiles<DT, D, 4> t0, t1, t2;
+            load(t0, 0);
+            load(t1, 1);
+            for (int j = 0; j < n; j += 3) {
+              load(t2, j + 2);
+              score(t0, j);
+              if (j + 1 >= n) break;
+              load(t0, j + 3);
+              score(t1, j + 1);
+              if (j + 2 >= n) break;
+              load(t1, j + 4);
+              score(t2, j + 2);
+            }
+          } else {
+            KeyTiles<DT, D, 4> t0, t1;
+            load(t0, 0);
+            for (int j = 0; j < n; j += 2) {
+              load(t1, j + 1);
+              score(t0, j);
+              if (j + 1 >= n) break;
+              load(t0, j + 2);
+              score(t1, j + 1);
+            }
+          }
+        };
         if (nrows == 4 && p.Hpad == 64)
-          score_key_tiles<DT, D, 4, 4, 4>(qs, wsm, 64, 4, cur, 0, em);
+          ring_loop(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
         else if (nrows == 1 && p.Hpad == 64)
-          score_key_tiles<DT, D, 4, 1, 4>(qs, wsm, 64, 1, cur, 0, em);
+          ring_loop(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
         else
-          score_key_tiles<DT, D, 4>(qs, wsm, p.Hpad, nrows, cur, 0, em);
+          ring_loop(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
       }
     }
+    leave();
+    f = base + c_end;
+    if (f >= f1) break;
+    base += nchunks;
+    do {
+      ++b;
+    } while (chunks_of(p, b, r0) == 0);
+    b = __builtin_amdgcn_readfirstlane(b);
   }
-  leave();
 }
 
 }  // namespace dsa
@@ -233,8 +261,9 @@ static hipError_t launch_dyn(Kern kernel, dim3 grid, dim3 block, size_t lds, hip
 
 template <int DT, int D>
 static hipError_t launch_score(const LiParams& p, dim3 grid, hipStream_t s) {
-  const size_t lds = query_lds_bytes<DT, D>(p.rcap, p.Hpad) + (size_t)p.rcap * kHistBins * 4;
-  return launch_dyn(li_score<DT, D>, grid, dim3(kScoreThreads), lds, s, p);
+  // buffer-store offsets are 32-bit: a row group's scores must stay below 2 GiB
+  if ((int64_t)kRowsPerBlock * p.score_stride * 4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  return launch_dyn(li_score<DT, D>, grid, dim3(kScoreThreads), score_lds_bytes<DT, D>(p.rcap, p.Hpad), s, p);
 }
 
 hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s) {

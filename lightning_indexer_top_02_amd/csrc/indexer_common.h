@@ -178,12 +178,16 @@ __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const un
 }
 
 // One wave scores NPT loaded key tiles for `nrows` staged rows.  emit(r,
-// slot, score) runs on lanes 0..15 for slots slot0 + pt * 16 + lane.
-// NR > 0 and MT > 0 fix the row count and Hpad / 16 at compile time: the
-// row and head-tile loops are then fully unrolled, so no loop reads the key
-// registers (a loop that does makes the compiler wait for every outstanding
-// vector load before entering it, prefetched tiles included).  The sums are
-// formed in the same order either way.
+// slot, score) runs on lanes 0..15 for slots slot0 + pt * 16 + lane, except
+// on the two unrolled shapes of four values per lane group: with NR = 4
+// every lane emits row g (lane group g) for each tile, and with NR = 1 and
+// NPT = 4 every lane emits slot slot0 + lane (tile g), so the head sums are
+// split over the lane groups by group4_sum_scatter and every emit runs on
+// all 64 lanes.  NR > 0 and MT > 0 fix the row count and Hpad / 16 at
+// compile time: the row and head-tile loops are then fully unrolled, so no
+// loop reads the key registers (a loop that does makes the compiler wait for
+// every outstanding vector load before entering it, prefetched tiles
+// included).  The sums are formed in the same order on every shape.
 template <int DT, int D, int NPT, int NR = 0, int MT = 0, class Emit>
 __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const float* wsm, int Hpad, int nrows,
                                                 const KeyTiles<DT, D, NPT>& t, int slot0, Emit&& emit) {
@@ -215,8 +219,8 @@ __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const f
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[pt] += wr[i] * relu_keep_nan(acc[pt][i]);
   };
-  auto row = [&](int r) {
-    float sacc[NPT];
+  // per-lane partial head sums of row r for each tile
+  auto row_sums = [&](int r, float (&sacc)[NPT]) {
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) sacc[pt] = 0.f;
     if constexpr (MT > 0) {
@@ -225,17 +229,44 @@ __device__ __forceinline__ void score_key_tiles(const unsigned char* qs, const f
     } else {
       for (int ht = 0; ht < Hpad / 16; ++ht) head_tile(r, ht, sacc);
     }
+  };
+  if constexpr (NR == 4) {
+    float sacc[4][NPT];
+    // rows one after another: each row's sums are pinned (empty asm) before
+    // the next row starts, else the compiler defers the epilogues and keeps
+    // all four rows' MFMA results, which no longer fit the registers
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      row_sums(r, sacc[r]);
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) asm volatile("" : "+v"(sacc[r][pt]));
+    }
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
-      const float s = group4_sum(sacc[pt]);
-      if (g == 0) emit(r, slot0 + pt * 16 + l16, s * t.kscale[pt]);
+      const float x[4] = {sacc[0][pt], sacc[1][pt], sacc[2][pt], sacc[3][pt]};
+      emit(g, slot0 + pt * 16 + l16, group4_sum_scatter(x) * t.kscale[pt]);
     }
-  };
-  if constexpr (NR > 0) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) row(r);
+  } else if constexpr (NR == 1 && NPT == 4) {
+    float sacc[4];
+    row_sums(0, sacc);
+    const float ks = g == 0 ? t.kscale[0] : (g == 1 ? t.kscale[1] : (g == 2 ? t.kscale[2] : t.kscale[3]));
+    emit(0, slot0 + lane, group4_sum_scatter(sacc) * ks);
   } else {
-    for (int r = 0; r < nrows; ++r) row(r);
+    auto row = [&](int r) {
+      float sacc[NPT];
+      row_sums(r, sacc);
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        const float s = group4_sum(sacc[pt]);
+        if (g == 0) emit(r, slot0 + pt * 16 + l16, s * t.kscale[pt]);
+      }
+    };
+    if constexpr (NR > 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) row(r);
+    } else {
+      for (int r = 0; r < nrows; ++r) row(r);
+    }
   }
 }
 
