@@ -91,7 +91,7 @@ IndexerPlan plan_indexer(const dsa_paged_t* pg) {
   p.cand_key_off = p.scores_off + align_up(T * p.score_stride * 4);
   p.cand_pos_off = p.cand_key_off + align_up(T * (size_t)p.cand_cap * 4);
   p.keep_off = p.cand_pos_off + align_up(T * (size_t)p.cand_cap * 4);
-  p.total = p.keep_off + align_up(T * (size_t)(p.score_stride / 32) * 4);
+  p.total = p.keep_off + align_up(T * (size_t)dsa_seg_keep_words(p.score_stride) * 4);
   return p;
 }
 

@@ -147,7 +147,7 @@ struct DsaIndexerLaunch {
   uint32_t* cand_key;  // [rows][cand_cap] selection candidates (two-pass)
   int32_t* cand_pos;
   int cand_cap;
-  uint32_t* keep_bits;  // [rows][score_stride / 32] kept-position bitmaps (two-pass)
+  uint32_t* keep_bits;  // [rows][dsa_seg_keep_words(score_stride)] kept-position bitmaps (two-pass)
   bool force_two_pass; // skip the fused kernel
   int score_route;     // two-pass scoring: 0 chosen by shape, 1 row-tiled, 2 position-tiled
 };
@@ -208,5 +208,6 @@ hipError_t dsa_launch_indexer_prefill_scores(const DsaIndexerLaunch& a, hipStrea
 hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s);
 int dsa_seg_max_segments();
 int dsa_seg_cand_cap(int max_ctx_len);
+int64_t dsa_seg_keep_words(int64_t score_stride);  // kept-position bitmap words per row
 bool dsa_indexer_rows_route(const DsaIndexerLaunch& a);
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s);

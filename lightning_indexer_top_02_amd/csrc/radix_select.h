@@ -71,6 +71,23 @@ __device__ __forceinline__ void kth_bin_loaded(const uint32_t (&v)[PER], int k, 
   above = wave_read_lane(ra, src);
 }
 
+// kth_bin_loaded that also returns the count of the bin it finds (0 when
+// the bins hold fewer than k keys).
+template <int PER>
+__device__ __forceinline__ void kth_bin_wave_count(const uint32_t* bins, int k, int& bin, int& above, int& total,
+                                                   int& count) {
+  uint32_t v[PER];
+  load_bins_wave<PER>(bins, v);
+  kth_bin_loaded<PER>(v, k, bin, above, total);
+  // the lane owning the bin reads its count
+  const int lane = threadIdx.x & 63, lo = PER * 64 - (lane + 1) * PER;
+  int mine = -1;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) mine = lo + j == bin ? (int)v[j] : mine;
+  const uint64_t owner = __ballot(mine >= 0);
+  count = owner ? wave_read_lane(mine, __ffsll((long long)owner) - 1) : 0;
+}
+
 template <int PER>
 __device__ __forceinline__ void kth_bin_wave(const uint32_t* bins, int k, int& bin, int& above, int& total) {
   uint32_t v[PER];

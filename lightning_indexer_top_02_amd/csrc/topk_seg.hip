@@ -13,19 +13,23 @@
 // key bits in the workspace.  A row is then cut into segments of 8192
 // positions and handled by three kernels:
 //   li_seg_gather  (a workgroup per segment): finds the histogram bin that
-//                  holds the K-th key, counts the segment's keys above it and
-//                  appends the keys of that bin (low 21 bits and position) to
-//                  the row's candidate list;
+//                  holds the K-th key, counts the segment's keys above it,
+//                  marks them in a bitmap of the row's kept positions and
+//                  appends the keys of that bin (low 21 bits and position)
+//                  to the row's candidate list;
 //   li_seg_resolve (a workgroup per row): two more radix digits over the
 //                  candidates give the K-th key exactly; if fewer keys equal
 //                  to it are kept than exist, a radix select over their
-//                  positions gives the last kept position; per-segment kept
+//                  positions gives the last kept position; the kept
+//                  candidates are marked in the bitmap and per-segment kept
 //                  counts become output offsets;
 //   li_seg_write   (a workgroup per segment): writes the kept positions of
-//                  its segment at its offset, in order, from a bitmap of
-//                  the row's kept positions (li_seg_gather sets the bits of
-//                  the keys above the boundary bin, li_seg_resolve those of
-//                  the kept candidates), so the scores are read only once.
+//                  its segment at its offset, in order, from the bitmap, so
+//                  the scores are read only once.
+// Thread t of a segment reads positions s0 + 1024 c + 4 t + e (c < 8,
+// e < 4): each wave load is 1 KB of consecutive scores, with no staging
+// buffer.  Bit 4 c + e of the segment's bitmap word t marks that position;
+// li_seg_write regathers the bits of 32 consecutive positions per thread.
 // A row whose boundary bin holds more keys than the candidate list can take
 // (heavy ties) is flagged and selected whole by li_seg_resolve's workgroup
 // (select_whole_row), and li_seg_write leaves it alone.  The per-row state
@@ -62,53 +66,25 @@ struct SegParams {
   uint32_t* cand_key;  // [rows][cand_cap] low 21 key bits
   int32_t* cand_pos;   // [rows][cand_cap] positions
   int cand_cap;
-  uint32_t* keep;      // [rows][score_stride / 32] bitmap of the kept positions
+  uint32_t* keep;      // [rows][keep_words] bitmap of the kept positions (layout above)
 };
+
+// Bitmap words per row: kSegLen / 32 per segment of the score stride.
+__host__ __device__ constexpr int64_t keep_words(int64_t score_stride) {
+  return (score_stride + kSegLen - 1) / kSegLen * (kSegLen / 32);
+}
+
+// Word and bit of position pos in its row's bitmap.
+__device__ __forceinline__ void keep_bit(int pos, int& word, int& bit) {
+  const int seg = pos / kSegLen, o = pos - seg * kSegLen;
+  word = seg * (kSegLen / 32) + ((o & 1023) >> 2);
+  bit = 4 * (o >> 10) + (o & 3);
+}
 
 __device__ __forceinline__ int visible_of(const SegParams& p, int i) {
   const int b = request_of_row(p.q_offsets, p.batch, i);
   const int nb = p.q_offsets[b + 1] - p.q_offsets[b];
   return p.ctx_lens[b] - nb + (i - p.q_offsets[b]) + 1;
-}
-
-// A segment's scores pass through LDS so that the global reads are
-// coalesced (float4 q of the segment from thread q % kSegThreads) while each
-// thread still ends up with kSegPer consecutive keys (position order is
-// thread order).  Rows are padded by 4 floats every 32, so the per-thread
-// 16-byte reads of a 16-lane group start 36 floats apart and fill all banks.
-constexpr int kSegBufFloats = kSegLen + kSegLen / 8;
-
-// Issue the segment's reads into the LDS buffer (s0: first position).
-__device__ __forceinline__ void fetch_seg_scores(const float* row, int s0, int vis, float* buf) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kSegPer / 4; ++j) {
-    const int q = j * kSegThreads + tid;  // float4 of the segment
-    const int t = s0 + 4 * q;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t + 4 <= vis) {
-      v = *reinterpret_cast<const float4*>(row + t);
-    } else {
-      if (t < vis) v.x = row[t];
-      if (t + 1 < vis) v.y = row[t + 1];
-      if (t + 2 < vis) v.z = row[t + 2];
-    }
-    *reinterpret_cast<float4*>(buf + 4 * q + 4 * (q >> 3)) = v;
-  }
-}
-
-// This thread's kSegPer consecutive keys from the buffer (key 0 past vis);
-// the caller has synchronised the workgroup after fetch_seg_scores.
-__device__ __forceinline__ void seg_keys_from_lds(const float* buf, int pos0, int vis, uint32_t (&key)[kSegPer]) {
-  const float* mine = buf + threadIdx.x * (kSegPer + kSegPer / 8);
-#pragma unroll
-  for (int c = 0; c < kSegPer; c += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(mine + c);
-    key[c] = pos0 + c < vis ? score_key(v.x) : 0u;
-    key[c + 1] = pos0 + c + 1 < vis ? score_key(v.y) : 0u;
-    key[c + 2] = pos0 + c + 2 < vis ? score_key(v.z) : 0u;
-    key[c + 3] = pos0 + c + 3 < vis ? score_key(v.w) : 0u;
-  }
 }
 
 // Sum over the workgroup (result valid in every thread).
@@ -119,45 +95,69 @@ __device__ __forceinline__ int block_sum(int v, int* wsum) {
   return total;
 }
 
+static_assert(kSegThreads * 32 == kSegLen, "one bitmap word of 32 positions per thread");
+
 __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   __shared__ __align__(16) int wsum[kSegThreads / 64];
   __shared__ int sh[3];
-  __shared__ __align__(16) float buf[kSegBufFloats];
   const int i = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int vis = visible_of(p, i);
   const int s0 = seg * kSegLen;
   if (vis <= p.K || s0 >= vis) return;
   uint32_t* hrow = p.hist + (int64_t)i * kHistStride;
-  // the segment's scores are in flight while wave 0 reads the histogram
-  fetch_seg_scores(p.scores + (int64_t)i * p.score_stride, s0, vis, buf);
-  if (tid < 64) {
-    int bin, above, total;
-    kth_bin_wave<32>(hrow, p.K, bin, above, total);
+  // waves 1-3 issue their score loads at once; wave 0 first finds the
+  // boundary bin in the row's histogram, then issues its own (its bins and
+  // scores are never live together, which keeps the register count low)
+  const float* row = p.scores + (int64_t)i * p.score_stride;
+  float4 v[8];
+  auto load_scores = [&]() {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int t = s0 + 1024 * c + 4 * tid;
+      v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t + 4 <= vis) {
+        v[c] = *reinterpret_cast<const float4*>(row + t);
+      } else {
+        if (t < vis) v[c].x = row[t];
+        if (t + 1 < vis) v[c].y = row[t + 1];
+        if (t + 2 < vis) v[c].z = row[t + 2];
+      }
+    }
+  };
+  if (tid >= 64) {
+    load_scores();
+  } else {
+    int bin, above, total, count;
+    kth_bin_wave_count<32>(hrow, p.K, bin, above, total, count);
     if (tid == 0) {
       sh[0] = bin;
-      sh[1] = (int)hrow[bin];
+      sh[1] = count;
     }
+    load_scores();
   }
   __syncthreads();
   const uint32_t bin1 = (uint32_t)sh[0];
   const bool gather = sh[1] <= p.cand_cap;
-  uint32_t key[kSegPer];
-  const int pos0 = s0 + tid * kSegPer;
-  seg_keys_from_lds(buf, pos0, vis, key);
-  int ngt = 0, neq = 0;
-  uint32_t gtm = 0u;  // bit c: position pos0 + c lies above the boundary bin
+  // key of element b of this thread (0 past the row; the callers also test t < vis)
+  auto key_of = [&](int b) {
+    const float4 q = v[b >> 2];
+    const float x = (b & 3) == 0 ? q.x : ((b & 3) == 1 ? q.y : ((b & 3) == 2 ? q.z : q.w));
+    return score_key(x);
+  };
+  // bit 4c + e of gtm / eqm: position s0 + 1024 c + 4 tid + e is visible and
+  // lies above / in the boundary bin
+  const int lim = vis - s0 - 4 * tid;
+  uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
-  for (int c = kSegPer - 1; c >= 0; --c) {
-    const uint32_t d = key[c] >> kLevelShift[0];
-    const bool gt = pos0 + c < vis && d > bin1;
-    ngt += gt;
-    neq += pos0 + c < vis && d == bin1;
-    gtm = (gtm << 1) | (gt ? 1u : 0u);
+  for (int b = 0; b < 32; ++b) {
+    const bool ok = 1024 * (b >> 2) + (b & 3) < lim;
+    const uint32_t d = key_of(b) >> kLevelShift[0];
+    gtm |= ok && d > bin1 ? 1u << b : 0u;
+    eqm |= ok && d == bin1 ? 1u << b : 0u;
   }
-  // this thread's 32 positions are one word of the row's kept-position
-  // bitmap (rows hold score_stride / 32 words, so the last segment's words
-  // past the row are not there); li_seg_resolve adds the kept candidates
-  if (gather && pos0 < vis) p.keep[(int64_t)i * (p.score_stride / 32) + pos0 / 32] = gtm;
+  const int ngt = __popc(gtm), neq = __popc(eqm);
+  // li_seg_resolve adds the kept candidates to the bitmap
+  if (gather) p.keep[i * keep_words(p.score_stride) + seg * (kSegLen / 32) + tid] = gtm;
   // keys above the boundary bin: a count per segment
   const int gt_total = block_sum<kSegThreads>(ngt, wsum);
   if (tid == 0) hrow[kSegBase + seg] = (uint32_t)gt_total;
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   uint32_t* ck = p.cand_key + (int64_t)i * p.cand_cap;
   int32_t* cp = p.cand_pos + (int64_t)i * p.cand_cap;
 #pragma unroll
-  for (int c = 0; c < kSegPer; ++c) {
-    if (pos0 + c < vis && (key[c] >> kLevelShift[0]) == bin1) {
+  for (int b = 0; b < 32; ++b) {
+    if ((eqm >> b) & 1u) {
       if (o < p.cand_cap) {
-        ck[o] = key[c] & 0x1fffffu;
-        cp[o] = pos0 + c;
+        ck[o] = key_of(b) & 0x1fffffu;
+        cp[o] = s0 + 1024 * (b >> 2) + 4 * tid + (b & 3);
       }
       ++o;
     }
@@ -454,13 +454,15 @@ __global__ __launch_bounds__(kResolveThreads) void li_seg_resolve(SegParams p) {
   const int nseg = (vis + kSegLen - 1) / kSegLen;
   for (int s = tid; s < nseg; s += kResolveThreads) sh.segc[s] = hrow[kSegBase + s];
   __syncthreads();
-  uint32_t* keep = p.keep + (int64_t)i * (p.score_stride / 32);
+  uint32_t* keep = p.keep + i * keep_words(p.score_stride);
   for (int c = tid; c < ncand; c += kResolveThreads) {
     const uint32_t k = ck[c];
     const int pos = cp[c];
     if (k > low || (k == low && pos <= limit)) {
       atomicAdd(&sh.segc[pos / kSegLen], 1u);
-      atomicOr(&keep[pos >> 5], 1u << (pos & 31));
+      int word, bit;
+      keep_bit(pos, word, bit);
+      atomicOr(&keep[word], 1u << bit);
     }
   }
   __syncthreads();
@@ -504,9 +506,20 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   if (s0 >= vis) return;
   // the kept positions are the set bits of the row's bitmap (the keys
   // above the boundary bin, from li_seg_gather, and the kept candidates,
-  // from li_seg_resolve); thread t owns positions s0 + 32 t .. + 31
-  const int pos0 = s0 + tid * kSegPer;
-  uint32_t sel = pos0 < vis ? p.keep[(int64_t)i * (p.score_stride / 32) + pos0 / 32] : 0u;
+  // from li_seg_resolve); thread t takes positions s0 + 32 t .. + 31, whose
+  // bits are bits 4c .. 4c + 3 (c = t / 32) of the segment's words
+  // 8 (t % 32) .. + 7
+  const int pos0 = s0 + tid * 32;
+  uint32_t sel = 0u;
+  if (pos0 < vis) {
+    const uint4* w4 = reinterpret_cast<const uint4*>(p.keep + i * keep_words(p.score_stride) + seg * (kSegLen / 32) +
+                                                     8 * (tid & 31));
+    const uint4 a = w4[0], b = w4[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const int c4 = 4 * (tid >> 5);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) sel |= ((w[m] >> c4) & 0xfu) << (4 * m);
+  }
   if (hrow[kStateFlags] & 1u) return;  // (uniform) the row was selected whole by li_seg_resolve
   const int off = (int)hrow[kSegBase + seg];
   int total;
@@ -525,6 +538,7 @@ using namespace dsa;
 
 int dsa_seg_max_segments() { return kMaxSegs; }
 int dsa_seg_cand_cap(int max_ctx_len) { return std::min((max_ctx_len + 255) / 256 * 256, 8192); }
+int64_t dsa_seg_keep_words(int64_t score_stride) { return keep_words(score_stride); }
 
 // The three segment kernels (flagged rows are selected inside li_seg_resolve).
 hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s) {

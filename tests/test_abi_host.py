@@ -149,8 +149,8 @@ def test_workspace_sizes():
     # arrival counters [B] u32 | digit histograms [T][3 * 2048] u32 |
     # scores [T][round_up(L, 256)] f32, each region 256-byte aligned
     # counters | histograms | scores | selection candidates (keys, positions; min(L, 8192) per row) |
-    # kept-position bitmaps (a bit per score slot, region rounded to 256 bytes)
-    assert need == 256 + 5 * 6144 * 4 + 5 * 1024 * 4 + 2 * 5 * 1024 * 4 + 768
+    # kept-position bitmaps (a bit per position of each 8192-position segment of the score stride)
+    assert need == 256 + 5 * 6144 * 4 + 5 * 1024 * 4 + 2 * 5 * 1024 * 4 + 5 * 256 * 4
     # one row of 128 heads at small batch splits the index list; fp32 never does
     one = good_paged(batch=1, num_q_tokens=1, max_q_per_req=1)
     s_bf16 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa()), 2048)
