@@ -181,7 +181,10 @@ __global__ __launch_bounds__(kScoreThreads, 2) __attribute__((amdgpu_waves_per_e
         }
         __syncthreads();
         auto load = [&](KeyTiles<DT, D, 4>& t, int j) __attribute__((always_inline)) {
-          const int phys = pages[4 * min(j, n - 1) + wave_u];  // this wave's page of chunk w0 + j (clamped)
+          // this wave's page of chunk w0 + j (clamped), in a scalar register:
+          // the addresses are then a scalar base plus fixed lane offsets, and
+          // no vector register is written between a tile's loads and its use
+          const int phys = __builtin_amdgcn_readfirstlane(pages[4 * min(j, n - 1) + wave_u]);
           load_key_tiles<DT, D, 4>(t, kbase + (int64_t)phys * kPage * D * Gm::ES,
                                    page_scales<DT, D>(p.k_scale, phys), 0);
           // issued here, not sunk below the scoring that follows (the
@@ -204,26 +207,31 @@ __global__ __launch_bounds__(kScoreThreads, 2) __attribute__((amdgpu_waves_per_e
             KeyTiles<DT, D, 4> t0, t1, t2;
             load(t0, 0);
             load(t1, 1);
-            for (int j = 0; j < n; j += 3) {
+            // whole turns of the ring, then the one or two chunks left: no
+            // exit inside the loop, so the waits in it see only the ring's
+            // own loads in flight
+            int j = 0;
+            for (; j + 3 <= n; j += 3) {
               load(t2, j + 2);
               score(t0, j);
-              if (j + 1 >= n) break;
               load(t0, j + 3);
               score(t1, j + 1);
-              if (j + 2 >= n) break;
               load(t1, j + 4);
               score(t2, j + 2);
             }
+            if (j < n) score(t0, j);
+            if (j + 1 < n) score(t1, j + 1);
           } else {
             KeyTiles<DT, D, 4> t0, t1;
             load(t0, 0);
-            for (int j = 0; j < n; j += 2) {
+            int j = 0;
+            for (; j + 2 <= n; j += 2) {
               load(t1, j + 1);
               score(t0, j);
-              if (j + 1 >= n) break;
               load(t0, j + 2);
               score(t1, j + 1);
             }
+            if (j < n) score(t0, j);
           }
         };
         if (nrows == 4 && p.Hpad == 64)

@@ -168,12 +168,13 @@ __device__ __forceinline__ void load_key_tiles(KeyTiles<DT, D, NPT>& t, const un
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) t.kf[pt][ks] = G::load_frag(kpage + (slot0 + pt * 16 + l16) * D * G::ES, ks, g);
+    for (int ks = 0; ks < G::KS; ++ks)
+      t.kf[pt][ks] = G::load_frag(kpage + (uint32_t)(slot0 + pt * 16 + l16) * (uint32_t)(D * G::ES), ks, g);
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt) {
     const int slot = slot0 + pt * 16 + l16;
-    t.kscale[pt] = DT == 2 ? static_cast<const float*>(kscale_page)[slot] : 1.f;
-    t.kmx[pt] = DT == 3 ? static_cast<const uint8_t*>(kscale_page)[slot * (D / 32) + g] : 0;
+    t.kscale[pt] = DT == 2 ? static_cast<const float*>(kscale_page)[(uint32_t)slot] : 1.f;
+    t.kmx[pt] = DT == 3 ? static_cast<const uint8_t*>(kscale_page)[(uint32_t)(slot * (D / 32) + g)] : 0;
   }
 }
 
