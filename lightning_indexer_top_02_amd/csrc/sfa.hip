@@ -92,16 +92,16 @@ constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chu
 // a scale per token and 128-element tile): the 512 latent dims as e4m3 codes,
 // a 16-byte block whose first four bytes are the tiles' E8M0 exponents
 // (power-of-two scales), then the 64 rope dims in bf16, 656 bytes.  A chunk
-// is gathered as 40 pieces per row (32 of codes, each with its tile's
-// exponent, and 8 of rope) and staged in the same bf16 LDS layout as the bf16
-// route, so everything after the staging is shared.  code * 2^e is exact in
+// is gathered by 16 threads per row: thread k takes code pieces k and k + 16
+// (16 codes each) and, for k < 8, rope piece k, and the first thread of the
+// 16 also loads the row's exponent word, which the others read from it with
+// lane reads at staging (41 loads per row, where one exponent load per code
+// piece took 72).  The rows are staged in the same bf16 LDS layout as the
+// bf16 route, so everything after the staging is shared.  code * 2^e is exact in
 // bf16, and gfx950's scaled conversion (v_cvt_scalef32_pk_bf16_fp8, which
 // applies the exponent of its fp32 scale operand) makes two values per
 // instruction.
 constexpr int kF8RowBytes = kVDim + 16 + 2 * (kQkDim - kVDim);
-constexpr int kF8CodePieces = kVDim / 16;
-constexpr int kF8RowItems = kF8CodePieces + (kQkDim - kVDim) * 2 / 16;
-constexpr int kF8Items = kSfaRows * kF8RowItems;
 static_assert(kF8RowBytes % 16 == 0, "fp8 latent rows stay 16-byte aligned");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -128,7 +128,9 @@ struct SfaXchg {
 template <int NW, bool F8>
 __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   constexpr int NT = NW * 128;
-  constexpr int PPT = ((F8 ? kF8Items : kPieces) + NT - 1) / NT;  // gathered pieces per thread per chunk
+  // fp8: RP rows per pass of 16 threads each, PASSES passes per chunk
+  constexpr int RP = NT / 16, PASSES = (kSfaRows + RP - 1) / RP;
+  constexpr int PPT = F8 ? 3 * PASSES : (kPieces + NT - 1) / NT;  // gathered pieces per thread per chunk
   constexpr int kHalfDims = kVDim / 2;
   extern __shared__ __align__(16) unsigned char smem[];
   SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + 2 * kKrowBytes);
@@ -178,25 +180,29 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   __syncthreads();
 
   // gather of one chunk into registers: PPT 16-byte pieces of its rows
-  // (fp8: code pieces with their tile scales, and rope pieces)
+  // (fp8: per pass two code pieces and a rope piece of one row, and the
+  // row's exponent word on the first lane of each 16-lane group)
   uint4 va[PPT];
-  float vs[F8 ? PPT : 1];
+  uint32_t ew[F8 ? PASSES : 1];
   const unsigned char* kv8 = static_cast<const unsigned char*>(p.kv);
   auto gather = [&](int c0) {
+    if constexpr (F8) {
+      const int k = tid & 15;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int it = tid + j * NT;
-      if constexpr (F8) {
-        const int r = it / kF8RowItems, part = it - r * kF8RowItems;
-        const int row = it < kF8Items ? rowidx[c0 + r] : -1;
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int r = ps * RP + (tid >> 4);
+        const int row = r < kSfaRows ? rowidx[c0 + r] : -1;
         const unsigned char* rb = kv8 + (int64_t)max(row, 0) * kF8RowBytes;
-        const bool code = part < kF8CodePieces;
-        const int off = code ? part * 16 : kVDim + 16 + (part - kF8CodePieces) * 16;
-        va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + off) : make_uint4(0u, 0u, 0u, 0u);
-        // the tile's scale 2^(E - 127) as an fp32 (exponent field E, E in 1 .. 254)
-        const uint32_t ew = row >= 0 && code ? *reinterpret_cast<const uint32_t*>(rb + kVDim) : 0u;
-        vs[j] = __uint_as_float(((ew >> (8 * (part >> 3))) & 0xFFu) << 23);
-      } else {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        va[3 * ps] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + 16 * k) : z;
+        va[3 * ps + 1] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + 16 * (k + 16)) : z;
+        va[3 * ps + 2] = row >= 0 && k < 8 ? *reinterpret_cast<const uint4*>(rb + kVDim + 16 + 16 * k) : z;
+        ew[ps] = row >= 0 && k == 0 ? *reinterpret_cast<const uint32_t*>(rb + kVDim) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        const int it = tid + j * NT;
         const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
         const int row = it < kPieces ? rowidx[c0 + r] : -1;
         va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + part * 8)
@@ -205,27 +211,40 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
     }
   };
   auto stage = [&](unsigned char* kb) {
+    if constexpr (F8) {
+      const int k = tid & 15, grp = (tid >> 4) & 3;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int it = tid + j * NT;
-      if constexpr (F8) {
-        const int r = it / kF8RowItems, part = it - r * kF8RowItems;
-        if (it >= kF8Items) continue;
-        if (part < kF8CodePieces) {  // 16 codes -> 16 bf16 values (32 bytes)
-          const uint32_t w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int r = ps * RP + (tid >> 4);
+        // the row's exponent word, from the first lane of this 16-lane group
+        const uint32_t e0 = wave_read_lane((int)ew[ps], 0), e1 = wave_read_lane((int)ew[ps], 16);
+        const uint32_t e2 = wave_read_lane((int)ew[ps], 32), e3 = wave_read_lane((int)ew[ps], 48);
+        const uint32_t e = grp == 0 ? e0 : (grp == 1 ? e1 : (grp == 2 ? e2 : e3));
+        if (r >= kSfaRows) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {  // code piece k + 16 q: 16 codes -> 16 bf16 values (32 bytes)
+          const int piece = k + 16 * q;
+          // the tile's scale 2^(E - 127) as an fp32 (exponent field E, E in 1 .. 254)
+          const float sc = __uint_as_float(((e >> (8 * (piece >> 3))) & 0xFFu) << 23);
+          const uint4 c = va[3 * ps + q];
+          const uint32_t w[4] = {c.x, c.y, c.z, c.w};
           uint32_t o8[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {  // codes 4k, 4k + 1 (low half), 4k + 2, 4k + 3 (high half)
-            o8[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], vs[j], false));
-            o8[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], vs[j], true));
+          for (int m = 0; m < 4; ++m) {  // codes 4m, 4m + 1 (low half), 4m + 2, 4m + 3 (high half)
+            o8[2 * m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[m], sc, false));
+            o8[2 * m + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[m], sc, true));
           }
-          uint4* d = reinterpret_cast<uint4*>(kb + r * kRowStride + part * 32);
+          uint4* d = reinterpret_cast<uint4*>(kb + r * kRowStride + piece * 32);
           d[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
           d[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-        } else {  // rope: already bf16
-          *reinterpret_cast<uint4*>(kb + r * kRowStride + kVDim * 2 + (part - kF8CodePieces) * 16) = va[j];
         }
-      } else {
+        if (k < 8)  // rope: already bf16
+          *reinterpret_cast<uint4*>(kb + r * kRowStride + kVDim * 2 + 16 * k) = va[3 * ps + 2];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        const int it = tid + j * NT;
         const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
         if (it < kPieces) *reinterpret_cast<uint4*>(kb + r * kRowStride + part * 16) = va[j];
       }
