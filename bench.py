@@ -14,6 +14,7 @@ bounded sample of the same workload and checks the GPU result against it.
 from __future__ import annotations
 
 import argparse
+import csv
 import glob
 import hashlib
 import json
@@ -244,6 +245,71 @@ def measured_traffic(kernel: str, workload: str):
     if d.get("source_hash") != kernel_source_hash():
         return None
     return d["bytes_per_launch"]
+
+
+# HBM byte counters: bytes moved = FETCH_SIZE KiB x FETCH_SCALE + WRITE_SIZE KiB
+# x WRITE_SCALE (x 1024), the factors a plain 256 MiB device copy of known
+# traffic gives (`--calibrate-copy 256` under rocprofv3 --pmc).
+FETCH_SCALE, WRITE_SCALE = 1.999817388043494, 1.0
+
+# The kernels of one call of each measured stage, by name.
+KERNEL_GROUPS = {
+    "indexer_topk": ("li_fused", "li_score", "li_prefill", "li_seg_gather", "li_seg_resolve", "li_seg_write"),
+    "indexer_scores": ("li_prefill",),
+    "sparse_attn": ("sfa_bf16", "sfa_f32", "sfa_combine"),
+}
+
+
+def traffic_summary(label: str, fetch_csv: str, write_csv: str, bench_args: str, out_dir: str = "") -> str:
+    """Per-launch HBM bytes of each stage from two rocprofv3 counter runs
+    (FETCH_SIZE, then WRITE_SIZE, one row per dispatch): the median over
+    dispatches of each kernel, summed over the kernels of one call, scaled by
+    the copy factors.  Writes profiles/traffic_<stage>_<label>.json (with the
+    kernel-source hash they hold for) and returns a markdown summary."""
+    per = {}
+    for path, ctr in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == ctr:
+                    per.setdefault(r["Kernel_Name"], {}).setdefault(ctr, []).append(float(r["Counter_Value"]))
+
+    def median(v):
+        v = sorted(v)
+        return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+    def moved(k):
+        return (median(per[k]["FETCH_SIZE"]) * FETCH_SCALE + median(per[k]["WRITE_SIZE"]) * WRITE_SCALE) * 1024
+
+    kern = [k for k in per if "FETCH_SIZE" in per[k] and "WRITE_SIZE" in per[k]]
+    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{label}_{c} -o run "
+            f"-- python3 bench.py {bench_args}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    lines = [f"# HBM traffic per launch: {label}", "", "Commands (one counter per run, from the repository root;"
+             " TMPDIR=/tmp), then `python3 bench.py --traffic-summary` on the two counter files:", "", "```",
+             *cmds, "```", "",
+             f"Scale factors (256 MiB device copy): FETCH x {FETCH_SCALE:.4f}, WRITE x {WRITE_SCALE:.4f}. "
+             f"Kernel sources: hash {kernel_source_hash()}.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes moved (MB) |", "|---|---|---|---|---|"]
+    for k in sorted(kern, key=lambda k: -moved(k)):
+        if "dsa::" not in k:
+            continue
+        lines.append(f"| `{k}` | {len(per[k]['FETCH_SIZE'])} | {median(per[k]['FETCH_SIZE']):.1f} | "
+                     f"{median(per[k]['WRITE_SIZE']):.1f} | {moved(k) / 1e6:.2f} |")
+    lines.append("")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    for group, names in KERNEL_GROUPS.items():
+        ks = [k for k in kern if any(f"dsa::{n}<" in k or f"dsa::{n}(" in k for n in names)]
+        if not ks:
+            continue
+        nbytes = sum(moved(k) for k in ks)
+        rec = {"kernel": group, "workload": label, "source_hash": kernel_source_hash(), "bytes_per_launch": nbytes,
+               "launches": ks, "fetch_kib": sum(median(per[k]["FETCH_SIZE"]) for k in ks),
+               "write_kib": sum(median(per[k]["WRITE_SIZE"]) for k in ks), "fetch_scale": FETCH_SCALE,
+               "write_scale": WRITE_SCALE, "commands": cmds}
+        with open(os.path.join(out_dir, f"traffic_{group}_{label}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        lines.append(f"- `{group}` = {' + '.join(f'`{k}`' for k in ks)}: {nbytes / 1e6:.2f} MB per call.")
+    return "\n".join(lines) + "\n"
 
 
 def calibrate_copy(mb: int, reps: int):
@@ -583,7 +649,15 @@ def main():
                     help="only run a plain MB-sized device copy (counter calibration)")
     ap.add_argument("--prolog-only", action="store_true",
                     help="only measure the two cache appends on one stream against two streams")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("LABEL", "FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 counter files (FETCH_SIZE, WRITE_SIZE) of a run of "
+                         "this script into profiles/traffic_<stage>_LABEL.json and print a summary")
+    ap.add_argument("--traffic-bench-args", default="",
+                    help="the bench.py arguments of the profiled run (recorded with the summary)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        print(traffic_summary(*args.traffic_summary, args.traffic_bench_args), end="")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",

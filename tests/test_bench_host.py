@@ -1,5 +1,6 @@
 """Host logic of bench.py (no GPU): the algorithmic byte and flop counts the
 roofline divides by, checked against hand counts on tiny cases."""
+import json
 import os
 import sys
 
@@ -52,3 +53,36 @@ def test_grid_names_every_scope_workload():
     speculative-verify and chunked-prefill workloads."""
     assert {"decode_32k_b8", "decode_32k_b32", "decode_32k_b64", "decode_32k_b128", "batched_fp8_narrow",
             "batched_fp8_wide", "spec_verify", "chunked_prefill"} <= set(bench.GRID)
+
+
+def test_traffic_summary_sums_the_kernels_of_a_call(tmp_path):
+    """Per-call HBM bytes: the median per dispatch of each kernel of the stage,
+    summed, scaled by the copy factors; other kernels are left out."""
+    rows = {
+        "FETCH_SIZE": [("void dsa::sfa_bf16<1, false>(dsa::SfaParams)", [100.0, 300.0, 200.0]),
+                       ("void dsa::sfa_combine<true, 4>(dsa::SfaParams)", [50.0, 50.0]),
+                       ("void dsa::li_fused<1, 128, 0>(dsa::FusedParams)", [10.0]),
+                       ("void at::native::copy_kernel(int)", [9999.0])],
+        "WRITE_SIZE": [("void dsa::sfa_bf16<1, false>(dsa::SfaParams)", [8.0, 8.0, 8.0]),
+                       ("void dsa::sfa_combine<true, 4>(dsa::SfaParams)", [1.0, 3.0]),
+                       ("void dsa::li_fused<1, 128, 0>(dsa::FusedParams)", [2.0]),
+                       ("void at::native::copy_kernel(int)", [9999.0])],
+    }
+    paths = {}
+    for ctr, kernels in rows.items():
+        p = tmp_path / f"{ctr}.csv"
+        with open(p, "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for name, vals in kernels:
+                for i, v in enumerate(vals):
+                    f.write(f'{i},"{name}",{ctr},{v}\n')
+        paths[ctr] = str(p)
+    out = bench.traffic_summary("w", paths["FETCH_SIZE"], paths["WRITE_SIZE"], "--no-cpu", str(tmp_path))
+    sfa = json.load(open(tmp_path / "traffic_sparse_attn_w.json"))
+    want = ((200.0 + 50.0) * bench.FETCH_SCALE + (8.0 + 2.0) * bench.WRITE_SCALE) * 1024
+    assert abs(sfa["bytes_per_launch"] - want) < 1e-6
+    assert sfa["source_hash"] == bench.kernel_source_hash()
+    idx = json.load(open(tmp_path / "traffic_indexer_topk_w.json"))
+    assert abs(idx["bytes_per_launch"] - (10.0 * bench.FETCH_SCALE + 2.0) * 1024) < 1e-6
+    assert not (tmp_path / "traffic_indexer_scores_w.json").exists()
+    assert "copy_kernel" not in out and "--pmc FETCH_SIZE" in out
