@@ -150,6 +150,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) __attribute__((amdgpu_waves_per_e
     const bool ok = pos <= first_pos + r0 + r;
     const uint32_t off = ok ? (uint32_t)(r * p.score_stride + pos) * 4u : 0x80000000u;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srs, (int)off, 0, 0);
+    asm volatile("" ::: "memory");  // (keeps the store out of the branch below)
     if (ok) atomicAdd(&hl[r * kHistBins + (score_key(sc) >> kLevelShift[0])], 1u);
   };
 
