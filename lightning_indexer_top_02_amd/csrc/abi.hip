@@ -131,7 +131,7 @@ SfaPlan plan_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int topk) {
   if (p.n_split > 1) {
     const size_t th = (size_t)pg->num_q_tokens * s->n_heads;
     p.part_o_off = 0;
-    p.part_lse_off = align_up((size_t)p.n_split * th * dsa::kVDim * 4);
+    p.part_lse_off = align_up((size_t)p.n_split * th * dsa::kVDim * 2);  // fp16 partial outputs
     p.total = p.part_lse_off + align_up((size_t)p.n_split * th * 4);
   }
   return p;
@@ -204,7 +204,7 @@ DsaSfaLaunch sfa_args(const dsa_paged_t* pg, const dsa_sfa_t* s, const int32_t* 
   a.n_split = plan.n_split;
   a.nw = plan.nw;
   a.rows_per_split = plan.rows_per_split;
-  a.part_o = plan.n_split > 1 ? reinterpret_cast<float*>(ws + plan.part_o_off) : nullptr;
+  a.part_o = plan.n_split > 1 ? reinterpret_cast<uint16_t*>(ws + plan.part_o_off) : nullptr;
   a.part_lse = plan.n_split > 1 ? reinterpret_cast<float*>(ws + plan.part_lse_off) : nullptr;
   return a;
 }

@@ -168,7 +168,7 @@ struct DsaSfaLaunch {
   int nw;  // 16-head tiles per bf16 workgroup (1..4, dividing n_heads / 16)
   // split-KV partials (used when n_split > 1)
   int n_split, rows_per_split;
-  float* part_o;       // [n_split][rows][H][512]
+  uint16_t* part_o;    // [n_split][rows][H][512] fp16 normalised partial outputs
   float* part_lse;     // [n_split][rows][H]
 };
 

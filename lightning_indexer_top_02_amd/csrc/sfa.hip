@@ -26,7 +26,8 @@
 // keeps each head's softmax state in one lane column, so the probabilities
 // feed the second product straight from the first's accumulators.  When the
 // index list is split over several workgroups (small batches), each writes a
-// normalised partial output and its log-sum-exp, and sfa_combine merges them.
+// normalised partial output (fp16) and its log-sum-exp, and sfa_combine merges
+// them.
 //
 // fp32 kernel (sfa_f32): VALU, one workgroup per (query row, head).
 #include <algorithm>
@@ -48,7 +49,7 @@ struct SfaParams {
   void* out;
   float* lse;
   int n_split, rows_per_split;
-  float* part_o;
+  uint16_t* part_o;  // fp16
   float* part_lse;
 };
 
@@ -66,6 +67,20 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // half) by gfx950's one-instruction conversion, v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
+// Split partials are stored as fp16 (nearest even): a normalised partial
+// output is a convex combination of value elements, so its magnitude stays
+// that of the values, and fp16's 11-bit significand keeps its rounding well
+// inside the output tolerance (bf16's 8 bits did not: two roundings reached
+// 2.4e-2 on integer-valued inputs), at half the bytes of fp32.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), f16x2_t));
+}
+__device__ __forceinline__ float4 unpack_f16x4(uint2 v) {
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, v.x), b = __builtin_bit_cast(f16x2_t, v.y);
+  return make_float4((float)a[0], (float)a[1], (float)b[0], (float)b[1]);
 }
 
 // LDS layout of one staged chunk of 32 rows: krow, a row-major copy of the
@@ -353,10 +368,11 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
     }
     if (p.lse && g == 0 && half == 0) p.lse[(int64_t)i * p.H + h] = lse_v;
   } else {
-    float* prow = p.part_o + (((int64_t)split * p.T + i) * p.H + h) * kVDim + d0;
+    uint16_t* prow = p.part_o + (((int64_t)split * p.T + i) * p.H + h) * kVDim + d0;
 #pragma unroll
     for (int et = 0; et < kHalfDims / 16; ++et)
-      *reinterpret_cast<f32x4*>(prow + et * 16) = o[et] * inv;
+      *reinterpret_cast<uint2*>(prow + et * 16) =
+          make_uint2(pack_f16x2(o[et][0] * inv, o[et][1] * inv), pack_f16x2(o[et][2] * inv, o[et][3] * inv));
     if (g == 0 && half == 0) p.part_lse[((int64_t)split * p.T + i) * p.H + h] = lse_v;
   }
 }
@@ -386,7 +402,7 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
   const bool ok = th < stride;
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* po = p.part_o + (ok ? th : 0) * kVDim + d0;
+  const uint16_t* po = p.part_o + (ok ? th : 0) * kVDim + d0;
   for (int s0 = 0; ok && s0 * G < p.n_split; s0 += kCombineBatch) {
     float l[kCombineBatch];
     float4 o[kCombineBatch];
@@ -394,7 +410,8 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
     for (int j = 0; j < kCombineBatch; ++j) {
       const int s = (s0 + j) * G + sg;
       l[j] = s < p.n_split ? p.part_lse[s * stride + th] : -INFINITY;
-      o[j] = s < p.n_split ? *reinterpret_cast<const float4*>(po + s * stride * kVDim) : make_float4(0.f, 0.f, 0.f, 0.f);
+      o[j] = s < p.n_split ? unpack_f16x4(*reinterpret_cast<const uint2*>(po + s * stride * kVDim))
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float bm = l[0];
 #pragma unroll
