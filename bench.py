@@ -281,7 +281,7 @@ def traffic_summary(label: str, fetch_csv: str, write_csv: str, bench_args: str,
         return (median(per[k]["FETCH_SIZE"]) * FETCH_SCALE + median(per[k]["WRITE_SIZE"]) * WRITE_SCALE) * 1024
 
     kern = [k for k in per if "FETCH_SIZE" in per[k] and "WRITE_SIZE" in per[k]]
-    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{label}_{c} -o run "
+    cmds = [f"timeout -s KILL 150 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{label}_{c} -o run "
             f"-- python3 bench.py {bench_args}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
     lines = [f"# HBM traffic per launch: {label}", "", "Commands (one counter per run, from the repository root;"
              " TMPDIR=/tmp), then `python3 bench.py --traffic-summary` on the two counter files:", "", "```",

@@ -386,10 +386,12 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
 // neighbouring lanes, lower lane first, so every lane of a group forms the
 // same result.  With G = 4 a merge of up to 64 splits is one memory round
 // trip (few rows, many splits); G = 1 keeps the grid small for large batches.
+// NB, the splits a thread reads at once, is the smallest of 2, 4, 8, 16 that
+// covers its share, so a two-split merge computes no exponentials for
+// absent splits (the sums are the same for any NB: an absent split adds 0).
 constexpr int kCombineThreads = 256;
-constexpr int kCombineBatch = 16;
 
-template <bool BF16, int G>
+template <bool BF16, int G, int NB>
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "lane groups within a quad");
   const int64_t gt = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
@@ -403,11 +405,11 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const uint16_t* po = p.part_o + (ok ? th : 0) * kVDim + d0;
-  for (int s0 = 0; ok && s0 * G < p.n_split; s0 += kCombineBatch) {
-    float l[kCombineBatch];
-    float4 o[kCombineBatch];
+  for (int s0 = 0; ok && s0 * G < p.n_split; s0 += NB) {
+    float l[NB];
+    float4 o[NB];
 #pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int s = (s0 + j) * G + sg;
       l[j] = s < p.n_split ? p.part_lse[s * stride + th] : -INFINITY;
       o[j] = s < p.n_split ? unpack_f16x4(*reinterpret_cast<const uint2*>(po + s * stride * kVDim))
@@ -415,14 +417,14 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
     }
     float bm = l[0];
 #pragma unroll
-    for (int j = 1; j < kCombineBatch; ++j) bm = fmaxf(bm, l[j]);
+    for (int j = 1; j < NB; ++j) bm = fmaxf(bm, l[j]);
     if (bm == -INFINITY) continue;  // no selected rows in these splits
     const float Mn = fmaxf(M, bm);
     const float r = expf(M - Mn);   // M = -inf gives 0 (acc and den are 0 then)
     den *= r;
     acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
 #pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const float wgt = l[j] == -INFINITY ? 0.f : expf(l[j] - Mn);
       den += wgt;
       acc.x += wgt * o[j].x; acc.y += wgt * o[j].y; acc.z += wgt * o[j].z; acc.w += wgt * o[j].w;
@@ -598,11 +600,18 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t groups = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
-  if (a.n_split >= 8)
-    hipLaunchKernelGGL((sfa_combine<true, 4>), dim3((unsigned)((4 * groups + kCombineThreads - 1) / kCombineThreads)),
-                       dim3(kCombineThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((sfa_combine<true, 1>), dim3((unsigned)((groups + kCombineThreads - 1) / kCombineThreads)),
-                       dim3(kCombineThreads), 0, s, p);
+  const int G = a.n_split >= 8 ? 4 : 1;
+  const int share = (a.n_split + G - 1) / G;  // splits per thread
+  const dim3 cgrid((unsigned)((G * groups + kCombineThreads - 1) / kCombineThreads));
+  if (G == 4) {
+    if (share <= 2) hipLaunchKernelGGL((sfa_combine<true, 4, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 4, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 8) hipLaunchKernelGGL((sfa_combine<true, 4, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((sfa_combine<true, 4, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
+  } else {
+    if (share <= 2) hipLaunchKernelGGL((sfa_combine<true, 1, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 1, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((sfa_combine<true, 1, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
