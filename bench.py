@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -226,11 +227,21 @@ class Step:
         dsa.indexer_scores(self.paged, self.indexers[s % self.R], self.scores, stream=stream)
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without its comments and blank-line or trailing-space
+    differences (the sources hold no string literal with // or /*)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter data taken on other sources is stale."""
+    """Hash of the HIP sources' code (comments left out): counter data taken
+    on other kernel code is stale."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "lightning_indexer_top_02_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
+        h.update(os.path.basename(f).encode() + b"\0")
+        h.update(strip_comments(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,22 +1,21 @@
 // indexer.hip -- lightning indexer, throughput path (gfx950): scores through
-// HBM, then one selection workgroup per query row.
+// HBM, then the segment-parallel selection of topk_seg.hip.
 //
 // Used when rows are too long (or too many per request) for the single fused
-// kernel (indexer_fused.hip).  Requests with many query rows (chunked prefill)
-// are scored by the row-tiled MFMA kernel of indexer_prefill.hip instead of
-// li_score; both write the same scores and histograms.  The scoring follows "Optimizing Inference for
-// Hybrid Attention Architectures: From Operator Fusion to Sequence Sharding",
-// section "Breaking Down the Computational Path of Hybrid Attention", item 1,
-// reading keys straight from the paged K cache ("Day0 Inference Support and
-// Performance Optimization for New LLM Architectures", section III, 3.1).
+// kernel (indexer_fused.hip).  Requests with many query rows (chunked
+// prefill) are scored by the row-tiled MFMA kernel of indexer_prefill.hip
+// instead of li_score; both write the same scores and histograms.  The
+// scoring follows "Optimizing Inference for Hybrid Attention Architectures:
+// From Operator Fusion to Sequence Sharding", section "Breaking Down the
+// Computational Path of Hybrid Attention", item 1, reading keys straight from
+// the paged K cache ("Day0 Inference Support and Performance Optimization for
+// New LLM Architectures", section III, 3.1).
 //
 // li_score: one workgroup = 4 waves, stepping 4 cache pages (256 positions)
 // at a time through its share of all requests' chunks, for up to 4 query rows
 // of the request at hand (the rows share one read of the keys).
 // It writes fp32 scores and a per-row histogram of the top 11 key bits (LDS,
 // then one global atomic per non-empty bin): the first radix level.
-//
-// Selection runs over segments of each row (topk_seg.hip).
 #include <algorithm>
 #include <type_traits>
 
