@@ -284,6 +284,21 @@ def test_batched_fp8_wide_full_exact():
     _full(case, sorted({int(lens.argmax()), int(lens.argmin())} | set(_seeded_rows(64, 6, 12))), routes=False)
 
 
+def test_position_tiled_many_chunks_per_workgroup():
+    """160 single-row requests at 262144 positions with a narrow fp8 indexer
+    (4 x 64): 163840 chunks of 256 positions over 512 scoring workgroups,
+    320 each, so every workgroup stages the block-table entries of its
+    chunks in two windows (256, then 64) and restarts its tile ring between
+    them; the rows at both ends of the batch against the oracle."""
+    case = inputs.make_case(name="many_chunks_fp8_4x64", seed=97, ctx_lens=[262144] * 160, idx_dtype="fp8",
+                            n_heads_idx=4, head_dim_idx=64, topk=2048, sfa_dtype=None, device="cuda")
+    print(f"\n[case] {case.name} seed={case.seed} B={case.batch} T={case.num_tokens} "
+          f"max_ctx={case.max_ctx} K={case.topk}", flush=True)
+    idx = parity.gpu_indexer_topk(case)
+    stats = parity.check_rows(case, idx, None, [0, 1, 63, 64, 158, 159])
+    print(f"[ok] {case.name}: {stats}", flush=True)
+
+
 # --- batched decode through the single-kernel indexer ---------------------------
 # Many 256-position chunks per workgroup switch the fused kernel to its
 # throughput modes (block-table entries in LDS, three key tiles in flight,
