@@ -100,7 +100,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   const bool row_ok = wave < nrows;
   const int row = q0 + r0 + wave;                 // this wave's query row
   const int vis_last = first_pos + r0 + nrows;    // positions any row here sees
-  const int myvis = row_ok ? first_pos + r0 + wave + 1 : 0;
+  // positions this wave's row sees (wave-uniform: the causal skip below is a
+  // scalar branch, not a divergent one)
+  const int myvis = __builtin_amdgcn_readfirstlane(row_ok ? first_pos + r0 + wave + 1 : 0);
 
   for (int c = tid; c < kPfRows * kHistBins; c += kPfThreads) lhist[c] = 0u;
 
@@ -141,19 +143,34 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   const unsigned char* kg = static_cast<const unsigned char*>(p.k);
   constexpr int PPR = D * ES / 16;       // 16-byte pieces per key row
   constexpr int PAGES = kPfTile / kPage;  // pages per tile
-  // Physical pages of a tile (-1 past the last page any row here sees: those
-  // pieces are zero-filled).  They are loaded one tile ahead of the keys, so
-  // the key loads never wait on a block-table read.
+  // Block-table entries of a tile's pages, read one tile ahead of the keys so
+  // that the key loads never wait on them.  Pages past the last one any row
+  // here sees read the last page's entry (every read is issued) and are
+  // zero-filled by fetch.
+  const int last_pg = (vis_last - 1) / kPage;
+  // (read through the constant address space: scalar loads, which leave the
+  // vector memory counter to the key loads and score stores)
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr btc = (const_i32_ptr)btrow;
   auto load_phys = [&](int tile, int (&ph)[PAGES]) {
 #pragma unroll
-    for (int i = 0; i < PAGES; ++i) {
-      const int pg = tile * PAGES + i;
-      ph[i] = pg * kPage < vis_last ? btrow[pg] : -1;
-    }
+    for (int i = 0; i < PAGES; ++i) ph[i] = btc[min(tile * PAGES + i, last_pg)];
   };
+  // Every vector memory operation of the tile loop is issued unconditionally
+  // (gfx950 counts loads and stores on one in-order counter, and a
+  // conditional one makes each wait for a tile's keys a wait for every
+  // outstanding store): keys and scales are buffer loads from a resource over
+  // one page, and a page past the rows' last position gets an offset beyond
+  // the resource, which reads zeros without touching memory.
+  constexpr uint32_t kPageBytes = kPage * D * ES;
+  constexpr uint32_t kOff = 0x80000000u;  // out of every resource's range
   uint4 pre[VPT];
   float pre_s = 0.f;
-  auto fetch = [&](const int (&ph)[PAGES]) {
+  // the keys of tile `tile`, whose block-table entries are ph
+  auto fetch = [&](int tile, const int (&ph_raw)[PAGES]) {
+    int ph[PAGES];
+#pragma unroll
+    for (int i = 0; i < PAGES; ++i) ph[i] = tile * PAGES + i <= last_pg ? ph_raw[i] : -1;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int c = tid + j * kPfThreads;  // 16-byte piece of the tile
@@ -162,19 +179,25 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
       int phys = ph[0];
 #pragma unroll
       for (int i = 1; i < PAGES; ++i) phys = (pos >> 6) == i ? ph[i] : phys;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (phys >= 0)
-        v = *reinterpret_cast<const uint4*>(kg + ((int64_t)phys * kPage + (pos & 63)) * (D * ES) + part * 16);
-      pre[j] = v;
+      // a wave's 1 KB of pieces lies in one page, so phys is wave-uniform
+      phys = __builtin_amdgcn_readfirstlane(phys);
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(kg) + (phys >= 0 ? (int64_t)phys * kPageBytes : 0), 0, kPageBytes, 0x00020000);
+      const uint32_t off = phys >= 0 ? (uint32_t)((pos & 63) * (D * ES) + part * 16) : kOff;
+      pre[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
     }
-    if (DT >= 2 && tid < kPfTile) {
+    if constexpr (DT >= 2) {
+      // threads below kPfTile load the scale of tile position tid (fp8: one
+      // fp32, MXFP8: the four E8M0 bytes of the position)
       int phys = ph[0];
 #pragma unroll
       for (int i = 1; i < PAGES; ++i) phys = (tid >> 6) == i ? ph[i] : phys;
-      const int64_t slot = (int64_t)phys * kPage + (tid & 63);
-      if (phys < 0) pre_s = 0.f;
-      else if (DT == 2) pre_s = static_cast<const float*>(p.k_scale)[slot];
-      else pre_s = __uint_as_float(static_cast<const uint32_t*>(p.k_scale)[slot]);  // 4 E8M0 bytes
+      phys = __builtin_amdgcn_readfirstlane(phys);
+      const auto rsc = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<unsigned char*>(const_cast<void*>(p.k_scale)) + (phys >= 0 ? (int64_t)phys * kPage * 4 : 0), 0,
+          kPage * 4, 0x00020000);
+      const uint32_t off = (phys >= 0 && tid < kPfTile) ? (uint32_t)(tid & 63) * 4u : kOff;
+      pre_s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, (int)off, 0, 0));
     }
   };
   auto stage = [&](int buf) {
@@ -253,11 +276,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
     if (DT == 2) s *= kscale;
     return s;
   };
-  auto emit = [&](float s, int pos) {
-    if (g < 2 && pos < myvis) {
-      p.scores[(int64_t)row * p.score_stride + pos] = s;
-      atomicAdd(&lhist[wave * kHistBins + (score_key(s) >> kLevelShift[0])], 1u);
-    }
+  // This wave's score row as a buffer of myvis positions: lanes g < 2 store
+  // the score of sub-tile position base + 16 (g & 1) + l16 (base < 0: none);
+  // the other lanes, and positions the row does not see, get offsets past the
+  // buffer, which the hardware drops.
+  const int srow_row = __builtin_amdgcn_readfirstlane(row_ok ? row : 0);  // (wave-uniform)
+  const auto srow = __builtin_amdgcn_make_buffer_rsrc(p.scores + (int64_t)srow_row * p.score_stride, 0, myvis * 4,
+                                                      0x00020000);
+  // (sub: which store of the tile, so that dropped stores get distinct
+  // offsets and are not merged into one)
+  auto store = [&](float s, int base, int sub) {
+    const int pos = base + (g & 1) * 16 + l16;
+    const bool on = g < 2 && base >= 0;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), srow,
+                                          (int)(on ? (uint32_t)pos * 4u : kOff + 4u * (uint32_t)sub), 0, 0);
+  };
+  auto count = [&](float s, int base) {
+    const int pos = base + (g & 1) * 16 + l16;
+    if (g < 2 && base >= 0 && pos < myvis) atomicAdd(&lhist[wave * kHistBins + (score_key(s) >> kLevelShift[0])], 1u);
   };
 
 #pragma unroll
@@ -267,50 +303,66 @@ __global__ __launch_bounds__(kPfThreads, 1) void li_prefill(PrefillParams p) {
   int pending = -1;  // first position of the sub-tile waiting in acc[1], or -1
 
   int ph_next[PAGES];
-  load_phys(0, ph_next);
-  if (ntiles > 0) {
-    fetch(ph_next);
-    stage(0);
-  }
+  load_phys(0, ph_next);  // (ntiles >= 1: every workgroup has a row)
+  fetch(0, ph_next);
+  stage(0);
   load_phys(1, ph_next);
-  if (ntiles > 1) {
-    fetch(ph_next);
-    load_phys(2, ph_next);
-  }
+  fetch(1, ph_next);  // (past the last tile: zeros)
+  load_phys(2, ph_next);
+  // dropped stores in place of a tile's score stores: the memory operations
+  // before the loop then end as each pass through it ends, and the counts the
+  // compiler derives for the loop's waits hold on the first pass too (else
+  // the block-table reads just above make every tile wait for everything)
+  __builtin_amdgcn_sched_barrier(0);  // (kept after the reads above)
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) store(0.f, -1, sub);
   for (int tile = 0; tile < ntiles; ++tile) {
     __syncthreads();  // tile is staged; the other buffer (tile - 1) is no longer read
     ktile = kbuf + (tile & 1) * kPfTile * KROW;
     ksc = kscb + (tile & 1) * kPfTile;
-    // tile + 1 goes into the other buffer after this tile's first sub-tile
-    // (its loads have had a whole tile to arrive), and tile + 2's loads start
-    auto next_tile = [&]() {
-      if (tile + 1 < ntiles) {
-        stage((tile + 1) & 1);
-        if (tile + 2 < ntiles) {
-          fetch(ph_next);
-          load_phys(tile + 3, ph_next);
-        }
-      }
-    };
-    if (tile * kPfTile >= myvis) {  // (also every wave without a row)
-      next_tile();
-      continue;
-    }
-    frag_t bf[2];
-    load_b(bf, 0, 0);
+    // tile + 1 goes into the other buffer (its loads have had a whole tile to
+    // arrive), and tile + 2's loads start; past the last tile they are zeros,
+    // staged into a buffer nobody reads.  This comes before the causal skip,
+    // so both paths hold the tiles in the same registers and issue the same
+    // memory operations (else every wait for a tile waits for all stores too).
+    stage((tile + 1) & 1);
+    fetch(tile + 2, ph_next);
+    load_phys(tile + 3, ph_next);
+    // A tile's four sub-tile scores are stored after the tile, from one
+    // place for the scored and the skipped tiles (whose stores are dropped),
+    // so every path through the loop issues the same memory operations in the
+    // same order.
+    float s_out[NSUB];
+    int b_out[NSUB];
+    if (tile * kPfTile < myvis) {  // (never for a wave without a row)
+      frag_t bf[2];
+      load_b(bf, 0, 0);
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int cur = sub & 1;
-      // the previous sub-tile (the last one of the previous tile when sub == 0)
-      const int prev_pos = sub == 0 ? pending : tile * kPfTile + (sub - 1) * kPfSub;
-      mfma_sub(acc[cur], sc_k[cur], sub, bf);
-      if (sub == 0) next_tile();  // (before this sub-tile's score stores, which it would wait for)
-      const float s = epilogue(acc[cur ^ 1], sc_k[cur ^ 1]);
-      if (prev_pos >= 0) emit(s, prev_pos + (g & 1) * 16 + l16);
+      for (int sub = 0; sub < NSUB; ++sub) {
+        const int cur = sub & 1;
+        // the previous sub-tile (the last one of the previous tile when sub == 0)
+        b_out[sub] = sub == 0 ? pending : tile * kPfTile + (sub - 1) * kPfSub;
+        mfma_sub(acc[cur], sc_k[cur], sub, bf);
+        s_out[sub] = epilogue(acc[cur ^ 1], sc_k[cur ^ 1]);
+        count(s_out[sub], b_out[sub]);
+      }
+      pending = tile * kPfTile + (NSUB - 1) * kPfSub;
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        s_out[sub] = 0.f;
+        b_out[sub] = -1;
+      }
     }
-    pending = tile * kPfTile + (NSUB - 1) * kPfSub;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) store(s_out[sub], b_out[sub], sub);
   }
-  if (pending >= 0) emit(epilogue(acc[1], sc_k[1]), pending + (g & 1) * 16 + l16);
+  {
+    const float sl = epilogue(acc[1], sc_k[1]);
+    store(sl, pending, 0);
+    count(sl, pending);
+  }
 
   __syncthreads();
   if (!p.hist) return;
