@@ -14,17 +14,18 @@
 // its row's whole query (64 heads x D) in registers as the MFMA A operand and
 // walks the request's positions in tiles of 128, which the eight waves share
 // through two LDS buffers: while tile t is used, tile t + 1 is written into
-// the other buffer (after t's first sub-tile; one barrier per tile), tile
-// t + 2's keys are in flight in registers and their block-table entries one
-// tile further ahead.
+// the other buffer (right after the tile's barrier, one barrier per tile),
+// tile t + 2's keys are in flight in registers and their block-table entries
+// one tile further ahead.
 //
 // Within a tile a wave takes 32 positions at a time: 64 heads x 32 positions
 // x D as MFMAs (one 16x16x128 step for 128-dim fp8, else 16x16x32 steps)
 // into 4 x 2 accumulator tiles, with the key fragments
 // of each contraction step read from LDS one step ahead.  The epilogue of a
-// sub-tile (ReLU, weights, the 64-head sum, the store) is issued together
-// with the MFMAs of the next one, on a second accumulator set, so the vector
-// ALU work overlaps the matrix cores instead of following them.  In the
+// sub-tile (ReLU, weights, the 64-head sum) is issued together with the
+// MFMAs of the next one, on a second accumulator set, so the vector ALU work
+// overlaps the matrix cores instead of following them; a tile's four score
+// stores follow the tile.  In the
 // accumulators the heads of a position sit in one lane column: lane group g
 // (lanes 16g .. 16g + 15) holds heads 16t + 4g + i, summed in-lane in
 // ascending head order; the four group sums are combined as
