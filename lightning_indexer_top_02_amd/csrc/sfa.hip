@@ -385,7 +385,8 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
 // when the maximum grows); the G partial merges are then combined across
 // neighbouring lanes, lower lane first, so every lane of a group forms the
 // same result.  With G = 4 a merge of up to 64 splits is one memory round
-// trip (few rows, many splits); G = 1 keeps the grid small for large batches.
+// trip (few rows, many splits); G = 1 keeps the grid small for large batches,
+// and G = 2 sits between (8 to 31 splits).
 // NB, the splits a thread reads at once, is the smallest of 2, 4, 8, 16 that
 // covers its share, so a two-split merge computes no exponentials for
 // absent splits (the sums are the same for any NB: an absent split adds 0).
@@ -600,7 +601,9 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t groups = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
-  const int G = a.n_split >= 8 ? 4 : 1;
+  // lanes per (row, head, 4 dims): 4 for 32 splits and more, 2 for 8 to 31
+  // (a batch-8 decode has 16: 26.2 us against 28.0 with 4), 1 below
+  const int G = a.n_split >= 32 ? 4 : (a.n_split >= 8 ? 2 : 1);
   const int share = (a.n_split + G - 1) / G;  // splits per thread
   const dim3 cgrid((unsigned)((G * groups + kCombineThreads - 1) / kCombineThreads));
   if (G == 4) {
@@ -608,6 +611,10 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
     else if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 4, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
     else if (share <= 8) hipLaunchKernelGGL((sfa_combine<true, 4, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
     else hipLaunchKernelGGL((sfa_combine<true, 4, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
+  } else if (G == 2) {
+    if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 2, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 8) hipLaunchKernelGGL((sfa_combine<true, 2, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((sfa_combine<true, 2, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
   } else {
     if (share <= 2) hipLaunchKernelGGL((sfa_combine<true, 1, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
     else if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 1, 4>), cgrid, dim3(kCombineThreads), 0, s, p);

@@ -484,4 +484,12 @@ def test_graph_replays_match_eager(flags):
         torch.cuda.synchronize()
         assert torch.equal(ii, ref[0]), f"eager call after replay {rep} differs"
     ctrl = ws[: 4 * case.batch].view(torch.int32)
-    assert int(ctrl.abs().sum()) == 0, "arrival counters not back to zero"
+    assert int(ctrl.abs().sum()) == 0, "arrival counters not back to zero"@pytest.mark.gpu
+def test_decode_32k_batch8_full():
+    """The 32K decode at batch 8: 16 attention splits per row, merged by two
+    lanes per (row, head, 4 dims); three rows against the oracle."""
+    case = inputs.decode_32k(batch=8, device="cuda", name="decode_32k_b8")
+    _full(case, [0, 3, 7], routes=False)
+
+
+
