@@ -53,7 +53,7 @@ dsa_status_t check_indexer(const dsa_paged_t* pg, const dsa_indexer_t* x) {
     if (x->head_dim != 128) return DSA_ERR_UNSUPPORTED;  // one 16x16x128 step
   }
   if (x->dtype == DSA_F32 && x->n_heads * x->head_dim > 4096) return DSA_ERR_UNSUPPORTED;
-  if ((int64_t)pg->max_ctx_len > (int64_t)dsa_seg_max_segments() * 8192) return DSA_ERR_UNSUPPORTED;
+  if ((int64_t)pg->max_ctx_len > (int64_t)dsa_seg_max_segments() * dsa_seg_length()) return DSA_ERR_UNSUPPORTED;
   if (x->dtype == DSA_F32 && (x->flags & DSA_INDEXER_SCORE_ROWS)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }

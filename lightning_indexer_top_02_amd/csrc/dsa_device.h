@@ -207,6 +207,7 @@ hipError_t dsa_launch_indexer_scores(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_indexer_prefill_scores(const DsaIndexerLaunch& a, hipStream_t s);
 hipError_t dsa_launch_topk_segments(const DsaIndexerLaunch& a, hipStream_t s);
 int dsa_seg_max_segments();
+int dsa_seg_length();  // positions per selection segment
 int dsa_seg_cand_cap(int max_ctx_len);
 int64_t dsa_seg_keep_words(int64_t score_stride);  // kept-position bitmap words per row
 bool dsa_indexer_rows_route(const DsaIndexerLaunch& a);

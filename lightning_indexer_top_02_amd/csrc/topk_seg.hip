@@ -26,10 +26,11 @@
 //   li_seg_write   (a workgroup per segment): writes the kept positions of
 //                  its segment at its offset, in order, from the bitmap, so
 //                  the scores are read only once.
-// Thread t of a segment reads positions s0 + 1024 c + 4 t + e (c < 8,
-// e < 4): each wave load is 1 KB of consecutive scores, with no staging
-// buffer.  Bit 4 c + e of the segment's bitmap word t marks that position;
-// li_seg_write regathers the bits of 32 consecutive positions per thread.
+// Thread t of a segment reads positions s0 + R c + 4 t + e (c < 8, e < 4,
+// R = 4 x the segment's threads): each wave load is 1 KB of consecutive
+// scores, with no staging buffer.  Bit 4 c + e of the segment's bitmap word t
+// marks that position; li_seg_write regathers the bits of 32 consecutive
+// positions per thread.
 // A row whose boundary bin holds more keys than the candidate list can take
 // (heavy ties) is flagged and selected whole by li_seg_resolve's workgroup
 // (select_whole_row), and li_seg_write leaves it alone.  The per-row state
@@ -43,8 +44,8 @@
 namespace dsa {
 
 constexpr int kSegLen = 8192;                     // positions per segment
-constexpr int kSegThreads = 256;
-constexpr int kSegPer = kSegLen / kSegThreads;    // positions per thread
+constexpr int kSegThreads = kSegLen / 32;         // one bitmap word of 32 positions per thread
+constexpr int kSegRound = 4 * kSegThreads;        // positions of one 16-byte load per thread
 constexpr int kResolveThreads = 1024;
 // words of a row's histogram block (kHistStride) after the level-1 bins
 constexpr int kSegBase = kHistBins;               // per-segment counts, then offsets
@@ -77,8 +78,8 @@ __host__ __device__ constexpr int64_t keep_words(int64_t score_stride) {
 // Word and bit of position pos in its row's bitmap.
 __device__ __forceinline__ void keep_bit(int pos, int& word, int& bit) {
   const int seg = pos / kSegLen, o = pos - seg * kSegLen;
-  word = seg * (kSegLen / 32) + ((o & 1023) >> 2);
-  bit = 4 * (o >> 10) + (o & 3);
+  word = seg * (kSegLen / 32) + ((o % kSegRound) >> 2);
+  bit = 4 * (o / kSegRound) + (o & 3);
 }
 
 __device__ __forceinline__ int visible_of(const SegParams& p, int i) {
@@ -95,7 +96,7 @@ __device__ __forceinline__ int block_sum(int v, int* wsum) {
   return total;
 }
 
-static_assert(kSegThreads * 32 == kSegLen, "one bitmap word of 32 positions per thread");
+static_assert(kSegThreads * 32 == kSegLen && kSegThreads % 64 == 0, "whole waves, a bitmap word per thread");
 
 __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   __shared__ __align__(16) int wsum[kSegThreads / 64];
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
   auto load_scores = [&]() {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int t = s0 + 1024 * c + 4 * tid;
+      const int t = s0 + kSegRound * c + 4 * tid;
       v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (t + 4 <= vis) {
         v[c] = *reinterpret_cast<const float4*>(row + t);
@@ -144,13 +145,13 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
     const float x = (b & 3) == 0 ? q.x : ((b & 3) == 1 ? q.y : ((b & 3) == 2 ? q.z : q.w));
     return score_key(x);
   };
-  // bit 4c + e of gtm / eqm: position s0 + 1024 c + 4 tid + e is visible and
+  // bit 4c + e of gtm / eqm: position s0 + kSegRound c + 4 tid + e is visible and
   // lies above / in the boundary bin
   const int lim = vis - s0 - 4 * tid;
   uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
   for (int b = 0; b < 32; ++b) {
-    const bool ok = 1024 * (b >> 2) + (b & 3) < lim;
+    const bool ok = kSegRound * (b >> 2) + (b & 3) < lim;
     const uint32_t d = key_of(b) >> kLevelShift[0];
     gtm |= ok && d > bin1 ? 1u << b : 0u;
     eqm |= ok && d == bin1 ? 1u << b : 0u;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_gather(SegParams p) {
     if ((eqm >> b) & 1u) {
       if (o < p.cand_cap) {
         ck[o] = key_of(b) & 0x1fffffu;
-        cp[o] = s0 + 1024 * (b >> 2) + 4 * tid + (b & 3);
+        cp[o] = s0 + kSegRound * (b >> 2) + 4 * tid + (b & 3);
       }
       ++o;
     }
@@ -507,16 +508,16 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
   // the kept positions are the set bits of the row's bitmap (the keys
   // above the boundary bin, from li_seg_gather, and the kept candidates,
   // from li_seg_resolve); thread t takes positions s0 + 32 t .. + 31, whose
-  // bits are bits 4c .. 4c + 3 (c = t / 32) of the segment's words
-  // 8 (t % 32) .. + 7
+  // bits are bits 4c .. 4c + 3 (c = t / (kSegRound / 32)) of the segment's
+  // words 8 (t % (kSegRound / 32)) .. + 7
   const int pos0 = s0 + tid * 32;
   uint32_t sel = 0u;
   if (pos0 < vis) {
     const uint4* w4 = reinterpret_cast<const uint4*>(p.keep + i * keep_words(p.score_stride) + seg * (kSegLen / 32) +
-                                                     8 * (tid & 31));
+                                                     8 * (tid % (kSegRound / 32)));
     const uint4 a = w4[0], b = w4[1];
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    const int c4 = 4 * (tid >> 5);
+    const int c4 = 4 * (tid / (kSegRound / 32));
 #pragma unroll
     for (int m = 0; m < 8; ++m) sel |= ((w[m] >> c4) & 0xfu) << (4 * m);
   }
@@ -537,6 +538,7 @@ __global__ __launch_bounds__(kSegThreads) void li_seg_write(SegParams p) {
 using namespace dsa;
 
 int dsa_seg_max_segments() { return kMaxSegs; }
+int dsa_seg_length() { return kSegLen; }
 int dsa_seg_cand_cap(int max_ctx_len) { return std::min((max_ctx_len + 255) / 256 * 256, 8192); }
 int64_t dsa_seg_keep_words(int64_t score_stride) { return keep_words(score_stride); }
 
