@@ -33,6 +33,7 @@
  *   on a bad argument the call returns a non-zero dsa_status_t and enqueues
  *   nothing.  Device data (page ids, lengths) is trusted: a page id outside
  *   [0, num_pages) or a ctx_len above max_ctx_len is undefined behaviour.
+ *   dsa_validate_paged checks that data on the device, on request.
  * Layouts (row-major, contiguous):
  *   paged pools      [num_pages][page_size][dim]        page_size = 64
  *   block_table      [batch][max_pages_per_req] int32   physical page ids
@@ -288,6 +289,32 @@ dsa_status_t dsa_fused_decode(const dsa_paged_t *paged, const dsa_indexer_t *idx
 #define DSA_STATIC_SCRATCH_BYTES (64u << 20)
 dsa_status_t dsa_fused_decode_static(const dsa_paged_t *paged, const dsa_indexer_t *idx,
                                      const dsa_sfa_t *sfa, int32_t *topk_idx, void *stream);
+
+/* Device-side check of the paging data every other call trusts (the block
+ * table maps position t of request b to page block_table[b][t / 64], slot
+ * t % 64: "Optimizing Inference for Hybrid Attention LLMs: Practices for Fast
+ * Adaptation", section 3.2; "Day0 Inference Support and Performance
+ * Optimization for New LLM Architectures", section III, 3.2).  One kernel
+ * enqueued on `stream` reads q_offsets, ctx_lens and the used entries of
+ * block_table (pages 0 .. ceil(ctx_len / 64) - 1 of each request, never past
+ * max_pages_per_req) and stores into *error_word (device, 4-byte aligned,
+ * overwritten: it needs no clearing) the OR of:
+ *   DSA_VALID_Q_OFFSETS  q_offsets[0] != 0, q_offsets[batch] != num_q_tokens,
+ *                        or q_offsets decreasing
+ *   DSA_VALID_ROWS       a request with more than max_q_per_req rows
+ *   DSA_VALID_CTX_LEN    ctx_len below the request's rows or above max_ctx_len
+ *   DSA_VALID_PAGE_COUNT ceil(ctx_len / 64) above max_pages_per_req
+ *   DSA_VALID_PAGE_ID    a used block-table entry outside [0, num_pages)
+ * 0 means the data meets the contract of the other calls.  Reads nothing else
+ * (no cache, query or index array), so it is safe on any data.  Needs no
+ * workspace.  INVALID_ARG for invalid paged arguments or a NULL or misaligned
+ * error_word. */
+#define DSA_VALID_Q_OFFSETS 1u
+#define DSA_VALID_ROWS 2u
+#define DSA_VALID_CTX_LEN 4u
+#define DSA_VALID_PAGE_COUNT 8u
+#define DSA_VALID_PAGE_ID 16u
+dsa_status_t dsa_validate_paged(const dsa_paged_t *paged, uint32_t *error_word, void *stream);
 
 /* Zero-fill a workspace (enqueued on `stream`).  ws_bytes % 4 == 0. */
 dsa_status_t dsa_workspace_init(void *ws, size_t ws_bytes, void *stream);

@@ -322,6 +322,17 @@ dsa_status_t dsa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
+dsa_status_t dsa_validate_paged(const dsa_paged_t* pg, uint32_t* error_word, void* stream) {
+  if (!valid_paged(pg) || !error_word || (reinterpret_cast<uintptr_t>(error_word) & 3)) return DSA_ERR_INVALID_ARG;
+  dsa_status_t st = check_device();
+  if (st != DSA_OK) return st;
+  return dsa_launch_validate(pg->q_offsets, pg->ctx_lens, pg->block_table, pg->batch, pg->num_q_tokens,
+                             pg->max_q_per_req, pg->max_ctx_len, pg->max_pages_per_req, pg->num_pages,
+                             error_word, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DSA_OK
+             : DSA_ERR_LAUNCH;
+}
+
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
 const char* dsa_status_string(dsa_status_t s) {

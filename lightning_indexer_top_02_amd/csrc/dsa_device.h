@@ -13,6 +13,14 @@ constexpr int kVDim = 512;
 constexpr int kHistBins = 2048;    // bins of the widest radix digit (11 bits)
 constexpr int kHistStride = 3 * kHistBins;  // per-row digit histograms in the workspace
 
+// Flag bits of dsa_validate_paged (the same values as the DSA_VALID_* macros
+// of the public header).
+constexpr uint32_t kValidQOffsets = 1u;   // q_offsets[0] != 0, a decrease, or q_offsets[batch] != T
+constexpr uint32_t kValidRows = 2u;       // a request with more than max_q_per_req rows
+constexpr uint32_t kValidCtxLen = 4u;     // ctx_len below its rows or above max_ctx_len
+constexpr uint32_t kValidPageCount = 8u;  // more pages than max_pages_per_req
+constexpr uint32_t kValidPageId = 16u;    // a used block-table entry outside [0, num_pages)
+
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
@@ -212,3 +220,6 @@ int dsa_seg_cand_cap(int max_ctx_len);
 int64_t dsa_seg_keep_words(int64_t score_stride);  // kept-position bitmap words per row
 bool dsa_indexer_rows_route(const DsaIndexerLaunch& a);
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s);
+hipError_t dsa_launch_validate(const int32_t* q_offsets, const int32_t* ctx_lens, const int32_t* block_table,
+                               int batch, int num_q_tokens, int max_q_per_req, int max_ctx_len,
+                               int max_pages_per_req, int num_pages, uint32_t* error_word, hipStream_t s);

@@ -144,6 +144,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_fused_decode_static.argtypes = [PP, PI, PS, P, P]
         lib.dsa_workspace_init.restype = ctypes.c_int
         lib.dsa_workspace_init.argtypes = [P, S, P]
+        lib.dsa_validate_paged.restype = ctypes.c_int
+        lib.dsa_validate_paged.argtypes = [PP, P, P]
         _lib = lib
     return _lib
 
@@ -229,6 +231,23 @@ def make_sfa(q, kv_cache, out, scale, dtype, lse=None, v_dim=512) -> Sfa:
         raise ValueError("sparse-attention shapes disagree")
     return Sfa(H, Dqk, v_dim, DTYPE_CODE[dtype], float(scale), _ptr(q), _ptr(kv_cache), _ptr(out),
                _ptr(lse))
+
+
+# flag bits of dsa_validate_paged
+VALID_Q_OFFSETS, VALID_ROWS, VALID_CTX_LEN, VALID_PAGE_COUNT, VALID_PAGE_ID = 1, 2, 4, 8, 16
+
+
+def validate_paged(paged: Paged, error_word: torch.Tensor, stream=None) -> torch.Tensor:
+    """dsa_validate_paged: enqueue the device check of q_offsets, ctx_lens and
+    the used block-table entries; ``error_word`` (int32 [1] on the device)
+    receives the OR of the VALID_* flags, 0 when the data is valid."""
+    _check_tensor(error_word, "error_word", (torch.int32,))
+    if error_word.numel() < 1:
+        raise ValueError("error_word needs one int32")
+    st = load().dsa_validate_paged(ctypes.byref(paged), _ptr(error_word), _stream(stream))
+    if st != DSA_OK:
+        raise DsaError(st, "dsa_validate_paged")
+    return error_word
 
 
 def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:

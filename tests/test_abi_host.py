@@ -215,3 +215,16 @@ def test_static_fused_decode_checks_before_device_work():
     assert need > (64 << 20)
     assert call(big, good_indexer(), good_sfa()) == 6
     assert "static" in dsa.status_string(6)
+
+
+def test_validate_paged_argument_checks():
+    """dsa_validate_paged refuses invalid paged arguments and a NULL or
+    misaligned error word on the host, before any device work."""
+    lib = dsa.load()
+
+    def call(paged, word=FAKE):
+        return lib.dsa_validate_paged(ctypes.byref(paged), word, None)
+    for kw in BAD_PAGED:
+        assert call(good_paged(**kw)) == 1, kw
+    assert call(good_paged(), None) == 1
+    assert call(good_paged(), FAKE + 2) == 1
