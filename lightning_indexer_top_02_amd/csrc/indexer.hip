@@ -192,8 +192,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) __attribute__((amdgpu_waves_per_e
           __builtin_amdgcn_sched_barrier(0);
         };
         // The ring for one scoring shape: one or four rows of 64 heads
-        // (decode, speculative verify) with the row and head-tile loops
-        // unrolled, anything else through the general loops (the sums are
+        // (decode, speculative verify) and one row of at most 16 heads (the
+        // narrow indexer) with the row and head-tile loops unrolled, anything
+        // else through the general loops (the sums are
         // formed in the same order either way).  Everything is inlined so the
         // tile sets stay in registers.
         auto ring_loop = [&](auto nr_c, auto mt_c) __attribute__((always_inline)) {
@@ -238,6 +239,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) __attribute__((amdgpu_waves_per_e
           ring_loop(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
         else if (nrows == 1 && p.Hpad == 64)
           ring_loop(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
+        else if (nrows == 1 && p.Hpad == 16)
+          ring_loop(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
         else
           ring_loop(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
       }
