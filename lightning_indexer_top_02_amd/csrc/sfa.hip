@@ -100,6 +100,22 @@ __device__ __forceinline__ float4 unpack_f16x4(uint2 v) {
 // measured 12 % slower).
 
 constexpr int kKrowBytes = kSfaRows * kRowStride;
+
+// Zeros standing in for an absent row (index -1, or a rope piece a lane does
+// not load): every gather load is issued, from this row when there is
+// nothing to read, so no branch surrounds a load and the waits for a chunk
+// count exactly.  An fp8 row of zeros (codes and exponent bytes 0) decodes
+// to zeros too.  (A global, not a constant-space, array: a pointer chosen
+// between it and the pool stays a global pointer, so the loads stay global
+// loads.  Nothing writes it.)
+__device__ __align__(16) unsigned char kZeroRow[kRowBytes] = {};
+// pointers into global memory (pool rows or the zero row), so the loads are
+// global loads and cannot alias the gather registers
+typedef const __attribute__((address_space(1))) unsigned char* gbyte_ptr;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(gbyte_ptr p) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t*>(p));
+}
 constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chunk
 
 // fp8 latent rows in HBM ("Day0 Inference Optimization for Next-Generation
@@ -108,10 +124,9 @@ constexpr int kPieces = kSfaRows * (kRowBytes / 16);  // 16-byte pieces of a chu
 // a 16-byte block whose first four bytes are the tiles' E8M0 exponents
 // (power-of-two scales), then the 64 rope dims in bf16, 656 bytes.  A chunk
 // is gathered by 16 threads per row: thread k takes code pieces k and k + 16
-// (16 codes each) and, for k < 8, rope piece k, and the first thread of the
-// 16 also loads the row's exponent word, which the others read from it with
-// lane reads at staging (41 loads per row, where one exponent load per code
-// piece took 72).  The rows are staged in the same bf16 LDS layout as the
+// (16 codes each) and rope piece k (the zero row for k >= 8), and each of the
+// 16 loads the row's exponent word (one address, so one cache line for the
+// group).  The rows are staged in the same bf16 LDS layout as the
 // bf16 route, so everything after the staging is shared.  code * 2^e is exact in
 // bf16, and gfx950's scaled conversion (v_cvt_scalef32_pk_bf16_fp8, which
 // applies the exponent of its fp32 scale operand) makes two values per
@@ -200,19 +215,20 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   uint4 va[PPT];
   uint32_t ew[F8 ? PASSES : 1];
   const unsigned char* kv8 = static_cast<const unsigned char*>(p.kv);
-  auto gather = [&](int c0) {
+  auto gather_into = [&](uint4 (&va)[PPT], uint32_t (&ew)[F8 ? PASSES : 1], int c0) __attribute__((always_inline)) {
     if constexpr (F8) {
       const int k = tid & 15;
 #pragma unroll
       for (int ps = 0; ps < PASSES; ++ps) {
         const int r = ps * RP + (tid >> 4);
         const int row = r < kSfaRows ? rowidx[c0 + r] : -1;
-        const unsigned char* rb = kv8 + (int64_t)max(row, 0) * kF8RowBytes;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        va[3 * ps] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + 16 * k) : z;
-        va[3 * ps + 1] = row >= 0 ? *reinterpret_cast<const uint4*>(rb + 16 * (k + 16)) : z;
-        va[3 * ps + 2] = row >= 0 && k < 8 ? *reinterpret_cast<const uint4*>(rb + kVDim + 16 + 16 * k) : z;
-        ew[ps] = row >= 0 && k == 0 ? *reinterpret_cast<const uint32_t*>(rb + kVDim) : 0u;
+        const gbyte_ptr zero = (gbyte_ptr)kZeroRow;
+        const gbyte_ptr rb = row >= 0 ? (gbyte_ptr)(kv8 + (int64_t)row * kF8RowBytes) : zero;
+        const gbyte_ptr rope = row >= 0 && k < 8 ? rb + kVDim + 16 + 16 * k : zero;
+        va[3 * ps] = gload16(rb + 16 * k);
+        va[3 * ps + 1] = gload16(rb + 16 * (k + 16));
+        va[3 * ps + 2] = gload16(rope);
+        ew[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(rb + kVDim);  // (one address per 16 lanes)
       }
     } else {
 #pragma unroll
@@ -220,21 +236,19 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
         const int it = tid + j * NT;
         const int r = it / (kRowBytes / 16), part = it - r * (kRowBytes / 16);
         const int row = it < kPieces ? rowidx[c0 + r] : -1;
-        va[j] = row >= 0 ? *reinterpret_cast<const uint4*>(kvg + (int64_t)row * kQkDim + part * 8)
-                         : make_uint4(0u, 0u, 0u, 0u);
+        const gbyte_ptr src = row >= 0 ? (gbyte_ptr)(kvg + (int64_t)row * kQkDim) : (gbyte_ptr)kZeroRow;
+        va[j] = gload16(src + part * 16);
       }
     }
   };
-  auto stage = [&](unsigned char* kb) {
+  auto stage_from = [&](const uint4 (&va)[PPT], const uint32_t (&ew)[F8 ? PASSES : 1], unsigned char* kb)
+                        __attribute__((always_inline)) {
     if constexpr (F8) {
-      const int k = tid & 15, grp = (tid >> 4) & 3;
+      const int k = tid & 15;
 #pragma unroll
       for (int ps = 0; ps < PASSES; ++ps) {
         const int r = ps * RP + (tid >> 4);
-        // the row's exponent word, from the first lane of this 16-lane group
-        const uint32_t e0 = wave_read_lane((int)ew[ps], 0), e1 = wave_read_lane((int)ew[ps], 16);
-        const uint32_t e2 = wave_read_lane((int)ew[ps], 32), e3 = wave_read_lane((int)ew[ps], 48);
-        const uint32_t e = grp == 0 ? e0 : (grp == 1 ? e1 : (grp == 2 ? e2 : e3));
+        const uint32_t e = ew[ps];  // the row's exponent word (every lane of the 16 loaded it)
         if (r >= kSfaRows) continue;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {  // code piece k + 16 q: 16 codes -> 16 bf16 values (32 bytes)
@@ -266,14 +280,32 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
     }
   };
 
-  // two chunk buffers: chunk c is read from buffer c % 2 while chunk c + 1
-  // is written into the other (after this chunk's S^T, its loads having had
-  // a whole chunk to arrive) and chunk c + 2's loads are issued
+  // Two chunk buffers: chunk c is read from buffer c % 2 while chunk c + 1
+  // is written into the other (after this chunk's S^T) and the loads of a
+  // later chunk are issued.  A one-tile workgroup (two waves, one workgroup
+  // per compute unit) gathers into two register sets in turn, chunk c into
+  // set c % 2, so two chunks' loads are in flight while one is computed
+  // (chunk c + 3's loads start as chunk c + 1 is staged); wider workgroups
+  // have one set, and chunk c + 2's loads start as chunk c + 1 is staged.
+  uint4 vb[NW == 1 ? PPT : 1];
+  uint32_t ewb[F8 ? PASSES : 1];
+  auto gather = [&](int c0) __attribute__((always_inline)) { gather_into(va, ew, c0); };
+  auto stage = [&](unsigned char* kb) __attribute__((always_inline)) { stage_from(va, ew, kb); };
   if (nrows > 0) {
     gather(0);
+    if constexpr (NW == 1) {
+      if (nrows > kSfaRows) gather_into(vb, ewb, kSfaRows);
+      __builtin_amdgcn_sched_barrier(0);  // (both sets' loads are issued before the staging waits)
+    }
     stage(smem);
   }
-  if (nrows > kSfaRows) gather(kSfaRows);
+  if (nrows > kSfaRows) {
+    if constexpr (NW == 1) {
+      if (nrows > 2 * kSfaRows) gather(2 * kSfaRows);
+    } else {
+      gather(kSfaRows);
+    }
+  }
   for (int c0 = 0; c0 < nrows; c0 += kSfaRows) {
     __syncthreads();  // chunk c is staged; the other buffer (chunk c - 1) is no longer read
     const unsigned char* krow = smem + ((c0 / kSfaRows) & 1) * kKrowBytes;
@@ -291,8 +323,20 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
     }
     sa += sb;
     if (c0 + kSfaRows < nrows) {
-      stage(smem + (((c0 / kSfaRows) + 1) & 1) * kKrowBytes);
-      if (c0 + 2 * kSfaRows < nrows) gather(c0 + 2 * kSfaRows);
+      unsigned char* kb = smem + (((c0 / kSfaRows) + 1) & 1) * kKrowBytes;
+      if constexpr (NW == 1) {
+        // chunk c + 1 is in set (c + 1) % 2; chunk c + 3 goes into it next
+        if (((c0 / kSfaRows) & 1) == 0) {
+          stage_from(vb, ewb, kb);
+          if (c0 + 3 * kSfaRows < nrows) gather_into(vb, ewb, c0 + 3 * kSfaRows);
+        } else {
+          stage(kb);
+          if (c0 + 3 * kSfaRows < nrows) gather(c0 + 3 * kSfaRows);
+        }
+      } else {
+        stage(kb);
+        if (c0 + 2 * kSfaRows < nrows) gather(c0 + 2 * kSfaRows);
+      }
     }
     float z[4];
 #pragma unroll
