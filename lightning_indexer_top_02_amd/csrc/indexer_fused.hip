@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kFusedThreads) void li_fused(FusedParams p) {
   using Gm = IdxGeom<DT, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) int wsum[kFusedWaves];
-  __shared__ int res[2];
+  __shared__ int res[3];
   __shared__ int s_last;
 
   const int G = p.G, K = p.K;

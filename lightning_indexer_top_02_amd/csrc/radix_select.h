@@ -153,12 +153,17 @@ namespace dsa {
 //
 // The two remaining digits (11 and 10 bits) come from LDS histograms
 // (`hist`, kHistBins words) of the keys matching the digits found so far.
+// When the second digit's bin holds exactly the keys still needed, all of
+// them are kept whatever their low 10 bits, so the third digit is skipped
+// and the keys are compared on their top 22 bits (the kept set is the same:
+// every key of that bin is at or above the K-th).  With continuous scores
+// that bin usually holds one key.
 // Output: the kept keys are the keys above the K-th plus the first `need`
 // keys equal to it.  Each thread builds bit masks of its keys above and equal
 // to the K-th; one scan of the per-thread counts gives every thread its
 // output offset, above_before + min(equal_before, need), and the thread
 // writes the positions of its mask bits in order.  `wsum` holds NT / 64
-// ints, `res` 2.
+// ints, `res` 3.
 template <int NT, int KPT>
 __device__ void select_from_level1(const uint32_t (&key)[KPT], int vis, int K, uint32_t bin1, int need,
                                    int32_t* out, uint32_t* hist, int* wsum, int* res) {
@@ -166,6 +171,7 @@ __device__ void select_from_level1(const uint32_t (&key)[KPT], int vis, int K, u
   const int base = tid * KPT;
   const bool active = base < vis;
   uint32_t prefix = bin1;
+  int low = 0;  // low key bits left unresolved (10 when the third digit is skipped)
   for (int level = 1; level < 3; ++level) {
     const int nbins = kLevelBins[level], shift = kLevelShift[level], pshift = kLevelShift[level - 1];
     for (int c = tid; c < nbins; c += NT) hist[c] = 0u;
@@ -179,25 +185,34 @@ __device__ void select_from_level1(const uint32_t (&key)[KPT], int vis, int K, u
     }
     __syncthreads();
     if (wave == 0) {
-      int bin, above;
-      kth_bin_wave(hist, nbins, need, bin, above);
+      int bin, above, total, count = -1;
+      if (level == 1) kth_bin_wave_count<kLevelBins[1] / 64>(hist, need, bin, above, total, count);
+      else kth_bin_wave<kLevelBins[2] / 64>(hist, need, bin, above, total);
       if (lane == 0) {
         res[0] = bin;
         res[1] = above;
+        res[2] = count;
       }
     }
     __syncthreads();
     prefix = (prefix << (level == 1 ? 11 : 10)) | (uint32_t)res[0];
     need -= res[1];
+    const bool whole = res[2] == need;  // (uniform: read from LDS by every thread)
     __syncthreads();
+    if (whole) {
+      low = shift;
+      break;
+    }
   }
   static_assert(KPT <= 32, "one mask bit per key");
+  // the K-th key (its top 32 - low bits); a padding key 0 stays below it
   const uint32_t kth = prefix;
   uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    gtm |= key[c] > kth ? (1u << c) : 0u;
-    eqm |= key[c] == kth ? (1u << c) : 0u;
+    const uint32_t k = key[c] >> low;
+    gtm |= k > kth ? (1u << c) : 0u;
+    eqm |= k == kth ? (1u << c) : 0u;
   }
   int packed_total;
   const int packed_before = block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), packed_total, wsum);
