@@ -398,6 +398,47 @@ def test_all_ties_keep_the_lowest_positions():
         print(f"[ok] all ties, {name} route", flush=True)
 
 
+@pytest.mark.parametrize("excess", [0, 100, -100], ids=["bin_taken_whole", "ties_past_k", "ties_below_k"])
+def test_planted_ties_at_the_boundary(excess):
+    """Two score values: every key is 1 except K + excess planted positions
+    per request, whose keys are 2, with |q| and positive weights, so their
+    scores are exactly twice the others and each group ties exactly.  With
+    excess 0 the K-th key's bin holds exactly the keys needed (all of them
+    tied), with 100 the tie rule drops the last 100 planted positions, and
+    with -100 it keeps the lowest 100 unplanted positions."""
+    case = inputs.decode_32k(ctx_lens=[20000, 9000], n_q=[1, 3], topk=2048, exact=True)
+    K = case.topk
+    bt = case.block_table
+    kf = torch.ones(case.k_cache.shape, dtype=torch.float32)
+    g = torch.Generator().manual_seed(4242)
+    planted = []
+    for b, span in enumerate([20000, 8998]):  # (request 1's earliest row sees 8998 positions)
+        pos = torch.randperm(span, generator=g)[:K + excess].tolist()
+        for t in pos:
+            kf[bt[b, t // 64], t % 64] = 2.0
+        planted.append(set(pos))
+    kb = kf.to(torch.bfloat16)
+    k = kb if case.k_cache.dtype == torch.bfloat16 else kb.view(case.k_cache.dtype)
+    qv = case.q_idx if case.q_idx.dtype == torch.bfloat16 else case.q_idx.view(torch.bfloat16)
+    qa = qv.float().abs().to(torch.bfloat16)
+    q = qa if case.q_idx.dtype == torch.bfloat16 else qa.view(case.q_idx.dtype)
+    case = parity.to_device(dataclasses.replace(case, k_cache=k.contiguous(), q_idx=q.contiguous(),
+                                                weights=case.weights.abs() + 1))
+    qo, lens = case.q_offsets.cpu().numpy(), case.ctx_lens.cpu().numpy()
+    for name, flags in {"default": 0, "two_pass": parity.dsa.INDEXER_TWO_PASS}.items():
+        idx = parity.gpu_indexer_topk(case, flags=flags).cpu().numpy()
+        for b in range(len(lens)):
+            n = qo[b + 1] - qo[b]
+            for j in range(n):
+                vis = int(lens[b] - n + j + 1)
+                val = np.ones(vis, dtype=np.int64)
+                val[[t for t in planted[b] if t < vis]] = 2
+                order = np.lexsort((np.arange(vis), -val))  # higher value first, then lower position
+                want = np.sort(order[:K])
+                assert np.array_equal(idx[qo[b] + j], want), f"{name}: request {b} row {j}"
+        print(f"[ok] planted ties excess={excess}, {name} route", flush=True)
+
+
 # --- sparse attention alone, on the oracle's indices ---------------------------
 def test_sfa_on_oracle_indices_with_padding():
     case = parity.to_device(inputs.decode_32k(ctx_lens=[9000, 1500, 200], n_q=[1, 2, 1], topk=1024))
