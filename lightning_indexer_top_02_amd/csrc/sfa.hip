@@ -155,8 +155,9 @@ struct SfaXchg {
   float lsum[2][4][16];   // [half][head tile][head]
 };
 
-template <int NW, bool F8>
+template <int NW, bool F8, bool TWO>
 __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
+  static_assert(!TWO || (NW == 1 && !F8), "two gather register sets: one-tile bf16 workgroups only");
   constexpr int NT = NW * 128;
   // fp8: RP rows per pass of 16 threads each, PASSES passes per chunk
   constexpr int RP = NT / 16, PASSES = (kSfaRows + RP - 1) / RP;
@@ -281,26 +282,28 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   };
 
   // Two chunk buffers: chunk c is read from buffer c % 2 while chunk c + 1
-  // is written into the other (after this chunk's S^T) and the loads of a
-  // later chunk are issued.  A one-tile workgroup (two waves, one workgroup
-  // per compute unit) gathers into two register sets in turn, chunk c into
-  // set c % 2, so two chunks' loads are in flight while one is computed
-  // (chunk c + 3's loads start as chunk c + 1 is staged); wider workgroups
-  // have one set, and chunk c + 2's loads start as chunk c + 1 is staged.
-  uint4 vb[NW == 1 ? PPT : 1];
+  // is written into the other (after this chunk's S^T) and chunk c + 2's
+  // loads are issued.  With TWO (one-tile bf16 workgroups whose split is one
+  // or two chunks: the single-row decode) the gather uses two register sets
+  // in turn, chunk c in set c % 2, so both chunks' loads are issued before
+  // the first is staged (and on longer splits chunk c + 3's loads start as
+  // chunk c + 1 is staged).  Measured: 16.5 against 16.8 us at the 32K
+  // single-row decode; on 16-chunk splits (the 16-head batch of 64 rows)
+  // two sets took 58.7 us against 53.0, and with fp8 rows 48.9 against 36.5.
+  uint4 vb[TWO ? PPT : 1];
   uint32_t ewb[F8 ? PASSES : 1];
   auto gather = [&](int c0) __attribute__((always_inline)) { gather_into(va, ew, c0); };
   auto stage = [&](unsigned char* kb) __attribute__((always_inline)) { stage_from(va, ew, kb); };
   if (nrows > 0) {
     gather(0);
-    if constexpr (NW == 1) {
+    if constexpr (TWO) {
       if (nrows > kSfaRows) gather_into(vb, ewb, kSfaRows);
       __builtin_amdgcn_sched_barrier(0);  // (both sets' loads are issued before the staging waits)
     }
     stage(smem);
   }
   if (nrows > kSfaRows) {
-    if constexpr (NW == 1) {
+    if constexpr (TWO) {
       if (nrows > 2 * kSfaRows) gather(2 * kSfaRows);
     } else {
       gather(kSfaRows);
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
     sa += sb;
     if (c0 + kSfaRows < nrows) {
       unsigned char* kb = smem + (((c0 / kSfaRows) + 1) & 1) * kKrowBytes;
-      if constexpr (NW == 1) {
+      if constexpr (TWO) {
         // chunk c + 1 is in set (c + 1) % 2; chunk c + 3 goes into it next
         if (((c0 / kSfaRows) & 1) == 0) {
           stage_from(vb, ewb, kb);
@@ -585,20 +588,23 @@ __global__ __launch_bounds__(kF32Threads) void sfa_f32(SfaParams p) {
 
 using namespace dsa;
 
-template <int NW, bool F8>
+template <int NW, bool F8, bool TWO = false>
 static hipError_t launch_sfa(dim3 grid, size_t lds, hipStream_t s, const SfaParams& p) {
   {
-    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(sfa_bf16<NW, F8>), lds);
+    const hipError_t e = dsa_allow_lds(reinterpret_cast<const void*>(sfa_bf16<NW, F8, TWO>), lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((sfa_bf16<NW, F8>), grid, dim3(NW * 128), lds, s, p);
+  hipLaunchKernelGGL((sfa_bf16<NW, F8, TWO>), grid, dim3(NW * 128), lds, s, p);
   return hipGetLastError();
 }
 
 template <bool F8>
 static hipError_t launch_sfa_nw(int nw, dim3 grid, size_t lds, hipStream_t s, const SfaParams& p) {
   switch (nw) {
-    case 1: return launch_sfa<1, F8>(grid, lds, s, p);
+    case 1:
+      if constexpr (!F8)  // splits of at most two chunks: both gathered at once (see sfa_bf16)
+        if (p.rows_per_split <= 2 * kSfaRows) return launch_sfa<1, false, true>(grid, lds, s, p);
+      return launch_sfa<1, F8>(grid, lds, s, p);
     case 2: return launch_sfa<2, F8>(grid, lds, s, p);
     case 3: return launch_sfa<3, F8>(grid, lds, s, p);
     default: return launch_sfa<4, F8>(grid, lds, s, p);
