@@ -127,6 +127,12 @@ SfaPlan plan_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int topk) {
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (topk + 63) / 64));
     p.rows_per_split = (int)round_up((topk + splits - 1) / splits, 32);
     p.n_split = (topk + p.rows_per_split - 1) / p.rows_per_split;
+  } else {  // fp32: 16 heads per workgroup, splits of whole 16-row chunks, about one workgroup per compute unit
+    const int64_t blocks = (int64_t)pg->num_q_tokens * (s->n_heads / 16);
+    int64_t splits = (kNominalCUs + blocks - 1) / blocks;
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (topk + 15) / 16));
+    p.rows_per_split = (int)round_up((topk + splits - 1) / splits, 16);
+    p.n_split = (topk + p.rows_per_split - 1) / p.rows_per_split;
   }
   if (p.n_split > 1) {
     const size_t th = (size_t)pg->num_q_tokens * s->n_heads;

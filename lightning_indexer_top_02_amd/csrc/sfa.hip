@@ -508,82 +508,143 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine(SfaParams p) {
   if (p.lse && d0 == 0) p.lse[th] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
-// fp32: one workgroup per (query row, head); logits of all selected rows in
-// LDS, then the softmax-weighted sum with each thread owning two output dims.
+// fp32 (VALU): one workgroup per (query row, 16 heads, split of the Top-K
+// list), like the bf16 route, so a single-row decode spreads over the chip.
+// The split's selected rows are staged 16 at a time in LDS (580-float rows:
+// 580 = 4 mod 64 banks, so the 16 rows a wave reads at one dim fall in 16
+// different bank groups); thread (h, r) forms the logit of head h and row r,
+// an online softmax runs over the chunks, and each thread then owns two
+// output dims of all 16 heads.  Splits write fp16 partials for sfa_combine;
+// a single split writes the output.
 constexpr int kF32Threads = 256;
-constexpr int kF32MaxK = 4096;
+constexpr int kF32Rows = 16;               // selected rows per chunk
+constexpr int kF32Heads = 16;              // heads per workgroup
+constexpr int kF32Stride = kQkDim + 4;     // padded LDS row (floats)
+static_assert(kF32Rows * kF32Heads == kF32Threads, "one logit per thread");
+static_assert(2 * kF32Threads == kVDim, "two output dims per thread");
 
-__global__ __launch_bounds__(kF32Threads) void sfa_f32(SfaParams p) {
-  __shared__ float qsh[kQkDim];
-  __shared__ float z[kF32MaxK];
-  __shared__ int rowoff[kF32MaxK];  // element offset of each selected row, -1 = none
-  __shared__ float red[kF32Threads / 64];
-  const int h = blockIdx.x, i = blockIdx.y;
-  const int b = request_of_row(p.q_offsets, p.batch, i);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* q = static_cast<const float*>(p.q) + ((int64_t)i * p.H + h) * kQkDim;
-  const float* kv = static_cast<const float*>(p.kv);
-  for (int d = tid; d < kQkDim; d += kF32Threads) qsh[d] = q[d];
-  const int32_t* irow = p.idx + (int64_t)i * p.K;
-  const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
-  __syncthreads();
-  float lmax = -INFINITY;
-  for (int r = tid; r < p.K; r += kF32Threads) {
-    const int t = irow[r];
-    if (t < 0) {
-      rowoff[r] = -1;
-      z[r] = -INFINITY;
-      continue;
-    }
-    const int64_t off = ((int64_t)btrow[t >> 6] * kPage + (t & 63)) * kQkDim;
-    rowoff[r] = (int)(off / kQkDim);  // row number in the pool
-    const float4* row = reinterpret_cast<const float4*>(kv + off);
-    float dot = 0.f;
-    for (int d = 0; d < kQkDim / 4; ++d) {
-      float4 a = row[d];
-      dot = fmaf(qsh[4 * d], a.x, dot);
-      dot = fmaf(qsh[4 * d + 1], a.y, dot);
-      dot = fmaf(qsh[4 * d + 2], a.z, dot);
-      dot = fmaf(qsh[4 * d + 3], a.w, dot);
-    }
-    z[r] = dot * p.scale;
-    lmax = fmaxf(lmax, z[r]);
-  }
-  for (int off = 32; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
-  if (lane == 0) red[wave] = lmax;
-  __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < kF32Threads / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-  float lsum = 0.f;
-  if (M != -INFINITY)
-    for (int r = tid; r < p.K; r += kF32Threads) {
-      const float e = rowoff[r] >= 0 ? expf(z[r] - M) : 0.f;
-      z[r] = e;
-      lsum += e;
-    }
-  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-  if (lane == 0) red[wave] = lsum;
-  __syncthreads();
-  float L = 0.f;
-  for (int w = 0; w < kF32Threads / 64; ++w) L += red[w];
-  float acc0 = 0.f, acc1 = 0.f;
-  if (M != -INFINITY)
-    for (int r = 0; r < p.K; ++r) {
-      const int ro = rowoff[r];
-      if (ro < 0) continue;
-      const float pr = z[r];
-      const float* row = kv + (int64_t)ro * kQkDim;
-      acc0 = fmaf(pr, row[tid], acc0);
-      acc1 = fmaf(pr, row[tid + kF32Threads], acc1);
-    }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* out = static_cast<float*>(p.out) + ((int64_t)i * p.H + h) * kVDim;
-  out[tid] = acc0 * inv;
-  out[tid + kF32Threads] = acc1 * inv;
-  if (p.lse && tid == 0) p.lse[(int64_t)i * p.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
+__host__ __device__ constexpr size_t sfa_f32_lds(int rows_per_split) {
+  return (size_t)(kF32Heads + kF32Rows) * kF32Stride * 4 + (size_t)(kF32Heads * kF32Rows + 2 * kF32Heads) * 4 +
+         (size_t)(rows_per_split + kF32Rows - 1) / kF32Rows * kF32Rows * 4;
 }
 
+__global__ __launch_bounds__(kF32Threads) void sfa_f32(SfaParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* qs = reinterpret_cast<float*>(smem);                // [16 heads][kF32Stride]
+  float* ks = qs + kF32Heads * kF32Stride;                   // [16 rows][kF32Stride]
+  float* pz = ks + kF32Rows * kF32Stride;                    // [16 heads][16 rows] probabilities
+  float* hs = pz + kF32Heads * kF32Rows;                     // [16] rescale factors, then [2][16] m and l
+  int* rowidx = reinterpret_cast<int*>(hs + 2 * kF32Heads);  // pool row of each selected row, -1 = none
+  const int n_hg = p.H / kF32Heads;
+  const int hg = blockIdx.x % n_hg, rs = blockIdx.x / n_hg;
+  const int split = rs % p.n_split, i = rs / p.n_split;
+  const int b = request_of_row(p.q_offsets, p.batch, i);
+  const int tid = threadIdx.x;
+  const int r_begin = split * p.rows_per_split;
+  const int nrows = max(0, min(p.K, r_begin + p.rows_per_split) - r_begin);
+  const int nr = (nrows + kF32Rows - 1) / kF32Rows * kF32Rows;
+  {
+    const int32_t* irow = p.idx + (int64_t)i * p.K + r_begin;
+    const int32_t* btrow = p.bt + (int64_t)b * p.bt_stride;
+    for (int r = tid; r < nr; r += kF32Threads) {
+      const int t = r < nrows ? irow[r] : -1;
+      rowidx[r] = t >= 0 ? btrow[t >> 6] * kPage + (t & 63) : -1;
+    }
+  }
+  const float* qg = static_cast<const float*>(p.q) + ((int64_t)i * p.H + hg * kF32Heads) * kQkDim;
+  for (int e = tid; e < kF32Heads * (kQkDim / 4); e += kF32Threads) {
+    const int h = e / (kQkDim / 4), d4 = e - h * (kQkDim / 4);
+    *reinterpret_cast<float4*>(qs + h * kF32Stride + 4 * d4) = reinterpret_cast<const float4*>(qg + h * kQkDim)[d4];
+  }
+  const float4* kv4 = static_cast<const float4*>(p.kv);
+  const int h = tid >> 4, r = tid & 15;  // this thread's logit
+  const int d0 = 2 * tid;                // this thread's output dims
+  float m = -INFINITY, l = 0.f;          // head h's running maximum and sum (the same in its 16 lanes)
+  float acc[kF32Heads][2];
+#pragma unroll
+  for (int hh = 0; hh < kF32Heads; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
+  for (int c0 = 0; c0 < nr; c0 += kF32Rows) {
+    __syncthreads();  // rowidx and the Q tile written; the previous chunk's rows no longer read
+    for (int e = tid; e < kF32Rows * (kQkDim / 4); e += kF32Threads) {
+      const int rr = e / (kQkDim / 4), d4 = e - rr * (kQkDim / 4);
+      const int row = rowidx[c0 + rr];
+      *reinterpret_cast<float4*>(ks + rr * kF32Stride + 4 * d4) =
+          row >= 0 ? kv4[(int64_t)row * (kQkDim / 4) + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    float dot = 0.f;
+    const float4* q4 = reinterpret_cast<const float4*>(qs + h * kF32Stride);
+    const float4* k4 = reinterpret_cast<const float4*>(ks + r * kF32Stride);
+#pragma unroll 8
+    for (int d4 = 0; d4 < kQkDim / 4; ++d4) {
+      const float4 a = q4[d4], k = k4[d4];
+      dot = fmaf(a.x, k.x, dot);
+      dot = fmaf(a.y, k.y, dot);
+      dot = fmaf(a.z, k.z, dot);
+      dot = fmaf(a.w, k.w, dot);
+    }
+    const bool live = rowidx[c0 + r] >= 0;
+    const float z = live ? dot * p.scale : -INFINITY;
+    float cm = z;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));  // over head h's 16 lanes
+    const float mn = fmaxf(m, cm);
+    const float al = mn == -INFINITY ? 1.f : expf(m - mn);  // (m = -inf: 0)
+    const float pr = live ? expf(z - mn) : 0.f;
+    float ps = pr;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    l = l * al + ps;
+    m = mn;
+    pz[h * kF32Rows + r] = pr;
+    if (r == 0) hs[h] = al;
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < kF32Heads; ++hh) {
+      const float a = hs[hh];
+      acc[hh][0] *= a;
+      acc[hh][1] *= a;
+    }
+#pragma unroll 4
+    for (int rr = 0; rr < kF32Rows; ++rr) {
+      const float2 v = *reinterpret_cast<const float2*>(ks + rr * kF32Stride + d0);
+#pragma unroll
+      for (int hh = 0; hh < kF32Heads; ++hh) {
+        const float pv = pz[hh * kF32Rows + rr];
+        acc[hh][0] = fmaf(pv, v.x, acc[hh][0]);
+        acc[hh][1] = fmaf(pv, v.y, acc[hh][1]);
+      }
+    }
+  }
+  __syncthreads();  // the last chunk's factors read
+  if (r == 0) {
+    hs[h] = m;
+    hs[kF32Heads + h] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < kF32Heads; ++hh) {
+    const float lh = hs[kF32Heads + hh];
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const int64_t th = (int64_t)i * p.H + hg * kF32Heads + hh;
+    if (p.n_split == 1)
+      *reinterpret_cast<float2*>(static_cast<float*>(p.out) + th * kVDim + d0) =
+          make_float2(acc[hh][0] * inv, acc[hh][1] * inv);
+    else
+      *reinterpret_cast<uint32_t*>(p.part_o + ((int64_t)split * p.T * p.H + th) * kVDim + d0) =
+          pack_f16x2(acc[hh][0] * inv, acc[hh][1] * inv);
+  }
+  if (tid < kF32Heads) {
+    const float lh = hs[kF32Heads + tid];
+    const float lse_v = lh > 0.f ? hs[tid] + logf(lh) : -INFINITY;
+    const int64_t th = (int64_t)i * p.H + hg * kF32Heads + tid;
+    if (p.n_split == 1) {
+      if (p.lse) p.lse[th] = lse_v;
+    } else {
+      p.part_lse[(int64_t)split * p.T * p.H + th] = lse_v;
+    }
+  }
+}
 }  // namespace dsa
 
 using namespace dsa;
@@ -611,6 +672,31 @@ static hipError_t launch_sfa_nw(int nw, dim3 grid, size_t lds, hipStream_t s, co
   }
 }
 
+template <bool BF16>
+static hipError_t launch_combine(const DsaSfaLaunch& a, hipStream_t s, const SfaParams& p) {
+  const int64_t groups = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
+  // lanes per (row, head, 4 dims): 4 for 32 splits and more, 2 for 8 to 31
+  // (a batch-8 decode has 16: 26.2 us against 28.0 with 4), 1 below
+  const int G = a.n_split >= 32 ? 4 : (a.n_split >= 8 ? 2 : 1);
+  const int share = (a.n_split + G - 1) / G;  // splits per thread
+  const dim3 cgrid((unsigned)((G * groups + kCombineThreads - 1) / kCombineThreads));
+  if (G == 4) {
+    if (share <= 2) hipLaunchKernelGGL((sfa_combine<BF16, 4, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 4) hipLaunchKernelGGL((sfa_combine<BF16, 4, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 8) hipLaunchKernelGGL((sfa_combine<BF16, 4, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((sfa_combine<BF16, 4, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
+  } else if (G == 2) {
+    if (share <= 4) hipLaunchKernelGGL((sfa_combine<BF16, 2, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 8) hipLaunchKernelGGL((sfa_combine<BF16, 2, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((sfa_combine<BF16, 2, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
+  } else {
+    if (share <= 2) hipLaunchKernelGGL((sfa_combine<BF16, 1, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else if (share <= 4) hipLaunchKernelGGL((sfa_combine<BF16, 1, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((sfa_combine<BF16, 1, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   SfaParams p;
   p.q_offsets = a.q_offsets;
@@ -631,8 +717,16 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
   if (a.dtype == 0) {
-    hipLaunchKernelGGL(sfa_f32, dim3(a.n_heads, a.num_rows), dim3(kF32Threads), 0, s, p);
-    return hipGetLastError();
+    if (a.n_heads % kF32Heads != 0) return hipErrorInvalidValue;
+    const int64_t wgs = (int64_t)a.n_split * a.num_rows * (a.n_heads / kF32Heads);
+    if (wgs * kF32Threads > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+    const size_t lds = sfa_f32_lds(a.rows_per_split);
+    const hipError_t e0 = dsa_allow_lds(reinterpret_cast<const void*>(sfa_f32), lds);
+    if (e0 != hipSuccess) return e0;
+    hipLaunchKernelGGL(sfa_f32, dim3((unsigned)wgs), dim3(kF32Threads), lds, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_split == 1) return e;
+    return launch_combine<false>(a, s, p);
   }
   const int nw = a.nw;  // 16-head tiles per workgroup
   if (nw < 1 || nw > 4 || (a.n_heads / 16) % nw != 0) return hipErrorInvalidValue;
@@ -650,25 +744,5 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  const int64_t groups = (int64_t)a.num_rows * a.n_heads * (kVDim / 4);
-  // lanes per (row, head, 4 dims): 4 for 32 splits and more, 2 for 8 to 31
-  // (a batch-8 decode has 16: 26.2 us against 28.0 with 4), 1 below
-  const int G = a.n_split >= 32 ? 4 : (a.n_split >= 8 ? 2 : 1);
-  const int share = (a.n_split + G - 1) / G;  // splits per thread
-  const dim3 cgrid((unsigned)((G * groups + kCombineThreads - 1) / kCombineThreads));
-  if (G == 4) {
-    if (share <= 2) hipLaunchKernelGGL((sfa_combine<true, 4, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 4, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else if (share <= 8) hipLaunchKernelGGL((sfa_combine<true, 4, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((sfa_combine<true, 4, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
-  } else if (G == 2) {
-    if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 2, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else if (share <= 8) hipLaunchKernelGGL((sfa_combine<true, 2, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((sfa_combine<true, 2, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
-  } else {
-    if (share <= 2) hipLaunchKernelGGL((sfa_combine<true, 1, 2>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else if (share <= 4) hipLaunchKernelGGL((sfa_combine<true, 1, 4>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((sfa_combine<true, 1, 8>), cgrid, dim3(kCombineThreads), 0, s, p);
-  }
-  return hipGetLastError();
+  return launch_combine<true>(a, s, p);
 }

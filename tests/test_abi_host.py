@@ -151,12 +151,14 @@ def test_workspace_sizes():
     # counters | histograms | scores | selection candidates (keys, positions; min(L, 8192) per row) |
     # kept-position bitmaps (a bit per position of each 8192-position segment of the score stride)
     assert need == 256 + 5 * 6144 * 4 + 5 * 1024 * 4 + 2 * 5 * 1024 * 4 + 5 * 256 * 4
-    # one row of 128 heads at small batch splits the index list; fp32 never does
+    # one row at small batch splits the index list, on both routes: fp16
+    # partial outputs [splits][rows][H][512] and fp32 log-sum-exps, each
+    # region 256-byte aligned (fp32: 16 splits of 16 rows for K = 256)
     one = good_paged(batch=1, num_q_tokens=1, max_q_per_req=1)
     s_bf16 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa()), 2048)
     assert s_bf16 > 0 and s_bf16 % 256 == 0
     s_f32 = lib.dsa_sparse_attn_workspace_size(ctypes.byref(one), ctypes.byref(good_sfa(dtype=0, n_heads=16)), 256)
-    assert s_f32 == 0
+    assert s_f32 == 16 * 16 * 512 * 2 + 1024
 
 
 def test_indexer_scores_argument_checks():
