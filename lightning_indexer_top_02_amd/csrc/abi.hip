@@ -123,7 +123,9 @@ SfaPlan plan_sfa(const dsa_paged_t* pg, const dsa_sfa_t* s, int topk) {
     // tiles holds ~230 VGPRs per lane, so a compute unit runs one at a time
     // and a larger grid only queues a second round (64 decode rows at 32K:
     // 107.6 us with two rounds, 94.2 us with one)
-    int64_t splits = (kNominalCUs + blocks - 1) / blocks;
+    // (one-tile workgroups, ~79 KB of LDS and 2 waves, fit two to a compute unit)
+    const int64_t target = p.nw == 1 ? 2 * kNominalCUs : kNominalCUs;
+    int64_t splits = (target + blocks - 1) / blocks;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (topk + 63) / 64));
     p.rows_per_split = (int)round_up((topk + splits - 1) / splits, 32);
     p.n_split = (topk + p.rows_per_split - 1) / p.rows_per_split;

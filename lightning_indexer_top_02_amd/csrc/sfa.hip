@@ -147,13 +147,23 @@ __device__ __forceinline__ uint2 read_vt4(const unsigned char* krow, int r0, int
 }
 
 // Exchange area between the two waves of a head tile (LDS, after the chunk
-// buffers and the row table): the chunk maxima of each half's 16 rows, the
-// probabilities each half feeds the other's P.V, and the final sums.
+// buffers): the chunk maxima of each half's 16 rows, the probabilities each
+// half feeds the other's P.V, and the final sums.  Sized for the workgroup's
+// NW tiles, so a one-tile workgroup takes 79 KB of LDS with a 512-row split
+// and two fit on a compute unit.
+template <int NW>
 struct SfaXchg {
-  float tmax[2][4][16];   // [half][head tile][head]
-  uint2 pv[2][4][64];     // [half][head tile][lane]: 4 bf16 probabilities
-  float lsum[2][4][16];   // [half][head tile][head]
+  float tmax[2][NW][16];   // [half][head tile][head]
+  uint2 pv[2][NW][64];     // [half][head tile][lane]: 4 bf16 probabilities
+  float lsum[2][NW][16];   // [half][head tile][head]
 };
+
+// dynamic LDS of a bf16/fp8 workgroup: two chunk buffers, the exchange area
+// and the split's row table
+__host__ __device__ constexpr size_t sfa_lds_bytes(int nw, int rows_per_split) {
+  return (size_t)2 * kKrowBytes + (size_t)nw * (2 * 16 * 4 + 2 * 64 * 8 + 2 * 16 * 4) +
+         (size_t)(rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
+}
 
 template <int NW, bool F8, bool TWO>
 __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
@@ -164,8 +174,9 @@ __global__ __launch_bounds__(NW * 128) void sfa_bf16(SfaParams p) {
   constexpr int PPT = F8 ? 3 * PASSES : (kPieces + NT - 1) / NT;  // gathered pieces per thread per chunk
   constexpr int kHalfDims = kVDim / 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  SfaXchg* xc = reinterpret_cast<SfaXchg*>(smem + 2 * kKrowBytes);
-  int* rowidx = reinterpret_cast<int*>(smem + 2 * kKrowBytes + sizeof(SfaXchg));  // pool row, -1 = none
+  static_assert(sizeof(SfaXchg<NW>) == (size_t)NW * (2 * 16 * 4 + 2 * 64 * 8 + 2 * 16 * 4), "sfa_lds_bytes");
+  SfaXchg<NW>* xc = reinterpret_cast<SfaXchg<NW>*>(smem + 2 * kKrowBytes);
+  int* rowidx = reinterpret_cast<int*>(smem + 2 * kKrowBytes + sizeof(SfaXchg<NW>));  // pool row, -1 = none
 
   // XCD-aware order: consecutive workgroups go to the eight XCDs in turn,
   // so the head groups of one (split, row) are given ids 8 apart and land on
@@ -738,8 +749,7 @@ hipError_t dsa_launch_sparse_attn(const DsaSfaLaunch& a, hipStream_t s) {
   if (wgs * nw * 128 > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
   hipError_t e0;
-  const size_t lds = (size_t)2 * kKrowBytes + sizeof(SfaXchg) +
-                     (size_t)(a.rows_per_split + kSfaRows - 1) / kSfaRows * kSfaRows * 4;
+  const size_t lds = sfa_lds_bytes(nw, a.rows_per_split);
   e0 = a.dtype == 2 ? launch_sfa_nw<true>(nw, grid, lds, s, p) : launch_sfa_nw<false>(nw, grid, lds, s, p);
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
