@@ -97,13 +97,17 @@ IndexerPlan plan_indexer(const dsa_paged_t* pg) {
 
 // 16-head tiles per SFA workgroup (waves = 2 per tile): up to 4, dividing the
 // head count.  A workgroup of 4 tiles shares each gathered row among 64
-// heads, which decides throughput once the batch fills the chip; when the
-// whole batch is at most 8 tiles (one 128-head row), the step is latency-bound
-// and 1-tile workgroups finish their chunks sooner (measured at the 32K
-// single-row decode: 18.3 us against 18.6 with 2 tiles and 21.6 with 4).
+// heads, which decides throughput once the batch fills the chip; smaller
+// batches are latency-bound, and narrower workgroups (more of them on a
+// compute unit) finish sooner although each row is gathered by more of
+// them.  By the batch's tiles (rows x 16-head groups), measured at 32K
+// decode with 128 heads: at most 8 (one row), 1 tile (16.5 us against 22
+// with 4); 16 or 32 (2 or 4 rows), 2 tiles (18.9 and 22.5 us against 22.0
+// and 27.7 with 4); 64 and more (8 rows), 4 tiles (26.3 us against 27.9).
 int sfa_waves(int n_heads, int64_t num_rows) {
   const int hq = n_heads / 16;
-  const int cap = num_rows * hq <= 8 ? 1 : 4;
+  const int64_t tiles = num_rows * hq;
+  const int cap = tiles <= 8 ? 1 : (tiles <= 32 ? 2 : 4);
   for (int nw = cap; nw > 1; --nw)
     if (hq % nw == 0) return nw;
   return 1;
