@@ -29,7 +29,12 @@
 // normalised partial output (fp16) and its log-sum-exp, and sfa_combine merges
 // them.
 //
-// fp32 kernel (sfa_f32): VALU, one workgroup per (query row, head).
+// The tiles per workgroup (NW) follow the batch: one tile when the batch is
+// at most 8 tiles, two up to 32, else four (see the host planner); absent
+// rows and unneeded pieces read a zero row, so every gather load is issued.
+//
+// fp32 kernel (sfa_f32): VALU, one workgroup per (query row, 16 heads, split
+// of the index list), merged by sfa_combine like the bf16 route.
 #include <algorithm>
 
 #include "dsa_device.h"
