@@ -91,6 +91,32 @@ def test_sfa_fp8_latent(heads, exact):
                           n_heads_sfa=heads))
 
 
+# head tiles per sparse-attention workgroup by batch (128 heads): 2 and 4
+# rows take 2-tile workgroups, 8 rows 4-tile ones
+@pytest.mark.parametrize("rows", [2, 4, 8])
+@pytest.mark.parametrize("sfa", ["bf16", "fp8"])
+def test_sfa_tile_widths_by_batch(rows, sfa):
+    _run(inputs.make_case(name=f"tiles_{rows}rows_{sfa}", seed=98 + rows, ctx_lens=[5000 + 777 * r for r in range(rows)],
+                          n_q=1, idx_dtype="bf16", n_heads_idx=64, head_dim_idx=128, topk=2048, sfa_dtype=sfa,
+                          n_heads_sfa=128))
+
+
+# fp32 sparse attention: splits of several 16-row chunks (64 single-row
+# requests: 4 splits of 64 rows, K = 250 leaves a ragged last chunk), and a
+# batch large enough for one split per row (the output written directly)
+@pytest.mark.parametrize("heads", [16, 32])
+def test_sfa_f32_multi_chunk_splits(heads):
+    _run(inputs.make_case(name=f"f32_4splits_{heads}h", seed=83, ctx_lens=[1000 + 7 * r for r in range(64)], n_q=1,
+                          idx_dtype="f32", n_heads_idx=4, head_dim_idx=64, topk=250, w_dist="uniform",
+                          sfa_dtype="f32", n_heads_sfa=heads, sfa_std=1.0))
+
+
+def test_sfa_f32_one_split_per_row():
+    _run(inputs.make_case(name="f32_1split", seed=84, ctx_lens=[600 + r for r in range(300)], n_q=1,
+                          idx_dtype="f32", n_heads_idx=4, head_dim_idx=64, topk=250, w_dist="uniform",
+                          sfa_dtype="f32", n_heads_sfa=16, sfa_std=1.0))
+
+
 @pytest.mark.parametrize("heads", [5, 17, 48])
 def test_odd_indexer_head_counts(heads):
     _run(inputs.make_case(name=f"heads{heads}", seed=79, ctx_lens=[5000, 777], n_q=[1, 2],
