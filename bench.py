@@ -539,6 +539,8 @@ def measure(name: str, case: inputs.Case, steps: int, warmup: int, eager: bool =
 # The grid of workloads measured beside the headline (the batch x sequence-length
 # baselines of the decode and prefill routes): name -> (maker, steps).
 GRID = {
+    "decode_32k_b2": (lambda dev: inputs.decode_32k(batch=2, device=dev), 100),
+    "decode_32k_b4": (lambda dev: inputs.decode_32k(batch=4, device=dev), 100),
     "decode_32k_b8": (lambda dev: inputs.decode_32k(batch=8, device=dev), 50),
     "decode_32k_b32": (lambda dev: inputs.decode_32k(batch=32, device=dev), 20),
     "decode_32k_b64": (lambda dev: inputs.decode_32k(batch=64, device=dev), 20),

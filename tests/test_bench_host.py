@@ -51,7 +51,8 @@ def test_replicas_cover_three_infinity_caches():
 def test_grid_names_every_scope_workload():
     """The grid carries the 32K batch sweep and the batched fp8 (both widths),
     speculative-verify and chunked-prefill workloads."""
-    assert {"decode_32k_b8", "decode_32k_b32", "decode_32k_b64", "decode_32k_b128", "batched_fp8_narrow",
+    assert {"decode_32k_b2", "decode_32k_b4", "decode_32k_b8", "decode_32k_b32", "decode_32k_b64", "decode_32k_b128",
+            "batched_fp8_narrow",
             "batched_fp8_wide", "spec_verify", "chunked_prefill"} <= set(bench.GRID)
 
 
